@@ -1,0 +1,176 @@
+"""Python binding of libqgemv (ctypes): argument marshalling only.
+
+Every step of the GEMV and the argmax runs in the HIP kernels of
+libqgemv.so; this module checks dtypes/shapes/devices of torch tensors,
+passes their device pointers and the current HIP stream to the C ABI, and
+turns negative status codes into QgemvError. PyTorch only provides device
+memory and streams. There is no fallback: if the library is missing the
+import fails.
+
+Build the library first: ``python -m bandwidth_bound_quantized_amd.build``
+(or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
+SRC_CANONICAL, SRC_BF16 = 0, 1
+OK, EINVAL, ESHAPE, EALIGN, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
+MAX_BATCH = 8
+ARGMAX_WS_WORDS_PER_ROW = 129
+GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
+FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128"}
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {_lib.qgemv_status_str(status).decode()}"
+        if status == EHIP:
+            msg += f" (hipError {_lib.qgemv_last_hip_error()})"
+        super().__init__(msg)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libqgemv.so not built at {LIB_PATH}; run "
+                          "`python -m bandwidth_bound_quantized_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i64, c_int, c_vp, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "qgemv_packed_size": (c_int, [c_int, c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
+        "qgemv_pack": (c_int, [c_int, c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+        "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
+        "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
+        "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
+        "qgemv_status_str": (ctypes.c_char_p, [c_int]),
+        "qgemv_last_hip_error": (c_int, []),
+        "qgemv_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_argmax", "qgemv_stream_read",
+           "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def version() -> str:
+    return _lib.qgemv_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise QgemvError(status, where)
+
+
+# ------------------------------------------------------------------ host side
+def packed_size(fmt: int, M: int, K: int) -> Tuple[int, int]:
+    w = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(_lib.qgemv_packed_size(fmt, M, K, ctypes.byref(w), ctypes.byref(s)), "qgemv_packed_size")
+    return w.value, s.value
+
+
+def pack(fmt: int, src_kind: int, src_w: np.ndarray, src_scales: Optional[np.ndarray], M: int,
+         K: int) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Host arrays in, host arrays out (codes as uint8 bytes, scales as uint16 bits)."""
+    wb, sb = packed_size(fmt, M, K)
+    src_w = np.ascontiguousarray(src_w)
+    dst_w = np.empty(wb, dtype=np.uint8)
+    dst_s = np.empty(sb // 2, dtype=np.uint16) if sb else None
+    sp = None
+    if src_scales is not None:
+        src_scales = np.ascontiguousarray(src_scales, dtype=np.uint16)
+        sp = src_scales.ctypes.data
+    st = _lib.qgemv_pack(fmt, src_kind, src_w.ctypes.data, sp, M, K, dst_w.ctypes.data,
+                         dst_s.ctypes.data if dst_s is not None else None)
+    _check(st, "qgemv_pack")
+    return dst_w, dst_s
+
+
+# ---------------------------------------------------------------- device side
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t, what: str, dtype=None) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def run(fmt: int, W, scales, x, y, M: int, K: int, batch: int, stream=None) -> None:
+    """y[:batch, :M] = W x (float32), all device tensors; see qgemv.h for layouts.
+
+    W: uint8 (any dtype works: only its bytes are read); scales: int16/uint16
+    binary16 bits or None for bf16; x: bf16 bits (int16/uint16/bfloat16)
+    [batch][K]; y: float32 [batch][M].
+    """
+    import torch
+    wp = _dev_ptr(W, "W")
+    sp = _dev_ptr(scales, "scales") if scales is not None else None
+    xp = _dev_ptr(x, "x", (torch.int16, torch.uint16, torch.bfloat16))
+    yp = _dev_ptr(y, "y", torch.float32)
+    if y.numel() < batch * M or x.numel() < batch * K:
+        raise ValueError("x or y too small for (batch, M, K)")
+    st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, _stream_handle(stream))
+    _check(st, "qgemv_run")
+
+
+def run_ptr(fmt: int, wp: int, sp: Optional[int], xp: int, yp: int, M: int, K: int, batch: int,
+            stream_handle: Optional[int]) -> None:
+    """Raw-pointer form of run() for timing loops (no tensor checks)."""
+    st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, stream_handle)
+    if st != OK:
+        raise QgemvError(st, "qgemv_run")
+
+
+def argmax(logits, V: int, batch: int, ws, idx, stream=None) -> None:
+    """idx[:batch] = first index of the max of each logits row (see qgemv.h)."""
+    import torch
+    lp = _dev_ptr(logits, "logits", torch.float32)
+    wsp = _dev_ptr(ws, "ws", (torch.int64, torch.uint64))
+    ip = _dev_ptr(idx, "idx", torch.int32)
+    if ws.numel() < batch * ARGMAX_WS_WORDS_PER_ROW:
+        raise ValueError("ws too small")
+    st = _lib.qgemv_argmax(lp, V, batch, wsp, ip, _stream_handle(stream))
+    _check(st, "qgemv_argmax")
+
+
+def argmax_workspace(batch: int, device="cuda"):
+    """A zero-filled argmax workspace (the kernel leaves it zero after every call)."""
+    import torch
+    return torch.zeros(batch * ARGMAX_WS_WORDS_PER_ROW, dtype=torch.int64, device=device)
+
+
+def stream_read(buf, nbytes: int, sink, grid: int = 0, unroll: int = 4, stream=None) -> None:
+    import torch
+    bp = _dev_ptr(buf, "buf")
+    sp = _dev_ptr(sink, "sink", (torch.int32, torch.uint32))
+    st = _lib.qgemv_stream_read(bp, nbytes, sp, grid, unroll, _stream_handle(stream))
+    _check(st, "qgemv_stream_read")

@@ -1,0 +1,450 @@
+// Fused-dequantization decode GEMV for CDNA4 (gfx950): y[b][m] = sum_k w(m,k) x[b][k].
+//
+// The decode step reads every weight once and does one multiply-add per
+// weight and batch row, so this kernel is bound by HBM bandwidth ("infer",
+// the roofline discussion; "Writing an LLM inference engine from scratch in
+// Rust", Lesson 1). Everything here serves one goal: stream each weight byte
+// from HBM exactly once, with wide coalesced loads and enough bytes in
+// flight, while keeping the per-byte instruction count well under what the
+// vector ALUs can issue at that rate.
+//
+// Work decomposition
+//   * A row of the weight matrix is a sequence of 16-byte "units" (8 bf16
+//     weights, 16 int8 weights, or 32 4-bit weights). Lane l of a wavefront
+//     loads units l, l+64, l+128, ... of each row it works on, so every
+//     16-byte load instruction of a wave covers 1 KiB of contiguous bytes.
+//   * A wave works on R rows at a time (a "row group") and walks all of K;
+//     waves take row groups in a grid-stride loop, with the next step's
+//     weight loads issued before the current step is computed (register
+//     double buffering), so a wave always has loads in flight.
+//   * x (all batch rows) is staged once per workgroup in LDS as bf16; the
+//     same LDS read feeds the R rows of a group.
+//   * Dequantization happens in registers and is never written back
+//     ("infer", design notes; Rust page, Lesson 2): codes are turned into
+//     packed bf16 pairs and multiplied with packed bf16 activations by
+//     v_dot2_f32_bf16 (two exact products and a float32 add per instruction).
+//     Each group's scale multiplies the group's partial sum once.
+//   * 4-bit codes: with c the nibble moved to bits 6..3 of a byte and 0x41
+//     as the high byte, the bf16 value is 8 + c/2 exactly. The 8 is removed
+//     with the per-unit sum of x, folded into the dot chain's start value:
+//     sum((8 + q/2) x) - 12 sum(x) = (1/2) sum((q - 8) x); the 1/2 is folded
+//     into the scale (exact). This is the Rust page's bias-removal identity
+//     (Lesson 6) with a smaller magic offset so less of the float32
+//     rounding is magnified by the cancellation.
+//   * int8 codes: sign-extended to float32 (exact) and packed to bf16 pairs
+//     by taking the high halves (exact: at most 8 significant bits).
+//   * The per-row reduction over the 64 lanes reduces all R*batch partial
+//     sums together by repeatedly exchanging half of them with the partner
+//     lane (each step halves the number of live values per lane).
+// No MFMA: at batch <= 8 this is a matrix-vector product, not a dense
+// contraction.
+#include <algorithm>
+
+#include "qgemv_internal.h"
+#include "qgemv.h"
+
+namespace qgemv {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+template <int FMT> struct Traits;
+template <> struct Traits<QGEMV_BF16> {
+  static constexpr int kElems = 8;      // weights per 16-byte unit
+  static constexpr int kPairs = 4;      // bf16 pairs per unit (= x dwords per unit)
+  static constexpr int kUnitsPerScale = 0;
+  static constexpr int kUC = 4;         // units per lane per step
+  static constexpr bool kBias = false;
+};
+template <> struct Traits<QGEMV_INT8_G32> {
+  static constexpr int kElems = 16;
+  static constexpr int kPairs = 8;
+  static constexpr int kUnitsPerScale = 2;
+  static constexpr int kUC = 2;
+  static constexpr bool kBias = false;
+};
+template <> struct Traits<QGEMV_Q4_0_G32> {
+  static constexpr int kElems = 32;
+  static constexpr int kPairs = 16;
+  static constexpr int kUnitsPerScale = 1;
+  static constexpr int kUC = 1;
+  static constexpr bool kBias = true;
+};
+template <> struct Traits<QGEMV_INT4_G128> {
+  static constexpr int kElems = 32;
+  static constexpr int kPairs = 16;
+  static constexpr int kUnitsPerScale = 4;
+  static constexpr int kUC = 1;
+  static constexpr bool kBias = true;
+};
+
+// Dword offset (within one batch row of x, stored as bf16 pairs) of the x
+// values that pair with the first and the second half of unit t's pairs.
+template <int FMT>
+__device__ __forceinline__ void x_offsets(int t, int& lo, int& hi) {
+  if constexpr (FMT == QGEMV_BF16) {
+    lo = 4 * t; hi = lo;
+  } else if constexpr (FMT == QGEMV_INT8_G32) {
+    lo = 8 * t; hi = lo + 4;
+  } else if constexpr (FMT == QGEMV_Q4_0_G32) {
+    // block t: low nibbles are elements 32t..32t+15, high nibbles 32t+16..32t+31
+    lo = 16 * t; hi = lo + 8;
+  } else {
+    // block t>>2, quarter c = t&3: low nibbles are elements 128(t>>2)+16c..+15,
+    // high nibbles the same positions + 64
+    lo = 64 * (t >> 2) + 8 * (t & 3); hi = lo + 32;
+  }
+}
+
+// Read the x dwords that pair with unit t from LDS (one batch row).
+template <int FMT>
+__device__ __forceinline__ void read_x(const uint32_t* xb, int t, uint32_t (&xv)[Traits<FMT>::kPairs]) {
+  int lo, hi;
+  x_offsets<FMT>(t, lo, hi);
+  if constexpr (FMT == QGEMV_BF16) {
+    u32x4 a = *reinterpret_cast<const u32x4*>(xb + lo);
+    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+  } else if constexpr (FMT == QGEMV_INT8_G32) {
+    u32x4 a = *reinterpret_cast<const u32x4*>(xb + lo);
+    u32x4 b = *reinterpret_cast<const u32x4*>(xb + hi);
+    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+    xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+  } else {
+    u32x4 a0 = *reinterpret_cast<const u32x4*>(xb + lo);
+    u32x4 a1 = *reinterpret_cast<const u32x4*>(xb + lo + 4);
+    u32x4 b0 = *reinterpret_cast<const u32x4*>(xb + hi);
+    u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + hi + 4);
+    xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+    xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+    xv[8] = b0.x; xv[9] = b0.y; xv[10] = b0.z; xv[11] = b0.w;
+    xv[12] = b1.x; xv[13] = b1.y; xv[14] = b1.z; xv[15] = b1.w;
+  }
+}
+
+// Turn one 16-byte unit of codes into packed bf16 pairs, in the order of the
+// x dwords read_x returns.
+template <int FMT>
+__device__ __forceinline__ void unpack(const u32x4& w, uint32_t (&p)[Traits<FMT>::kPairs]) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (FMT == QGEMV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = wd[i];
+  } else if constexpr (FMT == QGEMV_INT8_G32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // sign-extended bytes -> float32 (exact); a float32 holding an integer of
+      // at most 8 significant bits is exactly its own high half as bf16
+      const float f0 = static_cast<float>(static_cast<int32_t>(wd[i] << 24) >> 24);
+      const float f1 = static_cast<float>(static_cast<int32_t>(wd[i] << 16) >> 24);
+      const float f2 = static_cast<float>(static_cast<int32_t>(wd[i] << 8) >> 24);
+      const float f3 = static_cast<float>(static_cast<int32_t>(wd[i]) >> 24);
+      p[2 * i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                       __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+      p[2 * i + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                           __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+    }
+  } else {
+    // byte j of the unit: low nibble -> element j of the low run,
+    // high nibble -> element j of the high run. bf16 0x41cc with cc = nibble<<3
+    // is 8 + nibble/2.
+    constexpr uint32_t kMagic = 0x41414141u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (wd[i] << 3) & 0x78787878u;
+      const uint32_t hi = (wd[i] >> 1) & 0x78787878u;
+      p[2 * i] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
+      p[2 * i + 1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
+      p[8 + 2 * i] = __builtin_amdgcn_perm(kMagic, hi, 0x04010400u);
+      p[8 + 2 * i + 1] = __builtin_amdgcn_perm(kMagic, hi, 0x04030402u);
+    }
+  }
+}
+
+// Reduce N values per lane over the 64 lanes of a wave. Each step exchanges
+// half of the live values with lane ^ O and keeps the other half, so after
+// log2(N) steps every lane holds one value (index = lane >> (6 - log2 N)),
+// summed over 2^log2(N) lanes; plain butterflies finish the remaining lanes.
+template <int N, int O>
+__device__ __forceinline__ void halve(float* v, int lane) {
+  if constexpr (N > 1) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = upper ? v[i + N / 2] : v[i];
+      const float send = upper ? v[i] : v[i + N / 2];
+      v[i] = keep + __shfl_xor(send, O);
+    }
+    halve<N / 2, O / 2>(v, lane);
+  }
+}
+
+template <int O>
+__device__ __forceinline__ float butterfly(float x) {
+  if constexpr (O >= 1) {
+    x += __shfl_xor(x, O);
+    return butterfly<O / 2>(x);
+  } else {
+    return x;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float reduce_wave(float* v, int lane) {
+  halve<N, 32>(v, lane);
+  return butterfly<32 / N>(v[0]);
+}
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+template <int FMT, int NB, int R>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch) {
+  using T = Traits<FMT>;
+  constexpr int UC = T::kUC;
+  constexpr int P = T::kPairs;
+  extern __shared__ u32x4 lds_v4[];
+  uint32_t* lds = reinterpret_cast<uint32_t*>(lds_v4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int KD = K >> 1;                              // x dwords per batch row
+  const int U = K / T::kElems;                        // 16-byte units per row
+  const size_t row_bytes = static_cast<size_t>(U) * 16;
+  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
+  const int groups = (M + R - 1) / R;
+  const int waves_total = gridDim.x * kWaves;
+  const int nchunk = (U + 64 * UC - 1) / (64 * UC);
+
+  uint32_t* xs = lds;                                        // [NB][KD]
+  float* sxs = reinterpret_cast<float*>(lds + NB * KD);      // [NB][U] (4-bit only)
+
+  u32x4 wv[R][UC];
+  uint32_t sv[R][UC];   // binary16 scale bits, one per 32-bit register
+
+  // Issue the loads of one step (R rows x UC units per lane), branch-free:
+  // lanes past the end of a ragged row re-load the row's last unit (an
+  // in-bounds address on a line the wave reads anyway) and skip it when
+  // computing; rows past M re-load row M-1 and are not stored.
+  auto load_step = [&](int grp, int ch) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(grp * R + r, M - 1);
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(row) * row_bytes);
+#pragma unroll
+      for (int u = 0; u < UC; ++u) {
+        const int t = min(ch * 64 * UC + u * 64 + lane, U - 1);
+        wv[r][u] = __builtin_nontemporal_load(wrow + t);
+        if constexpr (T::kUnitsPerScale > 0)
+          sv[r][u] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
+      }
+    }
+  };
+
+  // ---- stage x. The first chunks are loaded before this wave's first
+  // weight loads are issued, so waiting for them does not wait for weights.
+  constexpr int kXPre = 4;
+  const int row_chunks = K / 8;                      // 16-byte chunks per x row
+  const int nxc = NB * row_chunks;                   // chunks staged (NB rows)
+  const int valid_xc = batch * row_chunks;           // chunks that exist in X
+  u32x4 xpre[kXPre];
+#pragma unroll
+  for (int j = 0; j < kXPre; ++j) {
+    const int i = tid + j * kThreads;
+    xpre[j] = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
+  }
+
+  int grp = blockIdx.x * kWaves + wave;
+  int ch = 0;
+  load_step(min(grp, groups - 1), 0);
+
+#pragma unroll
+  for (int j = 0; j < kXPre; ++j) {
+    const int i = tid + j * kThreads;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (i < nxc) reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? xpre[j] : zero;
+  }
+  for (int i = tid + kXPre * kThreads; i < nxc; i += kThreads) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 v = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
+    reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? v : zero;
+  }
+  __syncthreads();
+
+  if constexpr (T::kBias) {
+    // per-unit sums of x, pre-multiplied by -12 (the dot chain's start value)
+    constexpr uint32_t kOnes = 0x3f803f80u;          // bf16 pair (1.0, 1.0)
+    for (int i = tid; i < NB * U; i += kThreads) {
+      const int b = i / U, t = i - b * U;
+      uint32_t xv[P];
+      read_x<FMT>(xs + b * KD, t, xv);
+      float s = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) s = dot2(xv[p], kOnes, s);
+      sxs[i] = -12.f * s;
+    }
+    __syncthreads();
+  }
+
+  float acc[R][NB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  while (grp < groups) {
+    // compute the step whose loads are in flight
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
+      const int t = ch * 64 * UC + u * 64 + lane;
+      if (t < U) {
+        uint32_t pr[R][P];
+        float dsc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          unpack<FMT>(wv[r][u], pr[r]);
+          if constexpr (FMT == QGEMV_INT8_G32) dsc[r] = half_to_float(static_cast<uint16_t>(sv[r][u]));
+          else if constexpr (T::kBias) dsc[r] = 2.f * half_to_float(static_cast<uint16_t>(sv[r][u]));
+          else dsc[r] = 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          uint32_t xv[P];
+          read_x<FMT>(xs + b * KD, t, xv);
+          const float init = T::kBias ? sxs[b * U + t] : 0.f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if constexpr (FMT == QGEMV_BF16) {
+              float a = acc[r][b];
+#pragma unroll
+              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+              acc[r][b] = a;
+            } else {
+              float a = init;
+#pragma unroll
+              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+              acc[r][b] = __builtin_fmaf(dsc[r], a, acc[r][b]);
+            }
+          }
+        }
+      }
+    }
+
+    const int cur = grp;
+    if (++ch == nchunk) { ch = 0; grp += waves_total; }
+    if (grp < groups) load_step(grp, ch);
+
+    if (ch == 0) {
+      constexpr int V = R * NB;
+      float v[V];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
+      const float res = reduce_wave<V>(v, lane);
+      constexpr int SH = 6 - ilog2(V);
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int idx = lane >> SH;
+        const int r = idx / NB, b = idx % NB;
+        const int row = cur * R + r;
+        if (row < M && b < batch) Y[static_cast<size_t>(b) * M + row] = res;
+      }
+    }
+  }
+}
+
+int round_batch(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
+
+template <int FMT, int NB>
+hipError_t launch_fr(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t st) {
+  const uint8_t* W = static_cast<const uint8_t*>(a.W);
+  switch (R) {
+    case 1: gemv_kernel<FMT, NB, 1><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
+    case 2: gemv_kernel<FMT, NB, 2><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
+    default: gemv_kernel<FMT, NB, 4><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_f(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t st) {
+  switch (round_batch(a.batch)) {
+    case 1: return launch_fr<FMT, 1>(a, R, grid, lds, st);
+    case 2: return launch_fr<FMT, 2>(a, R, grid, lds, st);
+    case 4: return launch_fr<FMT, 4>(a, R, grid, lds, st);
+    default: return launch_fr<FMT, 8>(a, R, grid, lds, st);
+  }
+}
+
+template <int FMT, int NB, int R>
+void allow_big_lds() {
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, NB, R>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
+}  // namespace
+
+FmtInfo fmt_info(int fmt) {
+  switch (fmt) {
+    case QGEMV_BF16: return {1, 8};
+    case QGEMV_INT8_G32: return {32, 16};
+    case QGEMV_Q4_0_G32: return {32, 32};
+    default: return {128, 32};
+  }
+}
+
+size_t gemv_lds_bytes(int fmt, int K, int batch) {
+  const int nb = round_batch(batch);
+  size_t bytes = static_cast<size_t>(nb) * K * 2;
+  if (fmt == QGEMV_Q4_0_G32 || fmt == QGEMV_INT4_G128) bytes += static_cast<size_t>(nb) * (K / 32) * 4;
+  return bytes;
+}
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
+  const FmtInfo fi = fmt_info(a.fmt);
+  const int cus = device_cu_count();
+  const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);
+  // rows per wave step: as many as keep at least two workgroups per CU busy
+  int R = 4;
+  while (R > 1 && (a.M + R - 1) / R < 2 * cus * kWaves) R >>= 1;
+  const int groups = (a.M + R - 1) / R;
+  const int wg_needed = (groups + kWaves - 1) / kWaves;
+  int wg_per_cu = static_cast<int>(std::min<size_t>(8, (160 * 1024) / std::max<size_t>(lds, 1)));
+  if (wg_per_cu < 1) wg_per_cu = 1;
+  const int grid = std::max(1, std::min(wg_needed, cus * wg_per_cu));
+  if (lds > 64 * 1024) {
+    static bool once = [] {
+#define QG_ALLOW(F) allow_big_lds<F, 8, 1>(); allow_big_lds<F, 8, 2>(); allow_big_lds<F, 8, 4>(); \
+                    allow_big_lds<F, 4, 1>(); allow_big_lds<F, 4, 2>(); allow_big_lds<F, 4, 4>(); \
+                    allow_big_lds<F, 2, 1>(); allow_big_lds<F, 2, 2>(); allow_big_lds<F, 2, 4>(); \
+                    allow_big_lds<F, 1, 1>(); allow_big_lds<F, 1, 2>(); allow_big_lds<F, 1, 4>();
+      QG_ALLOW(QGEMV_BF16) QG_ALLOW(QGEMV_INT8_G32) QG_ALLOW(QGEMV_Q4_0_G32) QG_ALLOW(QGEMV_INT4_G128)
+#undef QG_ALLOW
+      return true;
+    }();
+    (void)once;
+  }
+  (void)fi;
+  switch (a.fmt) {
+    case QGEMV_BF16: return launch_f<QGEMV_BF16>(a, R, grid, lds, stream);
+    case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream);
+    case QGEMV_Q4_0_G32: return launch_f<QGEMV_Q4_0_G32>(a, R, grid, lds, stream);
+    default: return launch_f<QGEMV_INT4_G128>(a, R, grid, lds, stream);
+  }
+}
+
+}  // namespace qgemv

@@ -1,0 +1,281 @@
+// C-ABI front end of libqgemv: argument validation, the host-side weight
+// packer/quantizer, and dispatch to the HIP kernels.
+//
+// Every entry point validates everything it can on the host before touching
+// HIP, and reports problems as negative status values (never exceptions).
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "qgemv.h"
+#include "qgemv_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+bool valid_fmt(int fmt) { return fmt >= QGEMV_BF16 && fmt <= QGEMV_INT4_G128; }
+
+int group_of(int fmt) {
+  switch (fmt) {
+    case QGEMV_INT8_G32: return 32;
+    case QGEMV_Q4_0_G32: return 32;
+    case QGEMV_INT4_G128: return 128;
+    default: return 32;   // bf16: K must still be a multiple of 32
+  }
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int fmt, int64_t M, int64_t K) {
+  if (M < 1 || K < 1 || M >= kMaxDim || K >= kMaxDim) return QGEMV_ESHAPE;
+  if (K % group_of(fmt) != 0) return QGEMV_ESHAPE;
+  return QGEMV_OK;
+}
+
+void sizes(int fmt, int64_t M, int64_t K, size_t* w, size_t* s) {
+  const size_t mk = static_cast<size_t>(M) * static_cast<size_t>(K);
+  switch (fmt) {
+    case QGEMV_BF16: *w = 2 * mk; *s = 0; break;
+    case QGEMV_INT8_G32: *w = mk; *s = 2 * (mk / 32); break;
+    case QGEMV_Q4_0_G32: *w = mk / 2; *s = 2 * (mk / 32); break;
+    default: *w = mk / 2; *s = 2 * (mk / 128); break;
+  }
+}
+
+// ---------------------------------------------------------------- binary16
+// Host conversions written from the IEEE 754 binary16 definition:
+// 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+
+double half_to_double(uint16_t h) {
+  const int sign = h >> 15;
+  const int e = (h >> 10) & 0x1F;
+  const int f = h & 0x3FF;
+  double mag;
+  if (e == 0) mag = std::ldexp(static_cast<double>(f), -24);
+  else if (e == 31) mag = f ? NAN : INFINITY;
+  else mag = std::ldexp(static_cast<double>(1024 + f), e - 25);
+  return sign ? -mag : mag;
+}
+
+// double -> binary16, round to nearest with ties to even, overflow to inf.
+// Works on the double's bit pattern: take the 53-bit significand and shift
+// it right to the binary16 quantum of |v|'s binade (2^-24 below 2^-14),
+// rounding the shifted-out bits to nearest-even.
+uint16_t double_to_half(double v) {
+  uint64_t b;
+  std::memcpy(&b, &v, sizeof b);
+  const uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000);
+  const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+  if (mag > 0x7FF0000000000000ull) return 0x7E00;
+  if (mag == 0x7FF0000000000000ull) return sign | 0x7C00;
+  const int biased = static_cast<int>(mag >> 52);
+  if (biased == 0) return sign;                      // double subnormal/zero -> 0
+  int e = biased - 1023;                             // |v| = m * 2^(e-52)
+  const uint64_t m = (mag & ((uint64_t(1) << 52) - 1)) | (uint64_t(1) << 52);
+  const int shift = (e < -14) ? 28 - e : 42;         // keep quantum 2^-24 or 2^(e-10)
+  uint64_t n;
+  if (shift >= 64) {
+    n = 0;
+  } else {
+    n = m >> shift;
+    const uint64_t rem = m & ((uint64_t(1) << shift) - 1);
+    const uint64_t half = uint64_t(1) << (shift - 1);
+    if (rem > half || (rem == half && (n & 1))) ++n;
+  }
+  if (e < -14) return sign | static_cast<uint16_t>(n);   // n == 1024 is the smallest normal
+  if (n == 2048) { n = 1024; ++e; }
+  if (e > 15) return sign | 0x7C00;
+  return sign | static_cast<uint16_t>(((e + 15) << 10) | (n - 1024));
+}
+
+double bf16_to_double(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return static_cast<double>(f);
+}
+
+// Quantize one group of G bf16 weights. Returns false on a range error.
+bool quantize_group(int fmt, const uint16_t* w, int G, uint16_t* d_out, int* q_out) {
+  double v[128];
+  for (int j = 0; j < G; ++j) {
+    v[j] = bf16_to_double(w[j]);
+    if (!std::isfinite(v[j])) return false;
+  }
+  double d_exact;
+  if (fmt == QGEMV_INT8_G32) {
+    double amax = 0.0;
+    for (int j = 0; j < G; ++j) amax = std::fmax(amax, std::fabs(v[j]));
+    d_exact = amax / 127.0;
+  } else {
+    int first = 0;
+    for (int j = 1; j < G; ++j)
+      if (std::fabs(v[j]) > std::fabs(v[first])) first = j;   // strict: first of ties
+    d_exact = v[first] / -8.0;
+  }
+  uint16_t dh = double_to_half(d_exact);
+  if ((dh & 0x7FFF) == 0) dh = 0;                              // a zero scale is +0
+  if ((dh & 0x7C00) == 0x7C00) return false;                   // overflow
+  const double d = half_to_double(dh);
+  *d_out = dh;
+  for (int j = 0; j < G; ++j) {
+    if (fmt == QGEMV_INT8_G32) {
+      double q = (d == 0.0) ? 0.0 : std::nearbyint(v[j] / d);
+      q = std::fmin(127.0, std::fmax(-127.0, q));
+      q_out[j] = static_cast<int>(q);
+    } else {
+      double q = (d == 0.0) ? 8.0 : std::nearbyint(v[j] / d) + 8.0;
+      q = std::fmin(15.0, std::fmax(0.0, q));
+      q_out[j] = static_cast<int>(q);
+    }
+  }
+  return true;
+}
+
+int pack_from_bf16(int fmt, const uint16_t* src, int64_t M, int64_t K, void* dst_w,
+                   uint16_t* dst_s) {
+  if (fmt == QGEMV_BF16) {
+    std::memcpy(dst_w, src, static_cast<size_t>(M) * K * 2);
+    return QGEMV_OK;
+  }
+  const int G = group_of(fmt);
+  const int64_t ng = K / G;
+  int q[128];
+  // validate everything first so that nothing is written on error
+  for (int64_t i = 0; i < M * K; ++i)
+    if (!std::isfinite(bf16_to_double(src[i]))) return QGEMV_ERANGE;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t g = 0; g < ng; ++g) {
+      uint16_t dh;
+      if (!quantize_group(fmt, src + m * K + g * G, G, &dh, q)) return QGEMV_ERANGE;
+    }
+  }
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t g = 0; g < ng; ++g) {
+      uint16_t dh;
+      quantize_group(fmt, src + m * K + g * G, G, &dh, q);
+      dst_s[m * ng + g] = dh;
+      if (fmt == QGEMV_INT8_G32) {
+        int8_t* out = static_cast<int8_t*>(dst_w) + m * K + g * G;
+        for (int j = 0; j < G; ++j) out[j] = static_cast<int8_t>(q[j]);
+      } else {
+        uint8_t* out = static_cast<uint8_t*>(dst_w) + (m * ng + g) * (G / 2);
+        for (int j = 0; j < G / 2; ++j)
+          out[j] = static_cast<uint8_t>(q[j] | (q[j + G / 2] << 4));
+      }
+    }
+  }
+  return QGEMV_OK;
+}
+
+int record_hip(hipError_t e) {
+  if (e == hipSuccess) return QGEMV_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return QGEMV_EHIP;
+}
+
+}  // namespace
+
+namespace qgemv {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace qgemv
+
+extern "C" {
+
+int qgemv_packed_size(int fmt, int64_t M, int64_t K, size_t* w_bytes, size_t* s_bytes) {
+  if (!valid_fmt(fmt) || !w_bytes || !s_bytes) return QGEMV_EINVAL;
+  const int st = check_shape(fmt, M, K);
+  if (st) return st;
+  sizes(fmt, M, K, w_bytes, s_bytes);
+  return QGEMV_OK;
+}
+
+int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_scales, int64_t M,
+               int64_t K, void* dst_w, uint16_t* dst_scales) {
+  if (!valid_fmt(fmt)) return QGEMV_EINVAL;
+  if (src_kind != QGEMV_SRC_CANONICAL && src_kind != QGEMV_SRC_BF16) return QGEMV_EINVAL;
+  if (!src_w || !dst_w) return QGEMV_EINVAL;
+  const bool quantized = fmt != QGEMV_BF16;
+  if (quantized && !dst_scales) return QGEMV_EINVAL;
+  if (quantized && src_kind == QGEMV_SRC_CANONICAL && !src_scales) return QGEMV_EINVAL;
+  const int st = check_shape(fmt, M, K);
+  if (st) return st;
+  size_t wb, sb;
+  sizes(fmt, M, K, &wb, &sb);
+  if (src_kind == QGEMV_SRC_BF16)
+    return pack_from_bf16(fmt, static_cast<const uint16_t*>(src_w), M, K, dst_w, dst_scales);
+  std::memcpy(dst_w, src_w, wb);
+  if (quantized) std::memcpy(dst_scales, src_scales, sb);
+  return QGEMV_OK;
+}
+
+int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+              int64_t M, int64_t K, int batch, void* stream) {
+  if (!valid_fmt(fmt)) return QGEMV_EINVAL;
+  if (!W || !x || !y) return QGEMV_EINVAL;
+  if (fmt != QGEMV_BF16 && !scales) return QGEMV_EINVAL;
+  int st = check_shape(fmt, M, K);
+  if (st) return st;
+  if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
+  if (qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) > 160 * 1024) return QGEMV_ESHAPE;
+  if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return QGEMV_EALIGN;
+  if (fmt != QGEMV_BF16 && !aligned(scales, 4)) return QGEMV_EALIGN;
+  qgemv::GemvArgs a{fmt, W, scales, x, y, static_cast<int>(M), static_cast<int>(K), batch};
+  return record_hip(qgemv::launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
+                 void* stream) {
+  if (!logits || !ws || !idx) return QGEMV_EINVAL;
+  if (V < 1 || V > 0x7FFFFFFF || batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
+  if (!aligned(logits, 4) || !aligned(ws, 8) || !aligned(idx, 4)) return QGEMV_EALIGN;
+  return record_hip(qgemv::launch_argmax(logits, V, batch, ws, idx, static_cast<hipStream_t>(stream)));
+}
+
+int qgemv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
+                      void* stream) {
+  if (!buf || !sink) return QGEMV_EINVAL;
+  if (bytes == 0 || bytes % 16 != 0) return QGEMV_ESHAPE;
+  if (grid < 0 || grid > 1 << 20) return QGEMV_ESHAPE;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16) return QGEMV_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QGEMV_EALIGN;
+  if (grid == 0) grid = 2048;
+  return record_hip(qgemv::launch_stream_read(buf, bytes, sink, grid, unroll,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+const char* qgemv_status_str(int status) {
+  switch (status) {
+    case QGEMV_OK: return "QGEMV_OK";
+    case QGEMV_EINVAL: return "QGEMV_EINVAL: null pointer or unknown format/kind";
+    case QGEMV_ESHAPE: return "QGEMV_ESHAPE: unsupported shape or batch";
+    case QGEMV_EALIGN: return "QGEMV_EALIGN: misaligned pointer";
+    case QGEMV_ERANGE: return "QGEMV_ERANGE: non-finite weight or binary16 scale overflow";
+    case QGEMV_EHIP: return "QGEMV_EHIP: HIP call failed";
+    default: return "QGEMV: unknown status";
+  }
+}
+
+int qgemv_last_hip_error(void) { return g_last_hip_error; }
+
+const char* qgemv_version(void) { return "qgemv 0.1.0 gfx950"; }
+
+}  // extern "C"

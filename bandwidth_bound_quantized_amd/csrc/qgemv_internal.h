@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI front end (qgemv_api.cpp) and the
+// HIP kernel translation units. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+// Per-format geometry of one 16-byte "unit" of a weight row: the amount of
+// code bytes one lane loads with a single 16-byte load.
+//   bf16      : 8 weights per unit
+//   int8-g32  : 16 weights per unit, two units per scale group
+//   4-bit g32 : 32 weights per unit (one whole block)
+//   4-bit g128: 32 weights per unit, four units per scale group
+struct FmtInfo {
+  int group;          // weights per scale (1 for bf16)
+  int elems_per_unit; // weights per 16 code bytes
+};
+
+FmtInfo fmt_info(int fmt);
+
+// Launch-time description of one GEMV.
+struct GemvArgs {
+  int fmt;
+  const void* W;
+  const uint16_t* scales;
+  const uint16_t* x;
+  float* y;
+  int M;
+  int K;
+  int batch;
+};
+
+// Bytes of LDS the GEMV kernel stages per workgroup for this shape
+// (x as bf16 for the compiled batch, plus per-unit x sums for 4-bit formats).
+size_t gemv_lds_bytes(int fmt, int K, int batch);
+
+// Launch the GEMV on `stream`. Shapes have been validated by the caller.
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+
+// Launch the argmax (one kernel). ws: batch * 129 u64 words, zero on entry.
+hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
+                         hipStream_t stream);
+
+// Streaming-read measurement kernel.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
+                              hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+constexpr int kArgmaxSlices = 128;   // max workgroups per batch row in the argmax
+
+}  // namespace qgemv

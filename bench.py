@@ -1,0 +1,306 @@
+"""Bench: fused-dequant decode GEMV throughput on one MI355X (gfx950).
+
+One "step" is one pass of the whole hot path over one batch: every GEMV of
+the workload (qgemv_run) and, where the workload ends in an LM head, the
+argmax of its logits (qgemv_argmax). The default workload is the Q4_0-g32
+GEMV set at TinyLlama-1.1B decode shapes (qkv 2560x2048, o 2048x2048,
+gate_up 11264x2048, down 2048x5632, lm_head 32000x2048) at batch 1, plus
+the argmax over the 32000 logits.
+
+Inputs are synthetic and seeded (synth), resident in HBM before timing, and
+rotated through >= 1 GiB of distinct device copies so that the 256 MB
+Infinity Cache cannot serve them. The timed steps are captured once in a
+HIP graph (the decode step of the infer page is a CUDA graph too) and
+replayed; events on the launch stream bracket exactly --steps steps.
+
+Reported (one JSON line):
+  value            algorithmic bytes per step / time per step (GB/s)
+  roofline         dominant kernel (largest bytes per launch): its bytes per
+                   launch / its average launch duration, against 8 TB/s
+  measured_peak    best rate of the streaming-read kernel over 4 GiB
+  cpu_baseline     the fp64 CPU oracle on one step, one thread
+Algorithmic bytes per GEMV = code bytes + scale bytes + x (2*B*K) + y (4*B*M);
+argmax = 4*B*V read + 4*B written.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--batch", type=int, default=None)
+    p.add_argument("--rotate-gib", type=float, default=1.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peak", action="store_true")
+    p.add_argument("--peak-gib", type=float, default=4.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--per-kernel", action="store_true", help="also time every GEMV of the step alone")
+    return p.parse_args()
+
+
+def gemv_bytes(qg, fmt, M, K, B):
+    w, s = qg.packed_size(fmt, M, K)
+    return w + s + 2 * B * K + 4 * B * M
+
+
+class Workload:
+    """Device-resident inputs for one workload, replicated n_sets times."""
+
+    def __init__(self, qg, torch, cfg, B, rotate_bytes):
+        self.qg, self.torch, self.cfg, self.B = qg, torch, cfg, B
+        self.gemvs = synth.make_workload(cfg, B)
+        self.has_argmax = synth.WORKLOAD_ARGMAX[cfg]
+        self.bytes = [gemv_bytes(qg, g.fmt, g.M, g.K, B) for g in self.gemvs]
+        self.argmax_bytes = 4 * B * self.gemvs[-1].M + 4 * B if self.has_argmax else 0
+        self.step_bytes = sum(self.bytes) + self.argmax_bytes
+        resident = sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0) for g in self.gemvs)
+        self.n_sets = max(1, math.ceil(rotate_bytes / resident))
+        dev = "cuda"
+        self.sets = []
+        base = []
+        for g in self.gemvs:
+            W = torch.from_numpy(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8)).to(dev)
+            S = torch.from_numpy(g.s.reshape(-1).view(np.int16)).to(dev) if g.s is not None else None
+            X = torch.from_numpy(g.x.view(np.int16)).to(dev)
+            base.append((W, S, X))
+        for i in range(self.n_sets):
+            items = []
+            for (W, S, X), g in zip(base, self.gemvs):
+                Wi = W if i == 0 else W.clone()
+                Si = None if S is None else (S if i == 0 else S.clone())
+                Xi = X if i == 0 else X.clone()
+                Y = torch.empty((B, g.M), dtype=torch.float32, device=dev)
+                items.append((Wi, Si, Xi, Y))
+            ws = qg.argmax_workspace(B) if self.has_argmax else None
+            idx = torch.empty(B, dtype=torch.int32, device=dev) if self.has_argmax else None
+            self.sets.append((items, ws, idx))
+        torch.cuda.synchronize()
+        # raw pointers for the launch loop (argument marshalling only)
+        self.ptrs = []
+        for items, ws, idx in self.sets:
+            p = [(W.data_ptr(), None if S is None else S.data_ptr(), X.data_ptr(), Y.data_ptr())
+                 for W, S, X, Y in items]
+            self.ptrs.append((p, ws.data_ptr() if ws is not None else None,
+                              idx.data_ptr() if idx is not None else None))
+
+    def step(self, i, stream_handle):
+        qg = self.qg
+        p, wsp, ip = self.ptrs[i % self.n_sets]
+        for (wp, sp, xp, yp), g in zip(p, self.gemvs):
+            qg.run_ptr(g.fmt, wp, sp, xp, yp, g.M, g.K, self.B, stream_handle)
+        if self.has_argmax:
+            st = qg.lib().qgemv_argmax(p[-1][3], self.gemvs[-1].M, self.B, wsp, ip, stream_handle)
+            if st != qg.OK:
+                raise qg.QgemvError(st, "qgemv_argmax")
+
+    def launch_one(self, j, i, stream_handle):
+        g = self.gemvs[j]
+        wp, sp, xp, yp = self.ptrs[i % self.n_sets][0][j]
+        self.qg.run_ptr(g.fmt, wp, sp, xp, yp, g.M, g.K, self.B, stream_handle)
+
+
+def capture(torch, fn, count):
+    """Capture fn(i) for i in range(count) into one graph on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0, s.cuda_stream)          # eager warm call (loads code objects)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(count):
+            fn(i, h)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps=1):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_peak(qg, torch, gib):
+    """Best streaming-read rate over a gib-GiB buffer, sweeping grid and loads in flight."""
+    nbytes = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
+    best = (0.0, None)
+    sweep = []
+    for grid_per_cu in (4, 8, 16, 32):
+        for unroll in (2, 4, 8, 16):
+            grid = grid_per_cu * cus
+            h = torch.cuda.current_stream().cuda_stream
+            qg.stream_read(buf, nbytes, sink, grid=grid, unroll=unroll)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            times = []
+            for _ in range(5):
+                e0.record()
+                qg.lib().qgemv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, h)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            sweep.append({"grid": grid, "unroll": unroll, "GBps": round(gbps, 1)})
+            if gbps > best[0]:
+                best = (gbps, {"grid": grid, "unroll": unroll, "ms": ms})
+    del buf
+    torch.cuda.empty_cache()
+    return best[0], best[1], sweep
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle (fp64 dequantize + fp64 GEMV + argmax) on whole steps, one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            last = None
+            for g in wl.gemvs:
+                last, _ = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K)
+            if wl.has_argmax:
+                oracle.argmax_ref(last.astype(np.float32))
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or steps >= 50:
+                break
+    return steps, el
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
+                          "of the GEMV is described in DESIGN.md but not built",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    import bandwidth_bound_quantized_amd as qg
+
+    cfg = args.workload
+    B = args.batch if args.batch is not None else synth.WORKLOAD_BATCHES[cfg][0]
+    torch.cuda.set_device(0)
+    wl = Workload(qg, torch, cfg, B, args.rotate_gib * (1 << 30))
+    print(f"[bench] workload {cfg} B={B}: {len(wl.gemvs)} GEMVs, {wl.step_bytes} B/step, "
+          f"{wl.n_sets} rotation sets", file=sys.stderr, flush=True)
+
+    # ---- timed steps (graph of exactly `steps` steps, rotating through the sets)
+    g_warm = capture(torch, wl.step, max(1, args.warmup))
+    time_graph(torch, g_warm)
+    g_steps = capture(torch, wl.step, args.steps)
+    ms_total = time_graph(torch, g_steps)
+    ms_per_step = ms_total / args.steps
+    value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # ---- dominant kernel: the GEMV with the most bytes per launch, timed alone
+    dom = int(np.argmax(wl.bytes))
+    n_dom = max(wl.n_sets * 4, 64)
+    g_dom = capture(torch, lambda i, h: wl.launch_one(dom, i, h), n_dom)
+    time_graph(torch, g_dom)
+    dom_us = time_graph(torch, g_dom, reps=3) * 1e3 / n_dom
+    dom_gbps = wl.bytes[dom] / (dom_us * 1e-6) / 1e9
+
+    per_kernel = []
+    if args.per_kernel:
+        for j, gm in enumerate(wl.gemvs):
+            n = max(wl.n_sets * 4, 64)
+            gj = capture(torch, lambda i, h, j=j: wl.launch_one(j, i, h), n)
+            time_graph(torch, gj)
+            us = time_graph(torch, gj, reps=3) * 1e3 / n
+            per_kernel.append({"name": gm.name, "M": gm.M, "K": gm.K, "us": round(us, 3),
+                               "GBps": round(wl.bytes[j] / (us * 1e-6) / 1e9, 1)})
+            del gj
+
+    peak = None
+    if not args.no_peak:
+        peak_gbps, peak_cfg, sweep = measure_peak(qg, torch, args.peak_gib)
+        peak = {"GBps": round(peak_gbps, 1), "config": peak_cfg, "buffer_GiB": args.peak_gib}
+        print(f"[bench] measured streaming-read peak {peak_gbps:.1f} GB/s {peak_cfg}",
+              file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        steps, el = cpu_baseline(wl, args.cpu_seconds)
+        cpu = {"value": round(wl.step_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{steps} whole step(s) of workload {cfg} (all {len(wl.gemvs)} GEMVs"
+                         f"{' + argmax' if wl.has_argmax else ''}), fp64, one thread, {el:.1f} s"}
+
+    names = {1: "bf16_gemv_2048x2048", 2: "q4_0_g32_tinyllama_gemv_set+argmax",
+             3: "int8_g32_llama32_1b_gemv_set", 4: "q4_0_g32_tinyllama_decode_step_89_gemvs+argmax",
+             5: "int4_g128_ffn+int8_g32_lm_head+argmax"}
+    dtypes = {1: "bf16", 2: "q4_0", 3: "int8", 4: "q4_0", 5: "int4/int8"}
+    out = {
+        "metric": "fused-dequant GEMV achieved HBM GB/s and % of peak (bf16/int8/Q4_0, batch 1)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtypes[cfg],
+        "data": "synthetic (seeded; same shapes and value distributions as the workload)",
+        "config": {"workload": names[cfg], "batch": B,
+                   "gemvs": [[g.name, g.M, g.K] for g in wl.gemvs][:6] + (
+                       [["...", len(wl.gemvs)]] if len(wl.gemvs) > 6 else []),
+                   "bytes_per_step": wl.step_bytes, "rotation_sets": wl.n_sets,
+                   "rotation_bytes": wl.n_sets * sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0)
+                                                     for g in wl.gemvs),
+                   "timing": "HIP graph of exactly `steps` steps, events on the launch stream"},
+        "pct_of_spec_8TBps": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"qgemv_run {wl.gemvs[dom].name} {wl.gemvs[dom].M}x{wl.gemvs[dom].K}",
+                     "bytes_per_launch": wl.bytes[dom], "avg_launch_us": round(dom_us, 3),
+                     "launches": n_dom},
+        "cpu_baseline": cpu,
+    }
+    if peak is not None:
+        out["measured_peak"] = peak
+        out["pct_of_measured_peak"] = round(100 * value / peak["GBps"], 2)
+        out["roofline"]["pct_of_measured_peak"] = round(100 * dom_gbps / peak["GBps"], 2)
+    if per_kernel:
+        out["per_kernel"] = per_kernel
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * qgemv.h - C ABI of the fused-dequantization decode GEMV library (libqgemv.so)
+ *
+ * The operation: y = W x for one decode step, batch 1..8, with the weight
+ * dequantization done in registers while the weights stream from HBM. Decode
+ * reads every weight once and does one multiply-add with it, so the kernel
+ * is bound by HBM bandwidth and the only lever is the number of weight bytes
+ * ("Writing an LLM inference engine from scratch in Rust", Lesson 1; "infer",
+ * the roofline discussion and the quantized-GEMV table).
+ *
+ * Weight formats (planar: codes in one array, binary16 scales in another,
+ * both row-major; this is also the device layout qgemv_run reads):
+ *   QGEMV_BF16       W: uint16 bf16 bits [M][K]; no scales.
+ *   QGEMV_INT8_G32   W: int8 [M][K]; scales: binary16 [M][K/32];
+ *                    weight = code * scale (a 32-value int8 block with one
+ *                    scale, as in the Rust page's Lesson 6 and llama.cpp's
+ *                    Q8_0 cited on the infer page's perplexity notes).
+ *   QGEMV_Q4_0_G32   W: uint8 [M][K/32][16]; scales: binary16 [M][K/32];
+ *                    element j of a block is the low nibble of byte j,
+ *                    element j+16 the high nibble; weight = (code-8)*scale
+ *                    (Rust page, Lessons 1 and 6: 4.5 bits per weight, stored
+ *                    value = weight + 8).
+ *   QGEMV_INT4_G128  W: uint8 [M][K/128][64]; scales: binary16 [M][K/128];
+ *                    element j of a block is the low nibble of byte j,
+ *                    element j+64 the high nibble; weight = (code-8)*scale
+ *                    ("infer", g128 rows of the decode and perplexity tables;
+ *                    the nibble order is this library's reading, the same
+ *                    half-split as Q4_0).
+ * Activations x: bf16 bits [batch][K]. Output y: float32 [batch][M].
+ *
+ * Conventions for every entry point:
+ *   - returns QGEMV_OK (0) or a negative status; on error nothing has been
+ *     launched and no output has been written (errors are values, never
+ *     exceptions or aborts, as in the Mini Inference Engine page's block
+ *     pool, whose out-of-memory result is a sentinel);
+ *   - the library never allocates device memory, never frees, never keeps a
+ *     caller pointer past the call and never synchronizes a stream;
+ *   - the caller owns every buffer; device entry points run asynchronously
+ *     on the caller's stream (hipStream_t passed as void*, NULL = the null
+ *     stream); reading W and scales from several streams at once is safe;
+ *   - thread-safe; the HIP error of the last failed launch on the calling
+ *     thread is available from qgemv_last_hip_error().
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QGEMV_BF16 = 0,
+  QGEMV_INT8_G32 = 1,
+  QGEMV_Q4_0_G32 = 2,
+  QGEMV_INT4_G128 = 3
+};
+
+/* source kinds for qgemv_pack */
+enum {
+  QGEMV_SRC_CANONICAL = 0, /* codes + binary16 scales already in the layout above */
+  QGEMV_SRC_BF16 = 1       /* bf16 weights [M][K]: quantize them */
+};
+
+enum {
+  QGEMV_OK = 0,
+  QGEMV_EINVAL = -1, /* null pointer, unknown format or source kind */
+  QGEMV_ESHAPE = -2, /* M < 1, K not a positive multiple of the group (32, or
+                        128 for int4-g128), batch outside 1..8, V < 1, or K
+                        beyond what one workgroup's LDS can stage */
+  QGEMV_EALIGN = -3, /* W, x or y not 16-byte aligned; scales or logits not
+                        4-byte aligned; ws not 8-byte aligned */
+  QGEMV_ERANGE = -4, /* quantize: a non-finite weight, or a scale whose
+                        binary16 rounding overflows (|scale| > 65504) */
+  QGEMV_EHIP = -5    /* a HIP call failed; see qgemv_last_hip_error() */
+};
+
+/* Largest batch qgemv_run accepts (decode verifies up to 8 tokens per pass,
+ * the Rust page's speculative-decoding section). */
+#define QGEMV_MAX_BATCH 8
+
+/*
+ * qgemv_packed_size - bytes of the device layout of an M x K matrix.
+ * Host only, no HIP calls. *w_bytes gets the code bytes (2MK, MK, MK/2, MK/2
+ * for bf16, int8-g32, Q4_0-g32, int4-g128), *s_bytes the scale bytes
+ * (0 for bf16, else 2*M*K/G). These are the byte counts the pages use for
+ * their bandwidth figures (4.5 bits per weight for Q4_0; "infer"'s per-token
+ * weight totals). Errors: EINVAL (null out-pointer, bad fmt), ESHAPE.
+ */
+int qgemv_packed_size(int fmt, int64_t M, int64_t K, size_t* w_bytes, size_t* s_bytes);
+
+/*
+ * qgemv_pack - build the device layout in host memory (host only, no HIP
+ * calls; upload the result with any copy routine).
+ *   src_kind CANONICAL: src_w / src_scales are codes and binary16 scales in
+ *     the layout above; they are validated and copied. For bf16, src_scales
+ *     and dst_scales are ignored (may be NULL).
+ *   src_kind BF16: src_w is bf16 bits [M][K]; for a quantized format each
+ *     group is quantized (src_scales ignored): 4-bit formats take the
+ *     group's element of largest magnitude with its sign, m, and set
+ *     scale = binary16(m / -8) so that m maps to code 0 (Rust page, "Is the
+ *     4-bit model still good?"; "infer", design notes); int8-g32 sets
+ *     scale = binary16(max|w| / 127). Then code = round-half-even(w / scale)
+ *     (+8 for 4-bit), clamped to [0,15] or [-127,127]; ties in |w| go to the
+ *     first element; a scale that rounds to zero is stored as +0 with every
+ *     code 8 (4-bit) or 0 (int8). The division is done in double precision
+ *     after the scale has been rounded to binary16.
+ * dst_w must hold qgemv_packed_size's w_bytes, dst_scales its s_bytes.
+ * Errors: EINVAL, ESHAPE, ERANGE (BF16 source only). Deterministic.
+ */
+int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_scales,
+               int64_t M, int64_t K, void* dst_w, uint16_t* dst_scales);
+
+/*
+ * qgemv_run - y[b][m] = sum_k weight(m,k) * x[b][k], 0 <= b < batch.
+ * Device pointers. W / scales in the layout above (scales may be NULL for
+ * bf16); x: bf16 [batch][K]; y: float32 [batch][M], overwritten (not
+ * accumulated). Accumulation is float32; each 32-weight group's scale is
+ * applied once to the group's partial sum. 1 <= batch <= 8, M >= 1 (any
+ * value), K a multiple of 32 (of 128 for int4-g128) such that x fits in
+ * one workgroup's LDS: nb * K * 2 bytes (plus nb * K / 8 for the 4-bit
+ * formats) <= 163840, nb = batch rounded up to 1, 2, 4 or 8 (e.g. 4-bit:
+ * K <= 9632 at batch 5..8, K <= 77088 at batch 1; bf16/int8: K <= 10240 at
+ * batch 5..8).
+ * Alignment: W, x, y 16 bytes; scales 4 bytes.
+ * Asynchronous on `stream`; no allocation, no synchronization.
+ */
+int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+              int64_t M, int64_t K, int batch, void* stream);
+
+/* u64 words of workspace qgemv_argmax needs per batch row */
+#define QGEMV_ARGMAX_WS_WORDS_PER_ROW 129
+
+/*
+ * qgemv_argmax - greedy token: idx[b] = the first index of the largest
+ * logits[b][v] over 0 <= v < V ("infer", the decode pipeline figure and the
+ * per-kernel table's argmax row; its tests cover ties). Ties go to the lowest
+ * index; -0.0 equals +0.0; if a row holds a NaN the result is the index of
+ * its first NaN (NumPy argmax semantics); all -inf gives 0.
+ * Device pointers: logits float32 [batch][V] (4-byte aligned), idx int32
+ * [batch], ws: batch * QGEMV_ARGMAX_WS_WORDS_PER_ROW u64 words (8-byte
+ * aligned), owned by the caller. ws must be all zero before its first use;
+ * every call leaves it all zero again, so one zero-fill at allocation time
+ * suffices. Calls that may run concurrently need distinct ws buffers.
+ * 1 <= batch <= 8, 1 <= V <= 2^31 - 1. One kernel launch; asynchronous.
+ */
+int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
+                 void* stream);
+
+/*
+ * qgemv_stream_read - measurement helper: read `bytes` bytes of device
+ * memory at `buf` once with 16-byte loads and write one checksum word per
+ * workgroup to sink[0 .. grid-1] (so the reads cannot be elided). This is the
+ * streaming-read kernel whose best rate is the measured HBM peak that GEMV
+ * bandwidth is reported against (the infer page reports its GEMVs against a
+ * streaming-read peak it measured itself). grid: workgroups (0 = 2048),
+ * unroll: 16-byte loads in flight per thread per iteration (1, 2, 4, 8 or
+ * 16). buf 16-byte aligned, bytes a multiple of 16.
+ */
+int qgemv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
+                      void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* qgemv_status_str(int status);
+
+/* hipError_t of the last HIP failure on the calling thread (0 if none). */
+int qgemv_last_hip_error(void);
+
+/* Library version, e.g. "qgemv 0.1.0 gfx950". */
+const char* qgemv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

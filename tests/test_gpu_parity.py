@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: every output finite and |y - y_ref| <= 1e-3 * sum|w x| + 1e-5; hand-built
+blocks and one-hot probes bit-exact; argmax bit-exact against the oracle's
+argmax of the GPU's own logits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import bandwidth_bound_quantized_amd as qg  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from helpers import build_case, load_json  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dev(a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def gpu_gemv(fmt, w, s, x, M, K, B, y_fill=float("nan")):
+    Wd = dev(np.ascontiguousarray(w).reshape(-1).view(np.uint8))
+    Sd = dev(s.reshape(-1)) if s is not None else None
+    Xd = dev(np.ascontiguousarray(x).reshape(B, K))
+    Yd = torch.full((B, M), y_fill, dtype=torch.float32, device=DEV)
+    print(f"[gpu] qgemv_run fmt={qg.FMT_NAMES[fmt]} M={M} K={K} B={B}", flush=True)
+    qg.run(fmt, Wd, Sd, Xd, Yd, M, K, B)
+    torch.cuda.synchronize()
+    return Yd.cpu().numpy()
+
+
+def assert_parity(fmt, w, s, x, M, K, B, y, rows=None, what=""):
+    y_ref, a_ref = oracle.gemv_ref(fmt, w, s, x, M, K, rows=rows)
+    yg = y if rows is None else y[:, rows]
+    rep = oracle.parity_report(yg, y_ref, a_ref)
+    assert rep["ok"], f"{what} {rep}"
+    return rep
+
+
+def sample_rows(M, n=1536, seed=0):
+    if M <= 4096:
+        return None
+    rng = np.random.default_rng(seed)
+    r = np.concatenate([np.arange(64), np.arange(M - 64, M), rng.choice(M, n, replace=False)])
+    return np.unique(r)
+
+
+# ------------------------------------------------------------ hand blocks
+HAND = load_json("hand_blocks.json")["cases"]
+
+
+@pytest.mark.parametrize("case", HAND, ids=[c["name"] for c in HAND])
+def test_hand_built_blocks_exact(case):
+    fmt, M, K, w, s, x, y_exact = build_case(case)
+    B = x.shape[0]
+    y = gpu_gemv(fmt, w, s, x, M, K, B)
+    want = np.array([[float(v) for v in row] for row in y_exact], dtype=np.float64)
+    assert (y.astype(np.float64) == want).all(), (case["name"], y, want)
+
+
+# -------------------------------------------------------- workload configs
+def _workload_cases():
+    cases = []
+    for cfg in (1, 2, 3, 5):
+        for B in synth.WORKLOAD_BATCHES[cfg]:
+            for sp in synth.workload_specs(cfg):
+                cases.append((cfg, B, sp))
+    return cases
+
+
+@pytest.mark.parametrize("cfg,B,sp", _workload_cases(),
+                         ids=[f"cfg{c}-B{b}-{s.name}" for c, b, s in _workload_cases()])
+def test_workload_gemv_parity(cfg, B, sp):
+    g = synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+    y = gpu_gemv(g.fmt, g.w, g.s, g.x, g.M, g.K, B)
+    assert np.isfinite(y).all()
+    assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"cfg{cfg} {sp.name}")
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_decode_step_stream_layers_parity(B):
+    """The 89-GEMV TinyLlama decode-step stream: two full layers and the LM head."""
+    specs = synth.workload_specs(4)
+    pick = [s for s in specs if s.name.startswith("L0.") or s.name.startswith("L21.")] + [specs[-1]]
+    for sp in pick:
+        g = synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+        y = gpu_gemv(g.fmt, g.w, g.s, g.x, g.M, g.K, B)
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=sp.name)
+
+
+# ------------------------------------------------------------ exactness
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+def test_onehot_probes_bit_exact(fmt):
+    """x = e_k: y[b, m] = W_hat[m, k_b] exactly (one product, every other term 0)."""
+    M, K, B = 300, 1024, 8
+    g = synth.make_gemv("t", fmt, M, K, B, 8, fmt, "o")
+    rng = np.random.default_rng(fmt)
+    ks = rng.choice(K, B, replace=False)
+    ks[0], ks[1] = 0, K - 1
+    x = np.zeros((B, K), np.uint16)
+    x[np.arange(B), ks] = 0x3F80
+    y = gpu_gemv(fmt, g.w, g.s, x, M, K, B)
+    W_hat = oracle.dequantize(fmt, g.w, g.s, K)
+    want = W_hat[:, ks].T.astype(np.float32)
+    assert (y == want).all()
+
+
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("M,K", [(1, 128), (63, 256), (65, 384), (1000, 5632), (7, 9216)])
+def test_ragged_shapes_all_batches(fmt, M, K):
+    if K % synth.GROUP[fmt]:
+        K = (K // 128 + 1) * 128
+    for B in range(1, 9):
+        nb = 1 if B == 1 else 2 if B == 2 else 4 if B <= 4 else 8
+        lds = nb * K * 2 + (nb * K // 8 if fmt in (qg.Q4_0_G32, qg.INT4_G128) else 0)
+        if lds > 160 * 1024:
+            continue
+        g = synth.make_gemv("t", fmt, M, K, B, 7, M % 997, "down")
+        y = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B)
+        assert_parity(fmt, g.w, g.s, g.x, M, K, B, y, what=f"M={M} K={K} B={B}")
+
+
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+def test_zero_weights_random_x(fmt):
+    """All weights zero (codes 8 for 4-bit): every output within 1e-5 of 0."""
+    M, K, B = 256, 5632 if fmt != qg.INT4_G128 else 5632 - 5632 % 128, 2
+    g = synth.make_gemv("t", fmt, M, K, B, 7, 5, "o")
+    w = np.zeros_like(g.w)
+    if fmt in (qg.Q4_0_G32, qg.INT4_G128):
+        w[:] = 0x88
+    s = None if g.s is None else np.full_like(g.s, 0x1D1F)    # ~0.005, the largest generated scale
+    y = gpu_gemv(fmt, w, s, g.x, M, K, B)
+    assert (np.abs(y) <= 1e-5).all(), np.abs(y).max()
+
+
+def test_output_fully_written_and_guards_intact():
+    fmt, M, K, B = qg.Q4_0_G32, 1003, 2048, 3
+    g = synth.make_gemv("t", fmt, M, K, B, 7, 11, "qkv")
+    Wd = dev(g.w.reshape(-1).view(np.uint8))
+    Sd = dev(g.s.reshape(-1))
+    Xd = dev(g.x)
+    guard = 256
+    buf = torch.full((B * M + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    buf[:guard] = 12345.0
+    buf[-guard:] = -6789.0
+    Yd = buf[guard:guard + B * M]
+    assert Yd.data_ptr() % 16 == 0
+    qg.run(fmt, Wd, Sd, Xd, Yd, M, K, B)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert (h[:guard] == 12345.0).all() and (h[-guard:] == -6789.0).all()
+    y = h[guard:guard + B * M].reshape(B, M)
+    assert np.isfinite(y).all()
+    assert_parity(fmt, g.w, g.s, g.x, M, K, B, y)
+
+
+def test_repeat_runs_bitwise_identical():
+    fmt, M, K, B = qg.INT8_G32, 4096, 2048, 4
+    g = synth.make_gemv("t", fmt, M, K, B, 7, 12, "o")
+    a = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B)
+    b = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B, y_fill=0.0)
+    assert (a.view(np.uint32) == b.view(np.uint32)).all()
+
+
+def test_pack_bf16_then_run():
+    """qgemv_pack's quantizer output feeds qgemv_run; result within the GEMV tolerance of
+    the oracle run on the same codes (and the codes equal the oracle quantizer's)."""
+    rng = np.random.default_rng(4)
+    M, K, B = 512, 2048, 2
+    wbf = synth.bf16_normal(rng, (M, K), 0.02)
+    x = synth.bf16_normal(rng, (B, K), 1.0)
+    for fmt in (qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128):
+        codes, scales = qg.pack(fmt, qg.SRC_BF16, wbf, None, M, K)
+        y = gpu_gemv(fmt, codes, scales, x, M, K, B)
+        o_codes, o_scales = oracle.quantize_from_bf16(fmt, wbf, M, K)
+        assert_parity(fmt, o_codes, o_scales, x, M, K, B, y)
+
+
+# ------------------------------------------------------------------ argmax
+def gpu_argmax(logits: np.ndarray, ws=None):
+    B, V = logits.shape
+    L = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(DEV)
+    ws = qg.argmax_workspace(B) if ws is None else ws
+    idx = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    print(f"[gpu] qgemv_argmax V={V} B={B}", flush=True)
+    qg.argmax(L, V, B, ws, idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), ws
+
+
+def _argmax_cases():
+    rng = np.random.default_rng(21)
+    cases = {}
+    cases["random_128256x8"] = rng.standard_normal((8, 128256)).astype(np.float32)
+    cases["random_32000x1"] = rng.standard_normal((1, 32000)).astype(np.float32)
+    cases["ties_planted"] = synth.f32_logits_with_ties(rng, 8, 128256)
+    t = rng.standard_normal((4, 128256)).astype(np.float32)
+    # equal maxima straddling a slice boundary (2048-element slices), a wave
+    # boundary, and the first/last elements
+    for b, pos in enumerate([(2047, 2048), (63, 64), (0, 128255), (4095, 6143, 100000)]):
+        t[b, list(pos)] = 10.0
+    cases["ties_boundaries"] = t
+    n = rng.standard_normal((3, 5000)).astype(np.float32)
+    n[0, 4000] = np.nan; n[0, 17] = np.nan                 # first NaN wins
+    n[1, 3] = np.inf; n[1, 4999] = np.inf
+    n[2, 2500] = np.nan; n[2, 10] = np.inf
+    cases["nan_inf"] = n
+    z = np.full((2, 3000), -1.0, np.float32)
+    z[0, 5] = -0.0; z[0, 9] = 0.0                          # -0.0 ties +0.0 -> 5
+    z[1, 7] = 0.0; z[1, 2] = -0.0                          # -> 2
+    cases["signed_zeros"] = z
+    cases["all_neg_inf"] = np.full((2, 777), -np.inf, np.float32)
+    cases["tiny_V"] = rng.standard_normal((8, 1)).astype(np.float32)
+    cases["V7"] = np.array([[1, 5, 5, 2, 0, 5, 1]] * 2, np.float32)
+    cases["large_V"] = rng.standard_normal((1, 300001)).astype(np.float32)
+    return cases
+
+
+ARGMAX_CASES = _argmax_cases()
+
+
+@pytest.mark.parametrize("name", sorted(ARGMAX_CASES))
+def test_argmax_bit_exact(name):
+    logits = ARGMAX_CASES[name]
+    idx, ws = gpu_argmax(logits)
+    assert (idx == oracle.argmax_ref(logits)).all(), (idx, oracle.argmax_ref(logits))
+    assert (ws.cpu().numpy() == 0).all()     # workspace returned to zero
+
+
+def test_argmax_workspace_reuse_many_calls():
+    rng = np.random.default_rng(3)
+    ws = qg.argmax_workspace(8)
+    for i in range(20):
+        V = int(rng.integers(1, 200000))
+        B = int(rng.integers(1, 9))
+        logits = rng.standard_normal((B, V)).astype(np.float32)
+        idx, ws = gpu_argmax(logits, ws)
+        assert (idx == oracle.argmax_ref(logits)).all()
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_lm_head_then_argmax_on_gpu_logits(B):
+    """int8-g32 LM head 128256x2048 then argmax, all on the GPU; the argmax must equal the
+    oracle's argmax of the GPU's own logits, and the logits pass the GEMV tolerance."""
+    sp = synth.workload_specs(5)[-1]
+    g = synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+    Wd = dev(g.w.reshape(-1).view(np.uint8)); Sd = dev(g.s.reshape(-1)); Xd = dev(g.x)
+    Yd = torch.empty((B, sp.M), dtype=torch.float32, device=DEV)
+    ws = qg.argmax_workspace(B)
+    idx = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    qg.run(sp.fmt, Wd, Sd, Xd, Yd, sp.M, sp.K, B)
+    qg.argmax(Yd, sp.M, B, ws, idx)
+    torch.cuda.synchronize()
+    logits = Yd.cpu().numpy()
+    assert (idx.cpu().numpy() == oracle.argmax_ref(logits)).all()
+    assert_parity(sp.fmt, g.w, g.s, g.x, sp.M, sp.K, B, logits, rows=sample_rows(sp.M))
+
+
+# ------------------------------------------------------------ stream read
+def test_stream_read_checksum():
+    n = (64 << 20) + 48
+    rng = np.random.default_rng(0)
+    host = rng.integers(0, 2 ** 32, size=n // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(DEV)
+    for unroll in (1, 4, 16):
+        for grid in (1, 300, 2048):
+            sink = torch.zeros(grid, dtype=torch.int32, device=DEV)
+            qg.stream_read(buf, n, sink, grid=grid, unroll=unroll)
+            torch.cuda.synchronize()
+            x = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+            assert x == np.bitwise_xor.reduce(host)
