@@ -40,6 +40,11 @@ class QgemvError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch brings its own HIP runtime (soname libamdhip64.so.7). Loading it
+    # first makes libqgemv bind to that same runtime; loading libqgemv first
+    # would pull in a second HIP/HSA runtime and the two would fight over
+    # the device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libqgemv.so not built at {LIB_PATH}; run "
                           "`python -m bandwidth_bound_quantized_amd.build`")
