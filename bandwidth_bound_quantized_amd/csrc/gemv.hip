@@ -209,6 +209,70 @@ __device__ __forceinline__ float reduce_wave(float* v, int lane) {
 
 constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
+// Accumulate one unit of R rows against one batch row of x:
+// acc[r] += scale_r * sum_p dot2(pair_rp, x_p) (+ the 4-bit bias start value).
+template <int FMT, int R>
+__device__ __forceinline__ void accumulate_unit(const uint32_t (&pr)[R][Traits<FMT>::kPairs],
+                                                const float (&dsc)[R],
+                                                const uint32_t (&xv)[Traits<FMT>::kPairs],
+                                                float init, float* acc, int stride) {
+  constexpr int P = Traits<FMT>::kPairs;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if constexpr (FMT == QGEMV_BF16) {
+      float a = acc[r * stride];
+#pragma unroll
+      for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+      acc[r * stride] = a;
+    } else {
+      float a = init;
+#pragma unroll
+      for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+      acc[r * stride] = __builtin_fmaf(dsc[r], a, acc[r * stride]);
+    }
+  }
+}
+
+// Scale factor applied to a unit's dot chain: the binary16 scale for int8,
+// twice the scale for 4-bit codes (their bf16 values carry code/2), 1 for bf16.
+template <int FMT>
+__device__ __forceinline__ float unit_scale(uint32_t sbits) {
+  if constexpr (FMT == QGEMV_INT8_G32) return half_to_float(static_cast<uint16_t>(sbits));
+  else if constexpr (Traits<FMT>::kBias) return 2.f * half_to_float(static_cast<uint16_t>(sbits));
+  else return 1.f;
+}
+
+// Sum of the x values that pair with one unit, times -12: the start value of
+// a 4-bit unit's dot chain (removes the +8 folded into the bf16 codes).
+template <int FMT>
+__device__ __forceinline__ float bias_start(const uint32_t (&xv)[Traits<FMT>::kPairs]) {
+  constexpr uint32_t kOnes = 0x3f803f80u;              // bf16 pair (1.0, 1.0)
+  float s = 0.f;
+#pragma unroll
+  for (int p = 0; p < Traits<FMT>::kPairs; ++p) s = dot2(xv[p], kOnes, s);
+  return -12.f * s;
+}
+
+// Reduce acc[R][NB] over the wave and store row group `grp`'s outputs.
+template <int R, int NB>
+__device__ __forceinline__ void reduce_store(float (&acc)[R][NB], int lane, int grp, int M,
+                                             int batch, float* __restrict__ Y) {
+  constexpr int V = R * NB;
+  float v[V];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
+  const float res = reduce_wave<V>(v, lane);
+  constexpr int SH = 6 - ilog2(V);
+  if ((lane & ((1 << SH) - 1)) == 0) {
+    const int idx = lane >> SH;
+    const int r = idx / NB, b = idx % NB;
+    const int row = grp * R + r;
+    if (row < M && b < batch) Y[static_cast<size_t>(b) * M + row] = res;
+  }
+}
+
 template <int FMT, int NB, int R>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
@@ -367,6 +431,91 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
 }
 
+// Small-batch variant: x never goes through LDS. Lane l always works on the
+// same NCH units (l, l+64, ...) of every row, so it loads the x values those
+// units pair with once, straight into registers (with the 4-bit bias start
+// values), and then only streams weights: no LDS, no barrier, and the first
+// weight loads are in flight while x arrives.
+template <int FMT, int NB, int R, int NCH>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch) {
+  using T = Traits<FMT>;
+  constexpr int P = T::kPairs;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int U = K / T::kElems;
+  const size_t row_bytes = static_cast<size_t>(U) * 16;
+  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
+  const int groups = (M + R - 1) / R;
+  const int waves_total = gridDim.x * kWaves;
+
+  // x for this lane's units (issued first: the bias sums need it early)
+  uint32_t xr[NB][NCH][P];
+  float sx[NB][NCH];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint32_t* xb = reinterpret_cast<const uint32_t*>(X) + static_cast<size_t>(min(b, batch - 1)) * (K >> 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) read_x<FMT>(xb, min(c * 64 + lane, U - 1), xr[b][c]);
+  }
+
+  u32x4 wv[R][NCH];
+  uint32_t sv[R][NCH];
+  auto load_step = [&](int grp) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(grp * R + r, M - 1);
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(row) * row_bytes);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int t = min(c * 64 + lane, U - 1);
+        wv[r][c] = __builtin_nontemporal_load(wrow + t);
+        if constexpr (T::kUnitsPerScale > 0)
+          sv[r][c] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
+      }
+    }
+  };
+
+  int grp = blockIdx.x * kWaves + wave;
+  load_step(min(grp, groups - 1));
+
+  if constexpr (T::kBias) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) sx[b][c] = bias_start<FMT>(xr[b][c]);
+  }
+
+  float acc[R][NB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  while (grp < groups) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c * 64 + lane < U) {
+        uint32_t pr[R][P];
+        float dsc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          unpack<FMT>(wv[r][c], pr[r]);
+          dsc[r] = unit_scale<FMT>(sv[r][c]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          accumulate_unit<FMT, R>(pr, dsc, xr[b][c], T::kBias ? sx[b][c] : 0.f, &acc[0][b], NB);
+      }
+    }
+    const int cur = grp;
+    grp += waves_total;
+    if (grp < groups) load_step(grp);
+    reduce_store<R, NB>(acc, lane, cur, M, batch, Y);
+  }
+}
+
 int round_batch(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
 
 template <int FMT, int NB>
@@ -396,6 +545,38 @@ void allow_big_lds() {
                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
+template <int FMT, int NB, int R, int NCH>
+hipError_t launch_xreg3(const GemvArgs& a, int grid, hipStream_t st) {
+  gemv_xreg_kernel<FMT, NB, R, NCH><<<grid, kThreads, 0, st>>>(
+      static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, a.batch);
+  return hipGetLastError();
+}
+
+template <int FMT, int NB, int NCH>
+hipError_t launch_xreg2(const GemvArgs& a, int R, int grid, hipStream_t st) {
+  switch (R) {
+    case 1: return launch_xreg3<FMT, NB, 1, NCH>(a, grid, st);
+    case 2: return launch_xreg3<FMT, NB, 2, NCH>(a, grid, st);
+    default: return launch_xreg3<FMT, NB, 4, NCH>(a, grid, st);
+  }
+}
+
+template <int FMT, int NB>
+hipError_t launch_xreg1(const GemvArgs& a, int R, int nch, int grid, hipStream_t st) {
+  switch (nch) {
+    case 1: return launch_xreg2<FMT, NB, 1>(a, R, grid, st);
+    case 2: return launch_xreg2<FMT, NB, 2>(a, R, grid, st);
+    case 3: return launch_xreg2<FMT, NB, 3>(a, R, grid, st);
+    default: return launch_xreg2<FMT, NB, 4>(a, R, grid, st);
+  }
+}
+
+template <int FMT>
+hipError_t launch_xreg(const GemvArgs& a, int R, int nch, int grid, hipStream_t st) {
+  if (round_batch(a.batch) == 1) return launch_xreg1<FMT, 1>(a, R, nch, grid, st);
+  return launch_xreg1<FMT, 2>(a, R, nch, grid, st);
+}
+
 }  // namespace
 
 FmtInfo fmt_info(int fmt) {
@@ -414,9 +595,31 @@ size_t gemv_lds_bytes(int fmt, int K, int batch) {
   return bytes;
 }
 
+bool gemv_uses_lds(int fmt, int K, int batch) {
+  const int U = K / fmt_info(fmt).elems_per_unit;
+  const int nch = (U + 63) / 64;
+  return !(round_batch(batch) <= 2 && nch <= 4);
+}
+
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
-  const FmtInfo fi = fmt_info(a.fmt);
   const int cus = device_cu_count();
+  const int U = a.K / fmt_info(a.fmt).elems_per_unit;
+  const int nch = (U + 63) / 64;
+  if (!gemv_uses_lds(a.fmt, a.K, a.batch)) {
+    // rows per step: up to 8 / NCH units in flight per lane, while keeping
+    // at least two workgroups per CU
+    int R = nch == 1 ? 4 : nch == 2 ? 4 : 2;
+    while (R > 1 && (a.M + R - 1) / R < 2 * cus * kWaves) R >>= 1;
+    const int groups = (a.M + R - 1) / R;
+    const int wg_needed = (groups + kWaves - 1) / kWaves;
+    const int grid = std::max(1, std::min(wg_needed, cus * 8));
+    switch (a.fmt) {
+      case QGEMV_BF16: return launch_xreg<QGEMV_BF16>(a, R, nch, grid, stream);
+      case QGEMV_INT8_G32: return launch_xreg<QGEMV_INT8_G32>(a, R, nch, grid, stream);
+      case QGEMV_Q4_0_G32: return launch_xreg<QGEMV_Q4_0_G32>(a, R, nch, grid, stream);
+      default: return launch_xreg<QGEMV_INT4_G128>(a, R, nch, grid, stream);
+    }
+  }
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
@@ -438,7 +641,6 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     }();
     (void)once;
   }
-  (void)fi;
   switch (a.fmt) {
     case QGEMV_BF16: return launch_f<QGEMV_BF16>(a, R, grid, lds, stream);
     case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream);

@@ -235,7 +235,9 @@ int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x,
   int st = check_shape(fmt, M, K);
   if (st) return st;
   if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
-  if (qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) > 160 * 1024) return QGEMV_ESHAPE;
+  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch) &&
+      qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) > 160 * 1024)
+    return QGEMV_ESHAPE;
   if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return QGEMV_EALIGN;
   if (fmt != QGEMV_BF16 && !aligned(scales, 4)) return QGEMV_EALIGN;
   qgemv::GemvArgs a{fmt, W, scales, x, y, static_cast<int>(M), static_cast<int>(K), batch};

@@ -37,6 +37,10 @@ struct GemvArgs {
 // (x as bf16 for the compiled batch, plus per-unit x sums for 4-bit formats).
 size_t gemv_lds_bytes(int fmt, int K, int batch);
 
+// Whether the GEMV of this shape stages x in LDS (batch > 2 or long rows);
+// otherwise each lane keeps its share of x in registers and no LDS is used.
+bool gemv_uses_lds(int fmt, int K, int batch);
+
 // Launch the GEMV on `stream`. Shapes have been validated by the caller.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 

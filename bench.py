@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--peak-gib", type=float, default=4.0)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--per-kernel", action="store_true", help="also time every GEMV of the step alone")
+    p.add_argument("--size-sweep", action="store_true",
+                   help="only time the streaming-read kernel at GEMV-like sizes (size-matched ceilings)")
     return p.parse_args()
 
 
@@ -181,6 +183,42 @@ def measure_peak(qg, torch, gib):
     return best[0], best[1], sweep
 
 
+def size_sweep(qg, torch, rotate_bytes):
+    """Streaming-read kernel at small sizes, rotated through >= rotate_bytes of distinct
+    buffers: the size-matched ceiling a kernel of that many bytes can reach."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for mb in (1, 2, 2.36, 4, 8, 13, 16, 32, 37, 64, 128, 256):
+        nbytes = int(mb * (1 << 20)) // 4096 * 4096
+        n = max(4, math.ceil(rotate_bytes / nbytes))
+        pool = torch.empty(n * nbytes // 4, dtype=torch.int32, device="cuda")
+        pool.fill_(3)
+        sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
+        best = None
+        for grid in (cus, 2 * cus, 4 * cus, 8 * cus):
+            for unroll in (1, 2, 4):
+                base = pool.data_ptr()
+
+                def fn(i, h, grid=grid, unroll=unroll):
+                    st = qg.lib().qgemv_stream_read(base + (i % n) * nbytes, nbytes, sink.data_ptr(),
+                                                    grid, unroll, h)
+                    if st != qg.OK:
+                        raise qg.QgemvError(st, "qgemv_stream_read")
+                g = capture(torch, fn, n)
+                time_graph(torch, g)
+                us = time_graph(torch, g, reps=3) * 1e3 / n
+                if best is None or us < best[0]:
+                    best = (us, grid, unroll)
+                del g
+        us, grid, unroll = best
+        out.append({"MiB": mb, "bytes": nbytes, "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+                    "grid": grid, "unroll": unroll, "rotation": n})
+        print(json.dumps(out[-1]), flush=True)
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, seconds):
     """The oracle (fp64 dequantize + fp64 GEMV + argmax) on whole steps, one thread."""
     import oracle
@@ -211,9 +249,12 @@ def main():
     import torch
     import bandwidth_bound_quantized_amd as qg
 
+    torch.cuda.set_device(0)
+    if args.size_sweep:
+        size_sweep(qg, torch, args.rotate_gib * (1 << 30))
+        return
     cfg = args.workload
     B = args.batch if args.batch is not None else synth.WORKLOAD_BATCHES[cfg][0]
-    torch.cuda.set_device(0)
     wl = Workload(qg, torch, cfg, B, args.rotate_gib * (1 << 30))
     print(f"[bench] workload {cfg} B={B}: {len(wl.gemvs)} GEMVs, {wl.step_bytes} B/step, "
           f"{wl.n_sets} rotation sets", file=sys.stderr, flush=True)
