@@ -43,6 +43,21 @@
 #include "qgemv_internal.h"
 #include "qgemv.h"
 
+// Launch-shape defaults (build-time; the values were chosen by measurement
+// on MI355X, see the tuning notes of this repository's design document).
+#ifndef QGEMV_XREG_MAX_R
+#define QGEMV_XREG_MAX_R 4        // rows per wave step, register-x kernel
+#endif
+#ifndef QGEMV_MIN_WAVES_PER_CU
+#define QGEMV_MIN_WAVES_PER_CU 8  // shrink R until this many waves per CU have work
+#endif
+#ifndef QGEMV_MAX_WG_PER_CU
+#define QGEMV_MAX_WG_PER_CU 8     // cap on resident workgroups per CU (persistent grid)
+#endif
+#ifndef QGEMV_NT_LOADS
+#define QGEMV_NT_LOADS 1          // stream weights with non-temporal loads
+#endif
+
 namespace qgemv {
 namespace {
 
@@ -55,6 +70,16 @@ constexpr int kWaves = kThreads / 64;
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// One 16-byte weight load; weights are read exactly once, so by default they
+// are fetched with the non-temporal hint and do not displace x in the caches.
+__device__ __forceinline__ u32x4 load_weights(const u32x4* p) {
+#if QGEMV_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
 }
 
 __device__ __forceinline__ float half_to_float(uint16_t h) {
@@ -312,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
       for (int u = 0; u < UC; ++u) {
         const int t = min(ch * 64 * UC + u * 64 + lane, U - 1);
-        wv[r][u] = __builtin_nontemporal_load(wrow + t);
+        wv[r][u] = load_weights(wrow + t);
         if constexpr (T::kUnitsPerScale > 0)
           sv[r][u] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
       }
@@ -470,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int t = min(c * 64 + lane, U - 1);
-        wv[r][c] = __builtin_nontemporal_load(wrow + t);
+        wv[r][c] = load_weights(wrow + t);
         if constexpr (T::kUnitsPerScale > 0)
           sv[r][c] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
       }
@@ -608,11 +633,11 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   if (!gemv_uses_lds(a.fmt, a.K, a.batch)) {
     // rows per step: up to 8 / NCH units in flight per lane, while keeping
     // at least two workgroups per CU
-    int R = nch == 1 ? 4 : nch == 2 ? 4 : 2;
-    while (R > 1 && (a.M + R - 1) / R < 2 * cus * kWaves) R >>= 1;
+    int R = std::min(QGEMV_XREG_MAX_R, nch == 1 ? 4 : nch == 2 ? 4 : 2);
+    while (R > 1 && (a.M + R - 1) / R < QGEMV_MIN_WAVES_PER_CU * cus) R >>= 1;
     const int groups = (a.M + R - 1) / R;
     const int wg_needed = (groups + kWaves - 1) / kWaves;
-    const int grid = std::max(1, std::min(wg_needed, cus * 8));
+    const int grid = std::max(1, std::min(wg_needed, cus * QGEMV_MAX_WG_PER_CU));
     switch (a.fmt) {
       case QGEMV_BF16: return launch_xreg<QGEMV_BF16>(a, R, nch, grid, stream);
       case QGEMV_INT8_G32: return launch_xreg<QGEMV_INT8_G32>(a, R, nch, grid, stream);
@@ -623,10 +648,10 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
-  while (R > 1 && (a.M + R - 1) / R < 2 * cus * kWaves) R >>= 1;
+  while (R > 1 && (a.M + R - 1) / R < QGEMV_MIN_WAVES_PER_CU * cus) R >>= 1;
   const int groups = (a.M + R - 1) / R;
   const int wg_needed = (groups + kWaves - 1) / kWaves;
-  int wg_per_cu = static_cast<int>(std::min<size_t>(8, (160 * 1024) / std::max<size_t>(lds, 1)));
+  int wg_per_cu = static_cast<int>(std::min<size_t>(QGEMV_MAX_WG_PER_CU, (160 * 1024) / std::max<size_t>(lds, 1)));
   if (wg_per_cu < 1) wg_per_cu = 1;
   const int grid = std::max(1, std::min(wg_needed, cus * wg_per_cu));
   if (lds > 64 * 1024) {
