@@ -7,7 +7,7 @@ turns negative status codes into QgemvError. PyTorch only provides device
 memory and streams. There is no fallback: if the library is missing the
 import fails.
 
-Build the library first: ``python -m bandwidth_bound_quantized_amd.build``
+Build the library first: ``python bandwidth_bound_quantized_amd/build.py``
 (or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
 SRC_CANONICAL, SRC_BF16 = 0, 1
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
 MAX_BATCH = 8
-ARGMAX_WS_WORDS_PER_ROW = 129
+ARGMAX_WS_WORDS_PER_ROW = 2
 GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
 FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128"}
 
@@ -47,13 +47,14 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libqgemv.so not built at {LIB_PATH}; run "
-                          "`python -m bandwidth_bound_quantized_amd.build`")
+                          "`python bandwidth_bound_quantized_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     c_i64, c_int, c_vp, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     sig = {
         "qgemv_packed_size": (c_int, [c_int, c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qgemv_pack": (c_int, [c_int, c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
         "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
+        "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
         "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
         "qgemv_status_str": (ctypes.c_char_p, [c_int]),
@@ -68,7 +69,8 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_argmax", "qgemv_stream_read",
+EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_run_grouped", "qgemv_argmax",
+           "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
 
@@ -153,6 +155,48 @@ def run_ptr(fmt: int, wp: int, sp: Optional[int], xp: int, yp: int, M: int, K: i
     st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, stream_handle)
     if st != OK:
         raise QgemvError(st, "qgemv_run")
+
+
+class GemvDesc(ctypes.Structure):
+    """Mirror of qgemv_gemv_desc."""
+    _fields_ = [("W", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("fmt", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def grouped_descs(entries) -> "ctypes.Array":
+    """entries: iterable of (fmt, W, scales, x, y, M, K) with device tensors (scales may be None)."""
+    import torch
+    items = list(entries)
+    arr = (GemvDesc * len(items))()
+    for i, (fmt, W, S, x, y, M, K) in enumerate(items):
+        arr[i] = GemvDesc(_dev_ptr(W, "W"), _dev_ptr(S, "scales") if S is not None else None,
+                          _dev_ptr(x, "x", (torch.int16, torch.uint16, torch.bfloat16)),
+                          _dev_ptr(y, "y", torch.float32), fmt, M, K, 0)
+    return arr
+
+
+ELEMS_PER_UNIT = {BF16: 8, INT8_G32: 16, Q4_0_G32: 32, INT4_G128: 32}
+
+
+def group_class(fmt: int, K: int, batch: int) -> int:
+    """The launch class qgemv_run_grouped puts a GEMV in (0: launched alone), per the
+    rule in qgemv.h: batch <= 2 and at most 4 16-byte units per lane-column of a row."""
+    nch = -(-K // (64 * ELEMS_PER_UNIT[fmt]))
+    return nch if (batch <= 2 and nch <= 4) else 0
+
+
+def run_grouped(descs, batch: int, stream=None) -> None:
+    """Independent GEMVs in as few launches as possible (see qgemv_run_grouped)."""
+    st = _lib.qgemv_run_grouped(ctypes.cast(descs, ctypes.c_void_p), len(descs), batch,
+                                _stream_handle(stream))
+    _check(st, "qgemv_run_grouped")
+
+
+def run_grouped_ptr(descs, batch: int, stream_handle) -> None:
+    st = _lib.qgemv_run_grouped(ctypes.cast(descs, ctypes.c_void_p), len(descs), batch, stream_handle)
+    if st != OK:
+        raise QgemvError(st, "qgemv_run_grouped")
 
 
 def argmax(logits, V: int, batch: int, ws, idx, stream=None) -> None:

@@ -1,6 +1,8 @@
 """Build libqgemv.so (HIP kernels for gfx950 + the C-ABI front end) in-tree.
 
-Usage: python -m bandwidth_bound_quantized_amd.build   (or build() from Python)
+Usage: python bandwidth_bound_quantized_amd/build.py   (or __graft_entry__.build())
+(run it as a script: importing it as a submodule imports the package, which
+loads the library it is about to rebuild)
 
 Every source is compiled by hipcc for gfx950 only. Packed-FP32 instruction
 selection is disabled for device code (-packed-fp32-ops); the host pass

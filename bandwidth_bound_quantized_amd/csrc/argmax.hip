@@ -2,14 +2,14 @@
 //
 // The decode step ends by picking the largest logit ("infer", decode
 // pipeline figure; its per-kernel table has the argmax over a 128256-word
-// vocabulary as a separate bandwidth-bound kernel). One launch: each
-// workgroup reduces one slice (about 1024 logits, one load per thread) of
-// one batch row to a 64-bit key whose high word orders the value and whose
-// low word is ~index (so the larger key is the larger value and, on equal
-// values, the lower index), and folds it into the row's running maximum in
-// the caller's workspace with a 64-bit atomic max. The last workgroup of a
-// row to finish (found with an agent-scope counter next to the maximum)
-// writes the index and returns both words to zero.
+// vocabulary as a separate bandwidth-bound kernel). One launch of
+// 256-thread workgroups: each reduces a slice (1-16 Ki logits) of one batch
+// row to a 64-bit key whose high word orders the value and whose low word is
+// ~index (so the larger key is the larger value and, on equal values, the
+// lower index). A row that fits one slice is one workgroup, which writes the
+// index itself; otherwise the slices of a row meet through a 64-bit atomic
+// max and a counter in the caller's workspace (the last slice writes the
+// index and zeroes both words).
 //
 // Order of values: NaN above everything (every NaN equal, so the first NaN
 // wins), then the IEEE order with -0.0 == +0.0.
@@ -19,7 +19,15 @@
 namespace qgemv {
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef QGEMV_ARGMAX_THREADS
+#define QGEMV_ARGMAX_THREADS 256
+#endif
+#ifndef QGEMV_ARGMAX_TARGET_WGS
+#define QGEMV_ARGMAX_TARGET_WGS 32    // workgroups per launch (all rows together)
+#endif
+constexpr int kThreads = QGEMV_ARGMAX_THREADS;
+constexpr int64_t kMinSlice = 1024;   // logits per workgroup, bounds of the adaptive slice
+constexpr int64_t kMaxSlice = 16384;
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
   uint32_t u = __float_as_uint(v);
@@ -47,6 +55,12 @@ __device__ __forceinline__ uint64_t block_max(uint64_t k, uint64_t* red) {
   return k;
 }
 
+// grid = (slices, batch). slices == 1: the workgroup writes idx directly. Otherwise
+// each slice folds its key into ws[row][0] with a 64-bit atomic max and counts itself
+// in ws[row][1]; the last slice of the row writes idx and zeroes both words.
+// Device-scope atomics on one address serialize (tens of ns each on MI355X), so the
+// number of slices per row is kept small.
+template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restrict__ logits,
                                                           int64_t V, int slices,
                                                           uint64_t* __restrict__ ws,
@@ -59,38 +73,65 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
   const int64_t end = beg + per < V ? beg + per : V;
   const float* row = logits + static_cast<int64_t>(b) * V;
 
-  // all of this thread's loads are issued before any is used (addresses
-  // clamped into the slice; elements past its end do not count)
   uint64_t key = 0;
-  constexpr int kU = 4;
-  for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += kU * kThreads) {
-    float v[kU];
+  if constexpr (VEC4) {
+    // rows start 16-byte aligned and per is a multiple of 4: float4 loads,
+    // all of a thread's loads issued before any is used
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kU = 8;
+    const int64_t n4 = (end - beg) / 4;
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(row + beg);
+    for (int64_t j0 = threadIdx.x; j0 < n4; j0 += kU * kThreads) {
+      f32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t i = i0 + u * kThreads;
-      v[u] = __builtin_nontemporal_load(row + (i < end ? i : end - 1));
+      for (int u = 0; u < kU; ++u) {
+        const int64_t j = j0 + u * kThreads;
+        v[u] = __builtin_nontemporal_load(r4 + (j < n4 ? j : n4 - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t j = j0 + u * kThreads;
+        if (j < n4) {
+          const uint32_t i = static_cast<uint32_t>(beg + 4 * j);
+          key = umax64(key, make_key(v[u].x, i));
+          key = umax64(key, make_key(v[u].y, i + 1));
+          key = umax64(key, make_key(v[u].z, i + 2));
+          key = umax64(key, make_key(v[u].w, i + 3));
+        }
+      }
     }
+  } else {
+    constexpr int kU = 8;
+    for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += kU * kThreads) {
+      float v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t i = i0 + u * kThreads;
-      if (i < end) key = umax64(key, make_key(v[u], static_cast<uint32_t>(i)));
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kThreads;
+        v[u] = __builtin_nontemporal_load(row + (i < end ? i : end - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kThreads;
+        if (i < end) key = umax64(key, make_key(v[u], static_cast<uint32_t>(i)));
+      }
     }
   }
   key = block_max(key, red);
-
-  // ws row: word 0 = running max key, word 1 = count of finished workgroups
+  if (threadIdx.x != 0) return;
+  if (slices == 1) {
+    idx[b] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFu));
+    return;
+  }
   uint64_t* slot = ws + static_cast<int64_t>(b) * QGEMV_ARGMAX_WS_WORDS_PER_ROW;
   uint32_t* counter = reinterpret_cast<uint32_t*>(slot + 1);
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_max(slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == static_cast<uint32_t>(slices - 1)) {
-      // every other workgroup's max happened before its counter increment
-      const uint64_t k = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      idx[b] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFu));
-      __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  __hip_atomic_fetch_max(slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev == static_cast<uint32_t>(slices - 1)) {
+    // every other slice's max happened before its counter increment
+    const uint64_t k = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    idx[b] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFu));
+    __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -98,11 +139,23 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
 
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                          hipStream_t stream) {
-  int64_t slices = (V + 1023) / 1024;                // one load per thread per slice
-  if (slices < 1) slices = 1;
+  // Slices of 1-16 Ki logits, aiming at ~32 workgroups per launch: fewer
+  // leave the load latency of each workgroup exposed, more make the
+  // same-address atomics that join the slices of a row queue up (measured on
+  // MI355X: V=32000 B=1 best with 32 slices, V=128256 B=8 with 8 per row).
+  int64_t slice = (V * batch + QGEMV_ARGMAX_TARGET_WGS - 1) / QGEMV_ARGMAX_TARGET_WGS;
+  slice = (slice + kMinSlice - 1) / kMinSlice * kMinSlice;
+  if (slice < kMinSlice) slice = kMinSlice;
+  if (slice > kMaxSlice) slice = kMaxSlice;
+  int64_t slices = (V + slice - 1) / slice;
   if (slices > kArgmaxSlices) slices = kArgmaxSlices;
+  const int64_t per = (V + slices - 1) / slices;
+  const bool vec4 = (V % 4 == 0) && (per % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
   dim3 grid(static_cast<unsigned>(slices), static_cast<unsigned>(batch));
-  argmax_kernel<<<grid, kThreads, 0, stream>>>(logits, V, static_cast<int>(slices), ws, idx);
+  if (vec4)
+    argmax_kernel<true><<<grid, kThreads, 0, stream>>>(logits, V, static_cast<int>(slices), ws, idx);
+  else
+    argmax_kernel<false><<<grid, kThreads, 0, stream>>>(logits, V, static_cast<int>(slices), ws, idx);
   return hipGetLastError();
 }
 

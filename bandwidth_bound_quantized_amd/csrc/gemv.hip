@@ -24,13 +24,13 @@
 //     packed bf16 pairs and multiplied with packed bf16 activations by
 //     v_dot2_f32_bf16 (two exact products and a float32 add per instruction).
 //     Each group's scale multiplies the group's partial sum once.
-//   * 4-bit codes: with c the nibble moved to bits 6..3 of a byte and 0x41
-//     as the high byte, the bf16 value is 8 + c/2 exactly. The 8 is removed
-//     with the per-unit sum of x, folded into the dot chain's start value:
-//     sum((8 + q/2) x) - 12 sum(x) = (1/2) sum((q - 8) x); the 1/2 is folded
-//     into the scale (exact). This is the Rust page's bias-removal identity
-//     (Lesson 6) with a smaller magic offset so less of the float32
-//     rounding is magnified by the cancellation.
+//   * 4-bit codes: each nibble is masked into its own byte and converted to
+//     bf16 exactly by the fp8 -> bf16 conversion instruction (a byte q in
+//     0..15 is the e4m3 number q * 2^-9; the conversion's scale 2^9 undoes
+//     that), two codes per instruction. The stored offset 8 is removed with
+//     the per-unit sum of x folded into the dot chain's start value:
+//     sum(q x) - 8 sum(x) = sum((q - 8) x) (the Rust page's bias-removal
+//     identity, Lesson 6).
 //   * int8 codes: sign-extended to float32 (exact) and packed to bf16 pairs
 //     by taking the high halves (exact: at most 8 significant bits).
 //   * The per-row reduction over the 64 lanes reduces all R*batch partial
@@ -182,18 +182,19 @@ __device__ __forceinline__ void unpack(const u32x4& w, uint32_t (&p)[Traits<FMT>
                                            __builtin_bit_cast(uint32_t, f2), 0x07060302u);
     }
   } else {
-    // byte j of the unit: low nibble -> element j of the low run,
-    // high nibble -> element j of the high run. bf16 0x41cc with cc = nibble<<3
-    // is 8 + nibble/2.
-    constexpr uint32_t kMagic = 0x41414141u;
+    // byte j of the unit: low nibble -> element j of the low run, high nibble
+    // -> element j of the high run. A byte holding a value 0..15 read as an
+    // fp8 e4m3 number is value * 2^-9 (subnormals for 0..7, exponent 1 for
+    // 8..15), so the fp8 -> bf16 conversion with scale 2^9 gives the code
+    // exactly, two bytes per instruction.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = (wd[i] << 3) & 0x78787878u;
-      const uint32_t hi = (wd[i] >> 1) & 0x78787878u;
-      p[2 * i] = __builtin_amdgcn_perm(kMagic, lo, 0x04010400u);
-      p[2 * i + 1] = __builtin_amdgcn_perm(kMagic, lo, 0x04030402u);
-      p[8 + 2 * i] = __builtin_amdgcn_perm(kMagic, hi, 0x04010400u);
-      p[8 + 2 * i + 1] = __builtin_amdgcn_perm(kMagic, hi, 0x04030402u);
+      const uint32_t lo = wd[i] & 0x0F0F0F0Fu;
+      const uint32_t hi = (wd[i] >> 4) & 0x0F0F0F0Fu;
+      p[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
+      p[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
+      p[8 + 2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
+      p[8 + 2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
     }
   }
 }
@@ -258,24 +259,23 @@ __device__ __forceinline__ void accumulate_unit(const uint32_t (&pr)[R][Traits<F
   }
 }
 
-// Scale factor applied to a unit's dot chain: the binary16 scale for int8,
-// twice the scale for 4-bit codes (their bf16 values carry code/2), 1 for bf16.
+// Scale factor applied to a unit's dot chain: the binary16 scale of the
+// unit's group (1 for bf16).
 template <int FMT>
 __device__ __forceinline__ float unit_scale(uint32_t sbits) {
-  if constexpr (FMT == QGEMV_INT8_G32) return half_to_float(static_cast<uint16_t>(sbits));
-  else if constexpr (Traits<FMT>::kBias) return 2.f * half_to_float(static_cast<uint16_t>(sbits));
-  else return 1.f;
+  if constexpr (FMT == QGEMV_BF16) return 1.f;
+  else return half_to_float(static_cast<uint16_t>(sbits));
 }
 
-// Sum of the x values that pair with one unit, times -12: the start value of
-// a 4-bit unit's dot chain (removes the +8 folded into the bf16 codes).
+// Sum of the x values that pair with one unit, times -8: the start value of a
+// 4-bit unit's dot chain, which turns sum(q x) into sum((q - 8) x).
 template <int FMT>
 __device__ __forceinline__ float bias_start(const uint32_t (&xv)[Traits<FMT>::kPairs]) {
   constexpr uint32_t kOnes = 0x3f803f80u;              // bf16 pair (1.0, 1.0)
   float s = 0.f;
 #pragma unroll
   for (int p = 0; p < Traits<FMT>::kPairs; ++p) s = dot2(xv[p], kOnes, s);
-  return -12.f * s;
+  return -8.f * s;
 }
 
 // Reduce acc[R][NB] over the wave and store row group `grp`'s outputs.
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   __syncthreads();
 
   if constexpr (T::kBias) {
-    // per-unit sums of x, pre-multiplied by -12 (the dot chain's start value)
+    // per-unit sums of x, pre-multiplied by -8 (the dot chain's start value)
     constexpr uint32_t kOnes = 0x3f803f80u;          // bf16 pair (1.0, 1.0)
     for (int i = tid; i < NB * U; i += kThreads) {
       const int b = i / U, t = i - b * U;
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       float s = 0.f;
 #pragma unroll
       for (int p = 0; p < P; ++p) s = dot2(xv[p], kOnes, s);
-      sxs[i] = -12.f * s;
+      sxs[i] = -8.f * s;
     }
     __syncthreads();
   }
@@ -406,9 +406,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           unpack<FMT>(wv[r][u], pr[r]);
-          if constexpr (FMT == QGEMV_INT8_G32) dsc[r] = half_to_float(static_cast<uint16_t>(sv[r][u]));
-          else if constexpr (T::kBias) dsc[r] = 2.f * half_to_float(static_cast<uint16_t>(sv[r][u]));
-          else dsc[r] = 1.f;
+          dsc[r] = unit_scale<FMT>(sv[r][u]);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -456,61 +454,223 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wave reduction without LDS round trips (for R * NB <= 8 partial sums).
+// v_permlane32_swap / v_permlane16_swap exchange whole 16-lane rows between
+// two registers: swap(X, Y) followed by one add leaves X's sum in the rows
+// whose lane bit 5 (or 4) is 0 and Y's sum in the others, which halves the
+// number of live values per lane in two instructions. The rest of a 16-lane
+// row is reduced with DPP lane permutations folded into the adds.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowShr4 = 0x114;    // row_shr:4 (bound_ctrl: lanes 0-3 read 0)
+constexpr int kDppRowShr8 = 0x118;    // row_shr:8
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+// (the two results are copied out of the returned vector before the bit
+// casts: a bit cast applied to a vector element directly read element 0 twice)
+__device__ __forceinline__ float halve32(float x, float y) {   // x to bit5=0 lanes, y to bit5=1
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __uint_as_float(r0) + __uint_as_float(r1);
+}
+__device__ __forceinline__ float halve16(float x, float y) {   // x to bit4=0 lanes, y to bit4=1
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __uint_as_float(r0) + __uint_as_float(r1);
+}
+__device__ __forceinline__ float row_allreduce(float x) {      // every lane: sum over its 16-lane row
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  x += dpp_f<kDppMirror>(x);
+  return x;
+}
+
+// Reduce v[0..V) over the 64 lanes. Returns this lane's result; *idx is the
+// value index it holds and *owner whether this lane stores it (one lane per
+// index).
+template <int V>
+__device__ __forceinline__ float reduce_wave_rows(float* v, int lane, int* idx, bool* owner) {
+  static_assert(V == 1 || V == 2 || V == 4 || V == 8, "V");
+  const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1, b0 = lane & 1;
+  // (the swaps write both operands, so a swap of a register with itself is
+  // not a butterfly; the final cross-row steps pair the value with zero and
+  // leave the complete sum in the rows whose bit is 0)
+  if constexpr (V == 1) {
+    float x = row_allreduce(v[0]);
+    x = halve32(x, 0.f);
+    x = halve16(x, 0.f);
+    *idx = 0;
+    *owner = lane == 0;
+    return x;
+  } else if constexpr (V == 2) {
+    float x = halve32(v[0], v[1]);
+    x = row_allreduce(x);
+    x = halve16(x, 0.f);
+    *idx = b5;
+    *owner = (lane & 31) == 0;
+    return x;
+  } else if constexpr (V == 4) {
+    const float a = halve32(v[0], v[2]);
+    const float b = halve32(v[1], v[3]);
+    float x = halve16(a, b);
+    x = row_allreduce(x);
+    *idx = 2 * b5 + b4;
+    *owner = (lane & 15) == 0;
+    return x;
+  } else {
+    const float a0 = halve32(v[0], v[4]), a1 = halve32(v[1], v[5]);
+    const float a2 = halve32(v[2], v[6]), a3 = halve32(v[3], v[7]);
+    const float c0 = halve16(a0, a2), c1 = halve16(a1, a3);
+    // bit 0: lanes with bit0 = 0 keep c0, the others c1
+    const float keep = b0 ? c1 : c0;
+    const float send = b0 ? c0 : c1;
+    float x = keep + dpp_f<kDppXor1>(send);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppRowShr4>(x);
+    x += dpp_f<kDppRowShr8>(x);          // lanes 12..15 of each row hold the row sums
+    *idx = 4 * b5 + 2 * b4 + b0;
+    *owner = (lane & 14) == 12;          // lanes 12 and 13 of each row
+    return x;
+  }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer: out-of-range
+// loads return 0). Built from wave-uniform values, so it lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+#if QGEMV_NT_LOADS
+constexpr int kWeightAux = 2;         // non-temporal
+#else
+constexpr int kWeightAux = 0;
+#endif
+
+// One GEMV of a table walked by the register-x kernel. `start` is the index of
+// the GEMV's first row group in the concatenation of all the table's groups.
+struct TableEntry {
+  const uint8_t* W;
+  const uint16_t* S;
+  const uint16_t* X;
+  float* Y;
+  int M;
+  int K;
+  int start;
+  int pad;
+};
+
+// Up to N independent GEMVs of one format and batch, passed by value (they
+// live in the kernel-argument segment and are read with scalar loads).
+template <int N>
+struct GemvTable {
+  int n;        // entries
+  int total;    // row groups over all entries
+  int pad0, pad1;
+  TableEntry e[N];
+};
+
 // Small-batch variant: x never goes through LDS. Lane l always works on the
-// same NCH units (l, l+64, ...) of every row, so it loads the x values those
-// units pair with once, straight into registers (with the 4-bit bias start
-// values), and then only streams weights: no LDS, no barrier, and the first
-// weight loads are in flight while x arrives.
-template <int FMT, int NB, int R, int NCH>
-__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(
-    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
-    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch) {
+// same NCH units (l, l+64, ...) of every row of a GEMV, so it loads the x
+// values those units pair with once, straight into registers (with the 4-bit
+// bias start values), and then only streams weights: no LDS, no barrier, and
+// the first weight loads are in flight while x arrives.
+//
+// The kernel walks a table of GEMVs (one entry for qgemv_run, up to N for a
+// grouped launch of independent GEMVs): the row groups of all entries are
+// numbered consecutively and waves take them in a grid-stride loop, so one
+// launch streams every entry's weights and pays the launch and ramp-up cost
+// once. A wave reloads its x registers when its next row group belongs to
+// another entry.
+template <int FMT, int NB, int R, int NCH, int N>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<N> tab, int batch) {
   using T = Traits<FMT>;
   constexpr int P = T::kPairs;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int U = K / T::kElems;
-  const size_t row_bytes = static_cast<size_t>(U) * 16;
-  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
-  const int groups = (M + R - 1) / R;
-  const int waves_total = gridDim.x * kWaves;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int stride = gridDim.x * kWaves;
+  int item = blockIdx.x * kWaves + wave;
+  if (item >= tab.total) return;                 // no barriers in this kernel
 
-  // x for this lane's units (issued first: the bias sums need it early)
+  int j = 0;
+  if constexpr (N > 1) {
+    while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
+  }
+  const uint8_t* W;
+  const uint16_t* S;
+  float* Y;
+  int M, U, nsc, start, next_start, row_bytes;
   uint32_t xr[NB][NCH][P];
   float sx[NB][NCH];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const uint32_t* xb = reinterpret_cast<const uint32_t*>(X) + static_cast<size_t>(min(b, batch - 1)) * (K >> 1);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) read_x<FMT>(xb, min(c * 64 + lane, U - 1), xr[b][c]);
-  }
+  // per lane: byte offset of its unit in a row and of its unit's scale in a scale row
+  int woff[NCH], soff[NCH];
 
-  u32x4 wv[R][NCH];
-  uint32_t sv[R][NCH];
-  auto load_step = [&](int grp) {
+  // make entry j current: its geometry and this lane's x registers
+  auto enter = [&](int jj) {
+    const TableEntry& e = tab.e[jj];
+    W = e.W; S = e.S; Y = e.Y; M = e.M; start = e.start;
+    next_start = (N > 1 && jj + 1 < tab.n) ? tab.e[jj + 1].start : tab.total;
+    U = e.K / T::kElems;
+    row_bytes = U * 16;
+    nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(grp * R + r, M - 1);
-      const u32x4* wrow = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(row) * row_bytes);
+    for (int c = 0; c < NCH; ++c) {
+      const int t = min(c * 64 + lane, U - 1);
+      woff[c] = t * 16;
+      soff[c] = T::kUnitsPerScale ? (t / T::kUnitsPerScale) * 2 : 0;
+    }
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int t = min(c * 64 + lane, U - 1);
-        wv[r][c] = load_weights(wrow + t);
-        if constexpr (T::kUnitsPerScale > 0)
-          sv[r][c] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
-      }
+    for (int b = 0; b < NB; ++b) {
+      const uint32_t* xb = reinterpret_cast<const uint32_t*>(e.X) +
+                           static_cast<size_t>(min(b, batch - 1)) * (e.K >> 1);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) read_x<FMT>(xb, min(c * 64 + lane, U - 1), xr[b][c]);
     }
   };
 
-  int grp = blockIdx.x * kWaves + wave;
-  load_step(min(grp, groups - 1));
+  u32x4 wv[R][NCH];
+  uint32_t sv[R][NCH];
+  // loads of one row group through buffer resources whose base is the group's
+  // first row (scalar address math); rows past M read as zero and are not stored
+  auto load_step = [&](int grp) {
+    const int row0 = grp * R;
+    const int rows = min(R, M - row0);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(W + static_cast<size_t>(row0) * row_bytes, static_cast<uint32_t>(rows * row_bytes));
+    // the row offset goes into the VGPR offset: the hardware range check
+    // covers the VGPR and instruction offsets, not the SGPR offset
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        wv[r][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[c] + r * row_bytes, 0, kWeightAux));
+    if constexpr (T::kUnitsPerScale > 0) {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(S + static_cast<size_t>(row0) * nsc, static_cast<uint32_t>(rows * nsc * 2));
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          sv[r][c] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[c] + r * nsc * 2, 0, 0);
+    }
+  };
+  auto bias_sums = [&]() {
+    if constexpr (T::kBias) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) sx[b][c] = bias_start<FMT>(xr[b][c]);
+    }
+  };
 
-  if constexpr (T::kBias) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) sx[b][c] = bias_start<FMT>(xr[b][c]);
-  }
+  enter(j);
+  load_step(item - start);
+  bias_sums();
 
   float acc[R][NB];
 #pragma unroll
@@ -518,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
 
-  while (grp < groups) {
+  while (true) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c * 64 + lane < U) {
@@ -534,10 +694,39 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(
           accumulate_unit<FMT, R>(pr, dsc, xr[b][c], T::kBias ? sx[b][c] : 0.f, &acc[0][b], NB);
       }
     }
-    const int cur = grp;
-    grp += waves_total;
-    if (grp < groups) load_step(grp);
-    reduce_store<R, NB>(acc, lane, cur, M, batch, Y);
+    // issue the next row group's loads before reducing this one
+    const int grp = item - start;
+    const int cur_M = M;
+    float* cur_Y = Y;
+    item += stride;
+    const bool more = item < tab.total;
+    bool switched = false;
+    if (more) {
+      if constexpr (N > 1) {
+        if (item >= next_start) {
+          while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
+          enter(j);
+          switched = true;
+        }
+      }
+      load_step(item - start);
+    }
+    {
+      constexpr int V = R * NB;
+      float v[V];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
+      int idx;
+      bool owner;
+      const float res = reduce_wave_rows<V>(v, lane, &idx, &owner);
+      const int r = idx / NB, b = idx % NB;
+      const int row = grp * R + r;
+      if (owner && row < cur_M && b < batch) cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
+    }
+    if (!more) break;
+    if (switched) bias_sums();
   }
 }
 
@@ -572,8 +761,11 @@ void allow_big_lds() {
 
 template <int FMT, int NB, int R, int NCH>
 hipError_t launch_xreg3(const GemvArgs& a, int grid, hipStream_t st) {
-  gemv_xreg_kernel<FMT, NB, R, NCH><<<grid, kThreads, 0, st>>>(
-      static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, a.batch);
+  GemvTable<1> tab{};
+  tab.n = 1;
+  tab.total = (a.M + R - 1) / R;
+  tab.e[0] = TableEntry{static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, 0, 0};
+  gemv_xreg_kernel<FMT, NB, R, NCH, 1><<<grid, kThreads, 0, st>>>(tab, a.batch);
   return hipGetLastError();
 }
 
@@ -600,6 +792,45 @@ template <int FMT>
 hipError_t launch_xreg(const GemvArgs& a, int R, int nch, int grid, hipStream_t st) {
   if (round_batch(a.batch) == 1) return launch_xreg1<FMT, 1>(a, R, nch, grid, st);
   return launch_xreg1<FMT, 2>(a, R, nch, grid, st);
+}
+
+constexpr int kGroupMax = 64;       // GEMVs per grouped launch (kernel-argument table)
+
+template <int FMT, int NB, int R, int NCH>
+hipError_t launch_group4(const GemvArgs* a, int n, int total, int grid, hipStream_t st) {
+  GemvTable<kGroupMax> tab{};
+  tab.n = n;
+  tab.total = total;
+  int start = 0;
+  for (int i = 0; i < n; ++i) {
+    tab.e[i] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
+                          a[i].M, a[i].K, start, 0};
+    start += (a[i].M + R - 1) / R;
+  }
+  gemv_xreg_kernel<FMT, NB, R, NCH, kGroupMax><<<grid, kThreads, 0, st>>>(tab, a[0].batch);
+  return hipGetLastError();
+}
+
+template <int FMT, int NB, int NCH>
+hipError_t launch_group3(const GemvArgs* a, int n, int R, int total, int grid, hipStream_t st) {
+  if (R == 4) return launch_group4<FMT, NB, 4, NCH>(a, n, total, grid, st);
+  return launch_group4<FMT, NB, 2, NCH>(a, n, total, grid, st);
+}
+
+template <int FMT, int NB>
+hipError_t launch_group2(const GemvArgs* a, int n, int nch, int R, int total, int grid, hipStream_t st) {
+  switch (nch) {
+    case 1: return launch_group3<FMT, NB, 1>(a, n, R, total, grid, st);
+    case 2: return launch_group3<FMT, NB, 2>(a, n, R, total, grid, st);
+    case 3: return launch_group3<FMT, NB, 3>(a, n, R, total, grid, st);
+    default: return launch_group3<FMT, NB, 4>(a, n, R, total, grid, st);
+  }
+}
+
+template <int FMT>
+hipError_t launch_group1(const GemvArgs* a, int n, int nch, int R, int total, int grid, hipStream_t st) {
+  if (round_batch(a[0].batch) == 1) return launch_group2<FMT, 1>(a, n, nch, R, total, grid, st);
+  return launch_group2<FMT, 2>(a, n, nch, R, total, grid, st);
 }
 
 }  // namespace
@@ -671,6 +902,33 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream);
     case QGEMV_Q4_0_G32: return launch_f<QGEMV_Q4_0_G32>(a, R, grid, lds, stream);
     default: return launch_f<QGEMV_INT4_G128>(a, R, grid, lds, stream);
+  }
+}
+
+int gemv_group_class(int fmt, int K, int batch) {
+  if (gemv_uses_lds(fmt, K, batch)) return 0;
+  const int U = K / fmt_info(fmt).elems_per_unit;
+  return (U + 63) / 64;
+}
+
+int gemv_group_max() { return kGroupMax; }
+
+hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream) {
+  const int cus = device_cu_count();
+  const int nch = gemv_group_class(a[0].fmt, a[0].K, a[0].batch);
+  long rows = 0;
+  for (int i = 0; i < n; ++i) rows += a[i].M;
+  // rows per wave step: 4 for short rows while that still gives every CU's
+  // waves work; 2 otherwise (longer rows keep more x and weights in registers)
+  const int R = (nch <= 2 && rows / 4 >= static_cast<long>(QGEMV_MIN_WAVES_PER_CU) * cus) ? 4 : 2;
+  int total = 0;
+  for (int i = 0; i < n; ++i) total += (a[i].M + R - 1) / R;
+  const int grid = std::max(1, std::min((total + kWaves - 1) / kWaves, cus * QGEMV_MAX_WG_PER_CU));
+  switch (a[0].fmt) {
+    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, n, nch, R, total, grid, stream);
+    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, n, nch, R, total, grid, stream);
+    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, n, nch, R, total, grid, stream);
+    default: return launch_group1<QGEMV_INT4_G128>(a, n, nch, R, total, grid, stream);
   }
 }
 

@@ -5,7 +5,9 @@
 // HIP, and reports problems as negative status values (never exceptions).
 #include <cmath>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "qgemv.h"
 #include "qgemv_internal.h"
@@ -171,6 +173,22 @@ int pack_from_bf16(int fmt, const uint16_t* src, int64_t M, int64_t K, void* dst
   return QGEMV_OK;
 }
 
+int check_run_args(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, const float* y,
+                   int64_t M, int64_t K, int batch) {
+  if (!valid_fmt(fmt)) return QGEMV_EINVAL;
+  if (!W || !x || !y) return QGEMV_EINVAL;
+  if (fmt != QGEMV_BF16 && !scales) return QGEMV_EINVAL;
+  int st = check_shape(fmt, M, K);
+  if (st) return st;
+  if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
+  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch) &&
+      qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) > 160 * 1024)
+    return QGEMV_ESHAPE;
+  if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return QGEMV_EALIGN;
+  if (fmt != QGEMV_BF16 && !aligned(scales, 4)) return QGEMV_EALIGN;
+  return QGEMV_OK;
+}
+
 int record_hip(hipError_t e) {
   if (e == hipSuccess) return QGEMV_OK;
   g_last_hip_error = static_cast<int>(e);
@@ -229,19 +247,50 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
 
 int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
               int64_t M, int64_t K, int batch, void* stream) {
-  if (!valid_fmt(fmt)) return QGEMV_EINVAL;
-  if (!W || !x || !y) return QGEMV_EINVAL;
-  if (fmt != QGEMV_BF16 && !scales) return QGEMV_EINVAL;
-  int st = check_shape(fmt, M, K);
+  const int st = check_run_args(fmt, W, scales, x, y, M, K, batch);
   if (st) return st;
-  if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
-  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch) &&
-      qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) > 160 * 1024)
-    return QGEMV_ESHAPE;
-  if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 16)) return QGEMV_EALIGN;
-  if (fmt != QGEMV_BF16 && !aligned(scales, 4)) return QGEMV_EALIGN;
   qgemv::GemvArgs a{fmt, W, scales, x, y, static_cast<int>(M), static_cast<int>(K), batch};
   return record_hip(qgemv::launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+
+int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stream) {
+  if (!gemvs || n < 1) return QGEMV_EINVAL;
+  if (n > QGEMV_GROUP_MAX) return QGEMV_ESHAPE;
+  for (int i = 0; i < n; ++i) {
+    const qgemv_gemv_desc& g = gemvs[i];
+    const int st = check_run_args(g.fmt, g.W, g.scales, g.x, g.y, g.M, g.K, batch);
+    if (st) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // GEMVs the register-x kernel takes are launched together, one launch per
+  // (format, units per lane-column) class in order of first appearance; the
+  // others are launched one by one.
+  std::vector<qgemv::GemvArgs> todo;
+  std::vector<char> done(static_cast<size_t>(n), 0);
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const qgemv_gemv_desc& g = gemvs[i];
+    const int cls = qgemv::gemv_group_class(g.fmt, g.K, batch);
+    todo.clear();
+    for (int k = i; k < n; ++k) {
+      const qgemv_gemv_desc& h = gemvs[k];
+      if (done[k]) continue;
+      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) != cls))
+        continue;
+      todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
+      done[k] = 1;
+    }
+    const int maxn = cls == 0 ? 1 : qgemv::gemv_group_max();
+    for (size_t off = 0; off < todo.size(); off += maxn) {
+      const int cnt = static_cast<int>(std::min(todo.size() - off, static_cast<size_t>(maxn)));
+      const hipError_t e = cls == 0 ? qgemv::launch_gemv(todo[off], s)
+                                    : qgemv::launch_gemv_group(&todo[off], cnt, s);
+      const int st = record_hip(e);
+      if (st) return st;
+    }
+  }
+  return QGEMV_OK;
 }
 
 int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,

@@ -44,7 +44,16 @@ bool gemv_uses_lds(int fmt, int K, int batch);
 // Launch the GEMV on `stream`. Shapes have been validated by the caller.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
-// Launch the argmax (one kernel). ws: batch * 129 u64 words, zero on entry.
+// Grouped launches of independent GEMVs (register-x kernel only).
+// gemv_group_class: 0 if (fmt, K, batch) needs the LDS kernel, else the number
+// of 16-byte units per lane-column of a row (1..4); GEMVs of one format, batch
+// and class can share a launch. launch_gemv_group: n <= gemv_group_max()
+// GEMVs of one format, batch and class, already validated.
+int gemv_group_class(int fmt, int K, int batch);
+int gemv_group_max();
+hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream);
+
+// Launch the argmax (one kernel). ws: batch * 2 u64 words, zero on entry.
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                          hipStream_t stream);
 

@@ -130,8 +130,42 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
 int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
               int64_t M, int64_t K, int batch, void* stream);
 
+/* One GEMV of a grouped call (same meaning and layout rules as qgemv_run). */
+typedef struct {
+  const void* W;          /* device: codes (or bf16 weights) */
+  const uint16_t* scales; /* device: binary16 scales (NULL for bf16) */
+  const uint16_t* x;      /* device: bf16 [batch][K] */
+  float* y;               /* device: float32 [batch][M], overwritten */
+  int32_t fmt;
+  int32_t M;
+  int32_t K;
+  int32_t reserved;       /* set to 0 */
+} qgemv_gemv_desc;
+
+/* Largest n qgemv_run_grouped accepts in one call. */
+#define QGEMV_GROUP_MAX 1024
+
+/*
+ * qgemv_run_grouped - n independent GEMVs, all at the same batch:
+ * gemvs[i].y = W_i x_i for every i. Host array of descriptors (read during
+ * the call only); device pointers inside. No entry may read what another
+ * writes (no y of one entry may overlap any W, scales, x or y of another):
+ * the order in which entries are computed is unspecified. This is the shape
+ * of a decode step's independent projections (the GEMV sets and the
+ * 89-GEMV weight stream of a TinyLlama step measured here; the experts of a
+ * mixture-of-experts layer are another).
+ * Entries of one format that the small-batch kernel handles (batch <= 2 and
+ * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit)
+ * share launches (one per format and row-length class, up to 64 entries
+ * each), so the per-launch start-up cost is paid once per class instead of
+ * once per GEMV; other entries are launched one by one. All validation
+ * happens before anything is launched. Errors as qgemv_run; ESHAPE also
+ * for n > QGEMV_GROUP_MAX.
+ */
+int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stream);
+
 /* u64 words of workspace qgemv_argmax needs per batch row */
-#define QGEMV_ARGMAX_WS_WORDS_PER_ROW 129
+#define QGEMV_ARGMAX_WS_WORDS_PER_ROW 2
 
 /*
  * qgemv_argmax - greedy token: idx[b] = the first index of the largest
@@ -145,6 +179,8 @@ int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x,
  * every call leaves it all zero again, so one zero-fill at allocation time
  * suffices. Calls that may run concurrently need distinct ws buffers.
  * 1 <= batch <= 8, 1 <= V <= 2^31 - 1. One kernel launch; asynchronous.
+ * A row of up to 32768 logits is reduced by one workgroup without touching
+ * ws; longer rows are split into slices that meet in ws with atomics.
  */
 int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                  void* stream);

@@ -208,3 +208,29 @@ def test_pack_validation():
     w = ctypes.c_size_t(); s = ctypes.c_size_t()
     assert L.qgemv_packed_size(qg.BF16, 0, 32, ctypes.byref(w), ctypes.byref(s)) == qg.ESHAPE
     assert L.qgemv_packed_size(qg.BF16, 1, 32, None, ctypes.byref(s)) == qg.EINVAL
+
+
+def test_grouped_validation_errors_before_any_launch():
+    L = qg.lib()
+    good = dict(fmt=qg.Q4_0_G32, M=64, K=2048)
+
+    def descs(*entries):
+        arr = (qg.GemvDesc * len(entries))()
+        for i, e in enumerate(entries):
+            d = dict(W=FAKE, scales=FAKE, x=FAKE, y=FAKE, fmt=good["fmt"], M=good["M"], K=good["K"], reserved=0)
+            d.update(e)
+            arr[i] = qg.GemvDesc(**d)
+        return arr
+
+    assert L.qgemv_run_grouped(None, 1, 1, None) == qg.EINVAL
+    a = descs({})
+    assert L.qgemv_run_grouped(ctypes.cast(a, ctypes.c_void_p), 0, 1, None) == qg.EINVAL
+    assert L.qgemv_run_grouped(ctypes.cast(a, ctypes.c_void_p), 1, 0, None) == qg.ESHAPE
+    assert L.qgemv_run_grouped(ctypes.cast(a, ctypes.c_void_p), 1, 9, None) == qg.ESHAPE
+    big = descs(*([{}] * 2))
+    assert L.qgemv_run_grouped(ctypes.cast(big, ctypes.c_void_p), 1025, 1, None) == qg.ESHAPE
+    # one bad entry anywhere in the list rejects the whole call
+    for bad, want in [({"W": None}, qg.EINVAL), ({"fmt": 9}, qg.EINVAL), ({"K": 48}, qg.ESHAPE),
+                      ({"y": FAKE + 4}, qg.EALIGN), ({"scales": None}, qg.EINVAL), ({"M": 0}, qg.ESHAPE)]:
+        arr = descs({}, {}, bad, {})
+        assert L.qgemv_run_grouped(ctypes.cast(arr, ctypes.c_void_p), 4, 1, None) == want, bad

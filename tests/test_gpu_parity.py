@@ -210,10 +210,11 @@ def _argmax_cases():
     cases["random_128256x8"] = rng.standard_normal((8, 128256)).astype(np.float32)
     cases["random_32000x1"] = rng.standard_normal((1, 32000)).astype(np.float32)
     cases["ties_planted"] = synth.f32_logits_with_ties(rng, 8, 128256)
-    t = rng.standard_normal((4, 128256)).astype(np.float32)
-    # equal maxima straddling a slice boundary (2048-element slices), a wave
-    # boundary, and the first/last elements
-    for b, pos in enumerate([(2047, 2048), (63, 64), (0, 128255), (4095, 6143, 100000)]):
+    t = rng.standard_normal((6, 128256)).astype(np.float32)
+    # equal maxima straddling the slice boundaries of a 128256-logit row
+    # (4 slices of 32064), a wave boundary, and the first/last elements
+    for b, pos in enumerate([(32063, 32064), (63, 64), (0, 128255), (4095, 6143, 100000),
+                             (64127, 64128, 96191), (96192, 128255)]):
         t[b, list(pos)] = 10.0
     cases["ties_boundaries"] = t
     n = rng.standard_normal((3, 5000)).astype(np.float32)
@@ -229,6 +230,9 @@ def _argmax_cases():
     cases["tiny_V"] = rng.standard_normal((8, 1)).astype(np.float32)
     cases["V7"] = np.array([[1, 5, 5, 2, 0, 5, 1]] * 2, np.float32)
     cases["large_V"] = rng.standard_normal((1, 300001)).astype(np.float32)
+    lv = rng.standard_normal((3, 70001)).astype(np.float32)   # odd V: scalar loads, 3 slices
+    lv[0, [23334, 23333]] = 9.0; lv[1, [46667, 70000]] = 9.0; lv[2, 70000] = 9.0
+    cases["odd_V_multislice_ties"] = lv
     return cases
 
 
@@ -285,3 +289,65 @@ def test_stream_read_checksum():
             torch.cuda.synchronize()
             x = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
             assert x == np.bitwise_xor.reduce(host)
+
+
+# ------------------------------------------------------------ grouped GEMVs
+def _grouped(gemvs, B):
+    """Upload, run all gemvs in one qgemv_run_grouped call, return host outputs."""
+    dev_items = []
+    for g in gemvs:
+        W = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+        S = dev(g.s.reshape(-1)) if g.s is not None else None
+        X = dev(np.ascontiguousarray(g.x).reshape(B, g.K))
+        Y = torch.full((B, g.M), float("nan"), dtype=torch.float32, device=DEV)
+        dev_items.append((g.fmt, W, S, X, Y, g.M, g.K))
+    descs = qg.grouped_descs(dev_items)
+    print(f"[gpu] qgemv_run_grouped n={len(gemvs)} B={B}", flush=True)
+    qg.run_grouped(descs, B)
+    torch.cuda.synchronize()
+    return [it[4].cpu().numpy() for it in dev_items]
+
+
+@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (3, 1), (5, 1), (5, 2), (1, 2)])
+def test_grouped_workload_parity(cfg, B):
+    gemvs = [synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+             for sp in synth.workload_specs(cfg)]
+    ys = _grouped(gemvs, B)
+    for g, y in zip(gemvs, ys):
+        assert np.isfinite(y).all(), g.name
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"grouped {g.name}")
+
+
+def test_grouped_decode_step_stream_89_gemvs():
+    """All 89 GEMVs of the TinyLlama decode-step stream in one call (B=1): 64 sampled rows each."""
+    B = 1
+    gemvs = synth.make_workload(4, B)
+    ys = _grouped(gemvs, B)
+    rng = np.random.default_rng(5)
+    for g, y in zip(gemvs, ys):
+        rows = np.unique(np.concatenate([[0, g.M - 1], rng.choice(g.M, 62, replace=False)]))
+        assert np.isfinite(y).all(), g.name
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=rows, what=f"grouped {g.name}")
+
+
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_grouped_mixed_formats_ragged_and_fallback(B):
+    """Formats and row lengths mixed in one call, ragged M, entries the grouped kernel
+    does not take (int8 K=8192, and every entry at B=3) launched one by one."""
+    shapes = [(synth.Q4_0_G32, 1, 2048), (synth.BF16, 65, 256), (synth.INT8_G32, 1000, 2048),
+              (synth.Q4_0_G32, 63, 5632), (synth.INT4_G128, 300, 8192), (synth.INT8_G32, 70, 8192),
+              (synth.Q4_0_G32, 4097, 2048), (synth.BF16, 7, 2048), (synth.INT4_G128, 129, 384),
+              (synth.Q4_0_G32, 2, 96)]
+    gemvs = [synth.make_gemv(f"g{i}", f, M, K, B, 6, i, "o") for i, (f, M, K) in enumerate(shapes)]
+    ys = _grouped(gemvs, B)
+    for g, y in zip(gemvs, ys):
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"mixed {g.name}")
+
+
+def test_grouped_more_than_one_launch_per_class():
+    """130 small Q4_0 GEMVs: more than the 64 entries one launch's table holds."""
+    B = 1
+    gemvs = [synth.make_gemv(f"s{i}", synth.Q4_0_G32, 33 + i, 2048, B, 6, 100 + i, "qkv") for i in range(130)]
+    ys = _grouped(gemvs, B)
+    for g, y in zip(gemvs, ys):
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, what=g.name)
