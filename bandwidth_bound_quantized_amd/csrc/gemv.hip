@@ -57,6 +57,18 @@
 #ifndef QGEMV_NT_LOADS
 #define QGEMV_NT_LOADS 1          // stream weights with non-temporal loads
 #endif
+#ifndef QGEMV_MFMA_TARGET_WAVES_PER_CU
+#define QGEMV_MFMA_TARGET_WAVES_PER_CU 16  // matrix-core kernel: waves per CU worth aiming for
+#endif
+#ifndef QGEMV_MFMA_MAX_WAVES_PER_CU
+#define QGEMV_MFMA_MAX_WAVES_PER_CU 16     // ... and the most that fit (register budget)
+#endif
+#ifndef QGEMV_MFMA_FORCE_KS
+#define QGEMV_MFMA_FORCE_KS 0              // nonzero: fixed K split (if it divides the steps)
+#endif
+#ifndef QGEMV_MFMA_FORCE_TW
+#define QGEMV_MFMA_FORCE_TW 0              // nonzero: fixed tiles per workgroup
+#endif
 
 namespace qgemv {
 namespace {
@@ -730,6 +742,393 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<N> 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batch 3..8: matrix cores.
+//
+// From batch 3 on, the dot-product kernels above spend one dot2 instruction
+// per weight pair and batch row and become bound by the vector ALUs instead
+// of HBM. This kernel hands the products to the matrix cores:
+// v_mfma_f32_16x16x32_bf16 with A = x (16 rows: the batch rows, the rest
+// padding) and B = 32 dequantized weights of 16 weight rows, so that
+// D[b][i] is the dot product of batch row b and weight row i over one
+// 32-position "chunk" of K. The vector ALUs only unpack codes (exactly, as
+// above) and apply each group's scale to its chunk's D tile.
+//
+// Lane (i, q) = (lane % 16, lane / 16) loads 16 bytes of weight row i at
+// byte 16q of every 64-byte slice of the row, so each load instruction of a
+// wave reads 64 contiguous bytes of 16 rows. For the quantized formats the
+// four lanes of a row then exchange dwords with permlane swaps, after which
+// each lane holds, for each chunk of the slice, the 8 codes of k positions
+// 8q..8q+7 of that chunk. Which K elements those positions are depends on
+// how the format packs codes (chunk_elem below); x is staged in LDS in that
+// same order, so A and B always agree.
+//
+// In the D tile, lane (i, q) holds batch rows 4q..4q+3 of weight row i, so a
+// group's scale is one value per lane. The 4-bit formats' offset of 8 is
+// removed with the same identity as above, summed per group:
+// sum_g d_g sum(q x) - 8 sum_g d_g sum_g(x); the second term is itself a
+// small product of the scales with the per-group x sums and runs on the
+// float32 matrix instruction (v_mfma_f32_16x16x4_f32), four groups at a time.
+//
+// Work split: a workgroup has TW x KS waves; each of TW tiles of 16 rows is
+// shared by KS waves that take equal contiguous ranges of the row's steps
+// (a step is kSlices 64-byte slices). The KS partial tiles are added in LDS
+// in a fixed order. Workgroups loop over tiles; every wave issues the loads
+// of its next step before computing the current one.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT> struct MfmaFmt;
+template <> struct MfmaFmt<QGEMV_BF16> {
+  static constexpr int kSlices = 4;          // 64-byte row slices per step
+  static constexpr int kChunksPerSlice = 1;  // 32-position MFMA chunks per slice
+  static constexpr int kGroups = 0;          // scale groups per step
+  static constexpr int kChunksPerGroup = 0;
+  static constexpr int kStepElems = 128;     // K elements per step
+};
+template <> struct MfmaFmt<QGEMV_INT8_G32> {
+  static constexpr int kSlices = 2;
+  static constexpr int kChunksPerSlice = 2;
+  static constexpr int kGroups = 4;
+  static constexpr int kChunksPerGroup = 1;
+  static constexpr int kStepElems = 128;
+};
+template <> struct MfmaFmt<QGEMV_Q4_0_G32> {
+  static constexpr int kSlices = 2;
+  static constexpr int kChunksPerSlice = 4;
+  static constexpr int kGroups = 8;
+  static constexpr int kChunksPerGroup = 1;
+  static constexpr int kStepElems = 256;
+};
+template <> struct MfmaFmt<QGEMV_INT4_G128> {
+  static constexpr int kSlices = 4;
+  static constexpr int kChunksPerSlice = 4;
+  static constexpr int kGroups = 4;
+  static constexpr int kChunksPerGroup = 4;
+  static constexpr int kStepElems = 512;
+};
+
+// K element at position pos (0..31) of chunk c; position pos = 8q + 4h + j
+// is the j-th code of half h of lane row q after the exchange.
+//   bf16  : slice = chunk, lane row q loaded elements 8q..8q+7.
+//   int8  : slice = 2 chunks (groups); after one 32-lane swap, lane row q of
+//           chunk 0 holds elements 0-7, 16-23, 8-15, 24-31 for q = 0..3.
+//   Q4_0  : slice = 4 blocks; after the 4x4 dword transpose, lane row q holds
+//           byte dword q of each block: low nibbles 4q..4q+3, high nibbles
+//           16+4q..16+4q+3.
+//   int4-g128: slice = 1 group of 128; lane row q of chunk c holds byte
+//           dword q of the group's quarter c: elements 16c+4q.. (low) and
+//           64+16c+4q.. (high).
+template <int FMT>
+__device__ __forceinline__ int chunk_elem(int c, int pos) {
+  const int q = pos >> 3, h = (pos >> 2) & 1, j = pos & 3;
+  if constexpr (FMT == QGEMV_BF16) return 32 * c + pos;
+  else if constexpr (FMT == QGEMV_INT8_G32) return 32 * c + 16 * (q & 1) + 8 * (q >> 1) + 4 * h + j;
+  else if constexpr (FMT == QGEMV_Q4_0_G32) return 32 * c + 16 * h + 4 * q + j;
+  else return 128 * (c >> 2) + 64 * h + 16 * (c & 3) + 4 * q + j;
+}
+
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  x = r0; y = r1;
+}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  x = r0; y = r1;
+}
+
+// Four codes (one dword) of a 4-bit chunk -> 8 bf16 B-operand values.
+__device__ __forceinline__ bf16x8_t nibbles_to_b(uint32_t d) {
+  const uint32_t lo = d & 0x0F0F0F0Fu;
+  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
+  const u32x4 v = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true))};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Four int8 codes -> two bf16 pairs (in byte order).
+__device__ __forceinline__ void int8x4_to_bf16(uint32_t d, uint32_t& p0, uint32_t& p1) {
+  const float f0 = static_cast<float>(static_cast<int32_t>(d << 24) >> 24);
+  const float f1 = static_cast<float>(static_cast<int32_t>(d << 16) >> 24);
+  const float f2 = static_cast<float>(static_cast<int32_t>(d << 8) >> 24);
+  const float f3 = static_cast<float>(static_cast<int32_t>(d) >> 24);
+  p0 = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  p1 = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8_t int8_to_b(uint32_t d0, uint32_t d1) {
+  uint32_t p0, p1, p2, p3;
+  int8x4_to_bf16(d0, p0, p1);
+  int8x4_to_bf16(d1, p2, p3);
+  const u32x4 v = {p0, p1, p2, p3};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float scale_of(const uint32_t* s, int g) {
+  const uint32_t w = s[g >> 1];
+  return half_to_float(static_cast<uint16_t>((g & 1) ? (w >> 16) : w));
+}
+
+constexpr int kMfmaMaxThreads = 1024;
+
+template <int FMT, int NB>
+__global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch, int KS, int iters) {
+  using F = MfmaFmt<FMT>;
+  constexpr int kCPS = F::kChunksPerSlice;
+  constexpr int kChunks = F::kSlices * kCPS;          // chunks per step
+  constexpr int kSW = F::kGroups > 0 ? F::kGroups / 2 : 1;   // scale dwords per step
+  constexpr int kOutLanes = 4 * NB;                    // lanes holding real batch rows
+  extern __shared__ u32x4 lds_v4[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds_v4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int TW = static_cast<int>(blockDim.x >> 6) / KS;
+  const int tg = wave / KS;                            // tile slot of this wave
+  const int ks = wave - tg * KS;                       // K range of this wave
+  const int i = lane & 15, q = lane >> 4;
+  const int bcl = min(i, NB - 1);                      // A row this lane supplies
+  const int nchunk = K >> 5;
+  const int ngroups = F::kGroups ? K / (F::kStepElems / F::kGroups) : 0;
+  const int nsteps = K / F::kStepElems;
+  const int Lw = nsteps / KS;                          // steps per wave per tile
+  const uint32_t row_bytes = static_cast<uint32_t>(
+      FMT == QGEMV_BF16 ? 2 * K : FMT == QGEMV_INT8_G32 ? K : K / 2);
+  constexpr bool kBiasSums = F::kChunksPerGroup > 0 && FMT != QGEMV_INT8_G32;   // 4-bit formats
+  // LDS: x [nchunk][NB][32] bf16 | group sums [ngroups][NB] (4-bit) | partial tiles
+  float* sneg = reinterpret_cast<float*>(xs + static_cast<size_t>(nchunk) * NB * 32);
+  f32x4* red = reinterpret_cast<f32x4*>(sneg + (kBiasSums ? ngroups * NB : 0));
+
+  const uint32_t woff = i * row_bytes + 16 * q;
+  const uint32_t soff = i * ngroups * 2;
+
+  u32x4 wa[F::kSlices], wb[F::kSlices];
+  uint32_t sa[kSW], sb[kSW];
+
+  // loads of step s (of this wave's range) of the tile of iteration n;
+  // rows past M (and whole tiles past the end) read as zero
+  auto load = [&](u32x4 (&w)[F::kSlices], uint32_t (&s)[kSW], int n, int st_local) {
+    const int tile = (n * gridDim.x + blockIdx.x) * TW + tg;
+    const int row0 = tile * 16;
+    // (written as a select and a min: a clamp would be selected as a vector
+    // med3, and a buffer resource built from a vector register is looped
+    // over lanes)
+    const int rows = row0 < M ? min(16, M - row0) : 0;
+    const int st = ks * Lw + st_local;
+    // The lane's offset (row i, byte 16q) is the VGPR offset, which the
+    // range check covers: rows past M read as zero. The step's offset along
+    // the row is the SGPR offset (not range checked, always inside the row),
+    // so no vector register is computed here.
+    const uint8_t* base = W + (rows ? static_cast<size_t>(row0) * row_bytes : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(base, static_cast<uint32_t>(rows) * row_bytes);
+    const int so = st * (F::kSlices * 64);
+#pragma unroll
+    for (int l = 0; l < F::kSlices; ++l)
+      w[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 64 * l, so, kWeightAux));
+    if constexpr (F::kGroups > 0) {
+      const uint16_t* sbase = S + (rows ? static_cast<size_t>(row0) * ngroups : 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, static_cast<uint32_t>(rows * ngroups * 2));
+      const int sso = st * (F::kGroups * 2);
+      if constexpr (kSW == 4) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff, sso, 0));
+        s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+      } else {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff, sso, 0));
+        s[0] = v.x; s[1] = v.y;
+      }
+    }
+  };
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&w)[F::kSlices], const uint32_t (&s)[kSW], int st_local,
+                     f32x4& acc, f32x4& bacc) {
+    const int st = ks * Lw + st_local;
+    const int c0 = st * kChunks;
+#pragma unroll
+    for (int l = 0; l < F::kSlices; ++l) {
+      uint32_t r[4] = {w[l].x, w[l].y, w[l].z, w[l].w};
+      if constexpr (FMT != QGEMV_BF16) {
+        // The swaps below overwrite both of their registers. Swapping copies
+        // leaves the loaded registers untouched, so they stay where the next
+        // prefetch into this buffer puts them (otherwise the register
+        // allocator rotates them and has to copy in-flight load results,
+        // which waits for the prefetch).
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(r[k]) : "v"(r[k]));
+      }
+      if constexpr (FMT == QGEMV_INT8_G32) {
+        swap32(r[0], r[2]);
+        swap32(r[1], r[3]);
+      } else if constexpr (FMT != QGEMV_BF16) {
+        swap32(r[0], r[2]);
+        swap32(r[1], r[3]);
+        swap16(r[0], r[1]);
+        swap16(r[2], r[3]);
+      }
+      f32x4 dg = zero;
+#pragma unroll
+      for (int ch = 0; ch < kCPS; ++ch) {
+        const int c = c0 + l * kCPS + ch;
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4*>(xs + (static_cast<size_t>(c) * NB + bcl) * 32 + 8 * q));
+        if constexpr (FMT == QGEMV_BF16) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, w[l]), acc, 0, 0, 0);
+        } else if constexpr (FMT == QGEMV_INT8_G32) {
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), zero, 0, 0, 0);
+          const float sc = scale_of(s, l * kCPS + ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, d[j], acc[j]);
+        } else if constexpr (FMT == QGEMV_Q4_0_G32) {
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), zero, 0, 0, 0);
+          const float sc = scale_of(s, l * kCPS + ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, d[j], acc[j]);
+        } else {
+          dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), dg, 0, 0, 0);
+        }
+      }
+      if constexpr (FMT == QGEMV_INT4_G128) {
+        const float sc = scale_of(s, l);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, dg[j], acc[j]);
+      }
+    }
+    if constexpr (kBiasSums) {
+      // bias term: D[b][i] += sum over 4 groups of (-8 sum_g x_b) * d_ig;
+      // A lane (b, q) supplies group q's x sum, B lane (i, q) group q's scale
+#pragma unroll
+      for (int h = 0; h < F::kGroups / 4; ++h) {
+        const float av = sneg[(st * F::kGroups + 4 * h + q) * NB + bcl];
+        const uint32_t sw = (q >> 1) ? s[2 * h + 1] : s[2 * h];
+        const float bv = half_to_float(static_cast<uint16_t>(sw >> (16 * (q & 1))));
+        bacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, bacc, 0, 0, 0);
+      }
+    }
+  };
+
+  // D tile -> y: lane (i, q) holds batch rows 4q..4q+3 of row i of the tile
+  auto store = [&](const f32x4& v, int n) {
+    const int tile = (n * gridDim.x + blockIdx.x) * TW + tg;
+    const int row = tile * 16 + i;
+    if (row < M) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = 4 * q + j;
+        if (b < batch) Y[static_cast<size_t>(b) * M + row] = v[j];
+      }
+    }
+  };
+  int par = 0;
+  auto finish = [&](int n, f32x4& acc, f32x4& bacc) {
+    f32x4 t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = acc[j] + bacc[j];
+    acc = zero;
+    bacc = zero;
+    if (KS == 1) {
+      store(t, n);
+    } else {
+      f32x4* slot = red + static_cast<size_t>((par * TW + tg) * KS) * kOutLanes;
+      if (lane < kOutLanes) slot[ks * kOutLanes + lane] = t;
+      __syncthreads();
+      if (ks == 0 && lane < kOutLanes) {
+        f32x4 sum = slot[lane];
+        for (int k2 = 1; k2 < KS; ++k2) {
+          const f32x4 o = slot[k2 * kOutLanes + lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sum[j] += o[j];
+        }
+        store(sum, n);
+      }
+      par ^= 1;
+    }
+  };
+
+  const int nv = iters * Lw;           // steps of this wave (same for every wave)
+  if (nv > 0) load(wa, sa, 0, 0);
+
+  // ---- stage x (all K, NB rows; rows >= batch as zero) in chunk order,
+  // four 16-byte slots per thread per round so the loads overlap
+  {
+    const int nslots = nchunk * NB * 4;
+    for (int base = tid; base < nslots; base += 4 * static_cast<int>(blockDim.x)) {
+      u32x2 r0[4], r1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = base + u * static_cast<int>(blockDim.x);
+        const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
+        r0[u] = u32x2{0u, 0u};
+        r1[u] = u32x2{0u, 0u};
+        if (sl < nslots && b < batch) {
+          const uint16_t* xr = X + static_cast<size_t>(b) * K;
+          r0[u] = *reinterpret_cast<const u32x2*>(xr + chunk_elem<FMT>(c, 8 * qq));
+          r1[u] = *reinterpret_cast<const u32x2*>(xr + chunk_elem<FMT>(c, 8 * qq + 4));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = base + u * static_cast<int>(blockDim.x);
+        if (sl < nslots) reinterpret_cast<u32x4*>(xs)[sl] = u32x4{r0[u].x, r0[u].y, r1[u].x, r1[u].y};
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (kBiasSums) {
+    // -8 * (sum of x over each group), per batch row
+    constexpr uint32_t kOnes = 0x3f803f80u;
+    for (int e = tid; e < ngroups * NB; e += blockDim.x) {
+      const int g = e / NB, b = e - g * NB;
+      float sum = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < F::kChunksPerGroup; ++cc) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(xs + (static_cast<size_t>(g * F::kChunksPerGroup + cc) * NB + b) * 32);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 v = row[d];
+          sum = dot2(v.x, kOnes, sum);
+          sum = dot2(v.y, kOnes, sum);
+          sum = dot2(v.z, kOnes, sum);
+          sum = dot2(v.w, kOnes, sum);
+        }
+      }
+      sneg[e] = -8.f * sum;
+    }
+    __syncthreads();
+  }
+
+  // The next step's loads are issued unconditionally (past the last tile
+  // they address zero rows, read as zero and move no data): with a
+  // conditional issue the compiler could not count outstanding loads and
+  // would wait for all of them, prefetch included, before computing.
+  f32x4 acc = zero, bacc = zero;
+  int n = 0, s = 0;                    // (iteration, step) held in wa/sa
+  for (int v = 0; v < nv; v += 2) {
+    int n1 = n, s1 = s + 1;
+    if (s1 == Lw) { s1 = 0; ++n1; }
+    load(wb, sb, n1, s1);
+    compute(wa, sa, s, acc, bacc);
+    if (s + 1 == Lw) finish(n, acc, bacc);
+    if (v + 1 >= nv) break;
+    int n2 = n1, s2 = s1 + 1;
+    if (s2 == Lw) { s2 = 0; ++n2; }
+    load(wa, sa, n2, s2);
+    compute(wb, sb, s1, acc, bacc);
+    if (s1 + 1 == Lw) finish(n1, acc, bacc);
+    n = n2;
+    s = s2;
+  }
+}
+
 int round_batch(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
 
 template <int FMT, int NB>
@@ -833,6 +1232,94 @@ hipError_t launch_group1(const GemvArgs* a, int n, int nch, int R, int total, in
   return launch_group2<FMT, 2>(a, n, nch, R, total, grid, st);
 }
 
+// ---- matrix-core kernel: launch plan
+int mfma_step_elems(int fmt) {
+  switch (fmt) {
+    case QGEMV_BF16: return MfmaFmt<QGEMV_BF16>::kStepElems;
+    case QGEMV_INT8_G32: return MfmaFmt<QGEMV_INT8_G32>::kStepElems;
+    case QGEMV_Q4_0_G32: return MfmaFmt<QGEMV_Q4_0_G32>::kStepElems;
+    default: return MfmaFmt<QGEMV_INT4_G128>::kStepElems;
+  }
+}
+
+size_t mfma_lds_bytes(int fmt, int K, int NB, int KS, int TW) {
+  size_t b = static_cast<size_t>(NB) * K * 2;                       // x
+  if (fmt == QGEMV_Q4_0_G32) b += static_cast<size_t>(K / 32) * NB * 4;   // group sums
+  if (fmt == QGEMV_INT4_G128) b += static_cast<size_t>(K / 128) * NB * 4;
+  if (KS > 1) b += static_cast<size_t>(2) * TW * KS * (4 * NB) * 16;  // partial tiles
+  return b;
+}
+
+struct MfmaPlan {
+  int KS = 0, TW = 0, grid = 0, iters = 0;
+  size_t lds = 0;
+};
+
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+// Choose the K split (KS waves per tile, dividing the row's steps) and the
+// tiles per workgroup (TW) that keep the most waves busy on real tiles, up
+// to the target per CU; among equals, the fewest workgroups (each stages x
+// once), then the smallest workgroup.
+bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
+  const int NB = round_batch(batch);
+  if (NB < 4) return false;
+  const int step = mfma_step_elems(fmt);
+  if (K % step != 0) return false;
+  const int nsteps = K / step;
+  const int ntiles = (M + 15) / 16;
+  long best_score = -1;
+  MfmaPlan best;
+  for (int KS = 1; KS <= 16; ++KS) {
+    if (nsteps % KS != 0) continue;
+    if (QGEMV_MFMA_FORCE_KS && KS != QGEMV_MFMA_FORCE_KS) continue;
+    for (int TW = 1; TW * KS <= 16; TW *= 2) {
+      if (QGEMV_MFMA_FORCE_TW && TW != QGEMV_MFMA_FORCE_TW) continue;
+      const size_t lds = mfma_lds_bytes(fmt, K, NB, KS, TW);
+      if (lds > kLdsPerCu) continue;
+      const int wg_cu = std::min(static_cast<int>(kLdsPerCu / lds), QGEMV_MFMA_MAX_WAVES_PER_CU / (KS * TW));
+      if (wg_cu < 1) continue;
+      const int wgs_needed = (ntiles + TW - 1) / TW;
+      const int grid = std::max(1, std::min(wgs_needed, cus * wg_cu));
+      const long busy = static_cast<long>(std::min(ntiles, grid * TW)) * KS;
+      const long score = std::min(busy, static_cast<long>(cus) * QGEMV_MFMA_TARGET_WAVES_PER_CU);
+      const bool better = score > best_score ||
+                          (score == best_score && (grid < best.grid ||
+                                                   (grid == best.grid && KS * TW < best.KS * best.TW)));
+      if (better) {
+        best_score = score;
+        best.KS = KS;
+        best.TW = TW;
+        best.grid = grid;
+        best.iters = (ntiles + grid * TW - 1) / (grid * TW);
+        best.lds = lds;
+      }
+    }
+  }
+  if (best_score < 0) return false;
+  *out = best;
+  return true;
+}
+
+template <int FMT, int NB>
+hipError_t launch_mfma2(const GemvArgs& a, const MfmaPlan& p, hipStream_t st) {
+  if (p.lds > 64 * 1024) {
+    static const hipError_t once = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
+    if (once != hipSuccess) return once;
+  }
+  gemv_mfma_kernel<FMT, NB><<<p.grid, 64 * p.KS * p.TW, p.lds, st>>>(
+      static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, a.batch, p.KS, p.iters);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_mfma(const GemvArgs& a, const MfmaPlan& p, hipStream_t st) {
+  if (round_batch(a.batch) == 4) return launch_mfma2<FMT, 4>(a, p, st);
+  return launch_mfma2<FMT, 8>(a, p, st);
+}
+
 }  // namespace
 
 FmtInfo fmt_info(int fmt) {
@@ -874,6 +1361,15 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
       case QGEMV_INT8_G32: return launch_xreg<QGEMV_INT8_G32>(a, R, nch, grid, stream);
       case QGEMV_Q4_0_G32: return launch_xreg<QGEMV_Q4_0_G32>(a, R, nch, grid, stream);
       default: return launch_xreg<QGEMV_INT4_G128>(a, R, nch, grid, stream);
+    }
+  }
+  MfmaPlan plan;
+  if (plan_mfma(a.fmt, a.M, a.K, a.batch, cus, &plan)) {
+    switch (a.fmt) {
+      case QGEMV_BF16: return launch_mfma<QGEMV_BF16>(a, plan, stream);
+      case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32>(a, plan, stream);
+      case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32>(a, plan, stream);
+      default: return launch_mfma<QGEMV_INT4_G128>(a, plan, stream);
     }
   }
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);

@@ -351,3 +351,38 @@ def test_grouped_more_than_one_launch_per_class():
     ys = _grouped(gemvs, B)
     for g, y in zip(gemvs, ys):
         assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, what=g.name)
+
+
+# ------------------------------------------------ matrix-core path (batch 3..8)
+# Shapes chosen for the launch plans they produce: few tiles with the row's
+# steps split over up to 16 waves whose partial tiles are added in LDS
+# (2048x2048, 17x4096, 2048x8192), many tiles per workgroup and more than one
+# pass of the grid over them (40000x1024), a ragged last tile (4100, 17), and
+# the shortest rows each format takes on this path (16x512).
+MFMA_SHAPES = [(2048, 2048), (17, 4096), (4100, 1024), (16, 512), (40000, 1024), (2048, 8192)]
+
+
+@pytest.mark.parametrize("B", [3, 5, 8])
+@pytest.mark.parametrize("M,K", MFMA_SHAPES, ids=[f"{m}x{k}" for m, k in MFMA_SHAPES])
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128],
+                         ids=["bf16", "int8", "q4_0", "int4"])
+def test_mfma_path_shapes(fmt, M, K, B):
+    g = synth.make_gemv("t", fmt, M, K, B, 9, (M + K) % 991, "gate_up")
+    y = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B)
+    assert np.isfinite(y).all()
+    assert_parity(fmt, g.w, g.s, g.x, M, K, B, y, rows=sample_rows(M), what=f"M={M} K={K} B={B}")
+
+
+@pytest.mark.parametrize("fmt", [qg.Q4_0_G32, qg.INT4_G128], ids=["q4_0", "int4"])
+def test_mfma_path_all_codes_extreme(fmt):
+    """Every 4-bit code 0 or 15 with the largest generated scale and x of one sign:
+    the largest partial sums and the largest offset-term cancellation the
+    synthetic inputs can produce."""
+    M, K, B = 512, 4096, 8
+    g = synth.make_gemv("t", fmt, M, K, B, 9, 3, "down")
+    rng = np.random.default_rng(11)
+    w = np.where(rng.random(g.w.shape) < 0.5, 0x00, 0xFF).astype(np.uint8)
+    s = np.full_like(g.s, 0x1D1F)
+    x = synth.bf16_normal(rng, (B, K), 1.0) & np.uint16(0x7FFF)     # |x|: sign bit cleared
+    y = gpu_gemv(fmt, w, s, x, M, K, B)
+    assert_parity(fmt, w, s, x, M, K, B, y, what="extreme")
