@@ -180,8 +180,9 @@ ELEMS_PER_UNIT = {BF16: 8, INT8_G32: 16, Q4_0_G32: 32, INT4_G128: 32}
 
 
 def group_class(fmt: int, K: int, batch: int) -> int:
-    """The launch class qgemv_run_grouped puts a GEMV in (0: launched alone), per the
-    rule in qgemv.h: batch <= 2 and at most 4 16-byte units per lane-column of a row."""
+    """0 if qgemv_run_grouped launches this GEMV alone, else its 16-byte units per
+    lane-column of a row (1..4); per the rule in qgemv.h (batch <= 2 and at most 4
+    units per lane-column), GEMVs with a nonzero class share one launch per format."""
     nch = -(-K // (64 * ELEMS_PER_UNIT[fmt]))
     return nch if (batch <= 2 and nch <= 4) else 0
 

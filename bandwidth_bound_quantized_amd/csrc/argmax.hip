@@ -25,9 +25,12 @@ namespace {
 #ifndef QGEMV_ARGMAX_TARGET_WGS
 #define QGEMV_ARGMAX_TARGET_WGS 32    // workgroups per launch (all rows together)
 #endif
+#ifndef QGEMV_ARGMAX_MAX_SLICE
+#define QGEMV_ARGMAX_MAX_SLICE 16384
+#endif
 constexpr int kThreads = QGEMV_ARGMAX_THREADS;
 constexpr int64_t kMinSlice = 1024;   // logits per workgroup, bounds of the adaptive slice
-constexpr int64_t kMaxSlice = 16384;
+constexpr int64_t kMaxSlice = QGEMV_ARGMAX_MAX_SLICE;
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
   uint32_t u = __float_as_uint(v);

@@ -54,6 +54,12 @@
 #ifndef QGEMV_MAX_WG_PER_CU
 #define QGEMV_MAX_WG_PER_CU 8     // cap on resident workgroups per CU (persistent grid)
 #endif
+#ifndef QGEMV_GROUP_R2
+#define QGEMV_GROUP_R2 2          // grouped launch: rows per wave step at 2 units per lane-column
+#endif
+#ifndef QGEMV_GROUP_RLONG
+#define QGEMV_GROUP_RLONG 2       // ... and at 3 or 4 units per lane-column
+#endif
 #ifndef QGEMV_NT_LOADS
 #define QGEMV_NT_LOADS 1          // stream weights with non-temporal loads
 #endif
@@ -574,8 +580,11 @@ struct TableEntry {
   int M;
   int K;
   int start;
-  int pad;
+  int shape;    // xreg_shape(R, NCH) of the entry
 };
+
+// (rows per wave step, 16-byte units per lane-column of a row) as one code
+constexpr int xreg_shape(int R, int NCH) { return R * 16 + NCH; }
 
 // Up to N independent GEMVs of one format and batch, passed by value (they
 // live in the kernel-argument segment and are read with scalar loads).
@@ -598,21 +607,14 @@ struct GemvTable {
 // numbered consecutively and waves take them in a grid-stride loop, so one
 // launch streams every entry's weights and pays the launch and ramp-up cost
 // once. A wave reloads its x registers when its next row group belongs to
-// another entry.
+// another entry, and issues that group's loads before reducing the current
+// one unless the entry's (R, NCH) differs.
 template <int FMT, int NB, int R, int NCH, int N>
-__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<N> tab, int batch) {
+__device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
+                                        int batch, int lane) {
   using T = Traits<FMT>;
   constexpr int P = T::kPairs;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int stride = gridDim.x * kWaves;
-  int item = blockIdx.x * kWaves + wave;
-  if (item >= tab.total) return;                 // no barriers in this kernel
-
-  int j = 0;
-  if constexpr (N > 1) {
-    while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
-  }
+  constexpr int kShape = xreg_shape(R, NCH);
   const uint8_t* W;
   const uint16_t* S;
   float* Y;
@@ -711,17 +713,21 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<N> 
     const int cur_M = M;
     float* cur_Y = Y;
     item += stride;
-    const bool more = item < tab.total;
+    bool more = item < tab.total;
     bool switched = false;
     if (more) {
       if constexpr (N > 1) {
         if (item >= next_start) {
           while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
-          enter(j);
-          switched = true;
+          if (tab.e[j].shape != kShape) {
+            more = false;                // another shape: the caller dispatches it
+          } else {
+            enter(j);
+            switched = true;
+          }
         }
       }
-      load_step(item - start);
+      if (more) load_step(item - start);
     }
     {
       constexpr int V = R * NB;
@@ -740,7 +746,52 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<N> 
     if (!more) break;
     if (switched) bias_sums();
   }
+  return item;
 }
+
+// Row groups of a wave: item, item + stride, ... (grid-stride over the table).
+__device__ __forceinline__ int first_item(int& stride) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  stride = gridDim.x * kWaves;
+  return blockIdx.x * kWaves + wave;
+}
+
+// One GEMV (or a table of GEMVs of one shape) with a fixed (R, NCH).
+template <int FMT, int NB, int R, int NCH>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<1> tab, int batch) {
+  int stride;
+  const int item = first_item(stride);
+  if (item >= tab.total) return;                 // no barriers in this kernel
+  int j = 0;
+  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63);
+}
+
+// A table of GEMVs of one format whose entries may differ in (R, NCH): a
+// wave runs the specialization of the entry its row group belongs to and
+// moves to another specialization when its next row group does.
+template <int FMT, int NB, int N>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTable<N> tab, int batch) {
+  int stride;
+  int item = first_item(stride);
+  if (item >= tab.total) return;                 // no barriers in this kernel
+  const int lane = threadIdx.x & 63;
+  int j = 0;
+  while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
+  while (item < tab.total) {
+    switch (tab.e[j].shape) {
+#define QG_SHAPE(R_, C_) \
+      case xreg_shape(R_, C_): item = xreg_run<FMT, NB, R_, C_, N>(tab, j, item, stride, batch, lane); break;
+      // the shapes launch_gemv_group produces (the kernel's register budget,
+      // and with it its occupancy, is the largest of theirs)
+      QG_SHAPE(4, 1) QG_SHAPE(2, 1)
+      QG_SHAPE(QGEMV_GROUP_R2, 2)
+      QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
+#undef QG_SHAPE
+      default: return;                           // not produced by the host
+    }
+  }
+}
+
 
 // ---------------------------------------------------------------------------
 // Batch 3..8: matrix cores.
@@ -781,33 +832,49 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT> struct MfmaFmt;
+#ifndef QGEMV_MFMA_SLICES_BF16
+#define QGEMV_MFMA_SLICES_BF16 4
+#endif
+#ifndef QGEMV_MFMA_SLICES_INT8
+#define QGEMV_MFMA_SLICES_INT8 2
+#endif
+#ifndef QGEMV_MFMA_SLICES_Q4
+#define QGEMV_MFMA_SLICES_Q4 2
+#endif
+#ifndef QGEMV_MFMA_SLICES_INT4
+#define QGEMV_MFMA_SLICES_INT4 4
+#endif
+// kSlices: 64-byte row slices per step (per lane: 16 bytes each);
+// kChunksPerSlice: 32-position MFMA chunks per slice; kGroups: scale groups
+// per step; kChunksPerGroup: chunks sharing one scale; kStepElems: K
+// elements per step.
 template <> struct MfmaFmt<QGEMV_BF16> {
-  static constexpr int kSlices = 4;          // 64-byte row slices per step
-  static constexpr int kChunksPerSlice = 1;  // 32-position MFMA chunks per slice
-  static constexpr int kGroups = 0;          // scale groups per step
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_BF16;
+  static constexpr int kChunksPerSlice = 1;
+  static constexpr int kGroups = 0;
   static constexpr int kChunksPerGroup = 0;
-  static constexpr int kStepElems = 128;     // K elements per step
+  static constexpr int kStepElems = 32 * kSlices;
 };
 template <> struct MfmaFmt<QGEMV_INT8_G32> {
-  static constexpr int kSlices = 2;
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT8;
   static constexpr int kChunksPerSlice = 2;
-  static constexpr int kGroups = 4;
+  static constexpr int kGroups = 2 * kSlices;
   static constexpr int kChunksPerGroup = 1;
-  static constexpr int kStepElems = 128;
+  static constexpr int kStepElems = 64 * kSlices;
 };
 template <> struct MfmaFmt<QGEMV_Q4_0_G32> {
-  static constexpr int kSlices = 2;
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_Q4;
   static constexpr int kChunksPerSlice = 4;
-  static constexpr int kGroups = 8;
+  static constexpr int kGroups = 4 * kSlices;
   static constexpr int kChunksPerGroup = 1;
-  static constexpr int kStepElems = 256;
+  static constexpr int kStepElems = 128 * kSlices;
 };
 template <> struct MfmaFmt<QGEMV_INT4_G128> {
-  static constexpr int kSlices = 4;
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT4;
   static constexpr int kChunksPerSlice = 4;
-  static constexpr int kGroups = 4;
+  static constexpr int kGroups = kSlices;
   static constexpr int kChunksPerGroup = 4;
-  static constexpr int kStepElems = 512;
+  static constexpr int kStepElems = 128 * kSlices;
 };
 
 // K element at position pos (0..31) of chunk c; position pos = 8q + 4h + j
@@ -939,9 +1006,13 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
       const uint16_t* sbase = S + (rows ? static_cast<size_t>(row0) * ngroups : 0);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, static_cast<uint32_t>(rows * ngroups * 2));
       const int sso = st * (F::kGroups * 2);
-      if constexpr (kSW == 4) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff, sso, 0));
-        s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+      static_assert(kSW == 2 || kSW % 4 == 0, "scale dwords per step");
+      if constexpr (kSW % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < kSW / 4; ++u) {
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * u, sso, 0));
+          s[4 * u] = v.x; s[4 * u + 1] = v.y; s[4 * u + 2] = v.z; s[4 * u + 3] = v.w;
+        }
       } else {
         const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff, sso, 0));
         s[0] = v.x; s[1] = v.y;
@@ -1163,8 +1234,9 @@ hipError_t launch_xreg3(const GemvArgs& a, int grid, hipStream_t st) {
   GemvTable<1> tab{};
   tab.n = 1;
   tab.total = (a.M + R - 1) / R;
-  tab.e[0] = TableEntry{static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, 0, 0};
-  gemv_xreg_kernel<FMT, NB, R, NCH, 1><<<grid, kThreads, 0, st>>>(tab, a.batch);
+  tab.e[0] = TableEntry{static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, 0,
+                        xreg_shape(R, NCH)};
+  gemv_xreg_kernel<FMT, NB, R, NCH><<<grid, kThreads, 0, st>>>(tab, a.batch);
   return hipGetLastError();
 }
 
@@ -1195,41 +1267,27 @@ hipError_t launch_xreg(const GemvArgs& a, int R, int nch, int grid, hipStream_t 
 
 constexpr int kGroupMax = 64;       // GEMVs per grouped launch (kernel-argument table)
 
-template <int FMT, int NB, int R, int NCH>
-hipError_t launch_group4(const GemvArgs* a, int n, int total, int grid, hipStream_t st) {
+// Entries of one format and batch with their (R, NCH) already chosen.
+template <int FMT, int NB>
+hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n, int grid,
+                         hipStream_t st) {
   GemvTable<kGroupMax> tab{};
   tab.n = n;
-  tab.total = total;
   int start = 0;
   for (int i = 0; i < n; ++i) {
     tab.e[i] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
-                          a[i].M, a[i].K, start, 0};
-    start += (a[i].M + R - 1) / R;
+                          a[i].M, a[i].K, start, xreg_shape(R[i], nch[i])};
+    start += (a[i].M + R[i] - 1) / R[i];
   }
-  gemv_xreg_kernel<FMT, NB, R, NCH, kGroupMax><<<grid, kThreads, 0, st>>>(tab, a[0].batch);
+  tab.total = start;
+  gemv_xreg_group_kernel<FMT, NB, kGroupMax><<<grid, kThreads, 0, st>>>(tab, a[0].batch);
   return hipGetLastError();
 }
 
-template <int FMT, int NB, int NCH>
-hipError_t launch_group3(const GemvArgs* a, int n, int R, int total, int grid, hipStream_t st) {
-  if (R == 4) return launch_group4<FMT, NB, 4, NCH>(a, n, total, grid, st);
-  return launch_group4<FMT, NB, 2, NCH>(a, n, total, grid, st);
-}
-
-template <int FMT, int NB>
-hipError_t launch_group2(const GemvArgs* a, int n, int nch, int R, int total, int grid, hipStream_t st) {
-  switch (nch) {
-    case 1: return launch_group3<FMT, NB, 1>(a, n, R, total, grid, st);
-    case 2: return launch_group3<FMT, NB, 2>(a, n, R, total, grid, st);
-    case 3: return launch_group3<FMT, NB, 3>(a, n, R, total, grid, st);
-    default: return launch_group3<FMT, NB, 4>(a, n, R, total, grid, st);
-  }
-}
-
 template <int FMT>
-hipError_t launch_group1(const GemvArgs* a, int n, int nch, int R, int total, int grid, hipStream_t st) {
-  if (round_batch(a[0].batch) == 1) return launch_group2<FMT, 1>(a, n, nch, R, total, grid, st);
-  return launch_group2<FMT, 2>(a, n, nch, R, total, grid, st);
+hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n, int grid, hipStream_t st) {
+  if (round_batch(a[0].batch) == 1) return launch_group2<FMT, 1>(a, R, nch, n, grid, st);
+  return launch_group2<FMT, 2>(a, R, nch, n, grid, st);
 }
 
 // ---- matrix-core kernel: launch plan
@@ -1411,20 +1469,27 @@ int gemv_group_max() { return kGroupMax; }
 
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream) {
   const int cus = device_cu_count();
-  const int nch = gemv_group_class(a[0].fmt, a[0].K, a[0].batch);
   long rows = 0;
   for (int i = 0; i < n; ++i) rows += a[i].M;
-  // rows per wave step: 4 for short rows while that still gives every CU's
-  // waves work; 2 otherwise (longer rows keep more x and weights in registers)
-  const int R = (nch <= 2 && rows / 4 >= static_cast<long>(QGEMV_MIN_WAVES_PER_CU) * cus) ? 4 : 2;
-  int total = 0;
-  for (int i = 0; i < n; ++i) total += (a[i].M + R - 1) / R;
-  const int grid = std::max(1, std::min((total + kWaves - 1) / kWaves, cus * QGEMV_MAX_WG_PER_CU));
+  // rows per wave step: for 1 unit per lane-column, 4 while that still gives
+  // every CU's waves work, else 2; fewer for longer rows, which keep more x
+  // and weights in registers (one kernel serves all entries, and its
+  // register budget, hence its occupancy, is that of its largest shape)
+  const bool r4 = rows / 4 >= static_cast<long>(QGEMV_MIN_WAVES_PER_CU) * cus;
+  int R[kGroupMax], nch[kGroupMax];
+  long total = 0;
+  for (int i = 0; i < n; ++i) {
+    nch[i] = gemv_group_class(a[i].fmt, a[i].K, a[i].batch);
+    R[i] = nch[i] == 1 ? (r4 ? 4 : 2) : nch[i] == 2 ? QGEMV_GROUP_R2 : QGEMV_GROUP_RLONG;
+    total += (a[i].M + R[i] - 1) / R[i];
+  }
+  const int grid = static_cast<int>(std::max<long>(1, std::min<long>((total + kWaves - 1) / kWaves,
+                                                                     static_cast<long>(cus) * QGEMV_MAX_WG_PER_CU)));
   switch (a[0].fmt) {
-    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, n, nch, R, total, grid, stream);
-    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, n, nch, R, total, grid, stream);
-    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, n, nch, R, total, grid, stream);
-    default: return launch_group1<QGEMV_INT4_G128>(a, n, nch, R, total, grid, stream);
+    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, R, nch, n, grid, stream);
+    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, R, nch, n, grid, stream);
+    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, R, nch, n, grid, stream);
+    default: return launch_group1<QGEMV_INT4_G128>(a, R, nch, n, grid, stream);
   }
 }
 

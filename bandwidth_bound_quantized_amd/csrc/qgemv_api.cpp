@@ -264,8 +264,8 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // GEMVs the register-x kernel takes are launched together, one launch per
-  // (format, units per lane-column) class in order of first appearance; the
-  // others are launched one by one.
+  // format (up to gemv_group_max() entries) in order of first appearance;
+  // the others are launched one by one.
   std::vector<qgemv::GemvArgs> todo;
   std::vector<char> done(static_cast<size_t>(n), 0);
   for (int i = 0; i < n; ++i) {
@@ -276,7 +276,7 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
     for (int k = i; k < n; ++k) {
       const qgemv_gemv_desc& h = gemvs[k];
       if (done[k]) continue;
-      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) != cls))
+      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) == 0))
         continue;
       todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
       done[k] = 1;

@@ -45,10 +45,10 @@ bool gemv_uses_lds(int fmt, int K, int batch);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
 // Grouped launches of independent GEMVs (register-x kernel only).
-// gemv_group_class: 0 if (fmt, K, batch) needs the LDS kernel, else the number
-// of 16-byte units per lane-column of a row (1..4); GEMVs of one format, batch
-// and class can share a launch. launch_gemv_group: n <= gemv_group_max()
-// GEMVs of one format, batch and class, already validated.
+// gemv_group_class: 0 if (fmt, K, batch) needs another kernel, else the number
+// of 16-byte units per lane-column of a row (1..4); GEMVs of one format and
+// batch with a nonzero class can share a launch. launch_gemv_group:
+// n <= gemv_group_max() such GEMVs, already validated.
 int gemv_group_class(int fmt, int K, int batch);
 int gemv_group_max();
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream);
