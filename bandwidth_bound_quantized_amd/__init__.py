@@ -26,6 +26,7 @@ SRC_CANONICAL, SRC_BF16 = 0, 1
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
 MAX_BATCH = 8
 ARGMAX_WS_WORDS_PER_ROW = 2
+FUSED_ARGMAX_WS_WORDS_PER_ROW = 4096
 GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
 FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128"}
 
@@ -55,6 +56,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_pack": (c_int, [c_int, c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
         "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
         "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
+        "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
         "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
         "qgemv_status_str": (ctypes.c_char_p, [c_int]),
@@ -69,8 +71,8 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_run_grouped", "qgemv_argmax",
-           "qgemv_stream_read",
+EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_run_grouped",
+           "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
 
@@ -198,6 +200,32 @@ def run_grouped_ptr(descs, batch: int, stream_handle) -> None:
     st = _lib.qgemv_run_grouped(ctypes.cast(descs, ctypes.c_void_p), len(descs), batch, stream_handle)
     if st != OK:
         raise QgemvError(st, "qgemv_run_grouped")
+
+
+def run_grouped_argmax(descs, batch: int, argmax_entry: int, ws, idx, stream=None) -> None:
+    """run_grouped, then idx[:batch] = argmax of each row of descs[argmax_entry]'s y
+    (fused into that GEMV's launch where the small-batch kernel computes it)."""
+    import torch
+    wsp = _dev_ptr(ws, "ws", (torch.int64, torch.uint64))
+    ip = _dev_ptr(idx, "idx", torch.int32)
+    if ws.numel() < batch * FUSED_ARGMAX_WS_WORDS_PER_ROW or idx.numel() < batch:
+        raise ValueError("ws or idx too small")
+    st = _lib.qgemv_run_grouped_argmax(ctypes.cast(descs, ctypes.c_void_p), len(descs), batch,
+                                       argmax_entry, wsp, ip, _stream_handle(stream))
+    _check(st, "qgemv_run_grouped_argmax")
+
+
+def run_grouped_argmax_ptr(descs, batch: int, argmax_entry: int, wsp: int, ip: int, stream_handle) -> None:
+    st = _lib.qgemv_run_grouped_argmax(ctypes.cast(descs, ctypes.c_void_p), len(descs), batch,
+                                       argmax_entry, wsp, ip, stream_handle)
+    if st != OK:
+        raise QgemvError(st, "qgemv_run_grouped_argmax")
+
+
+def fused_argmax_workspace(batch: int, device="cuda"):
+    """A zero-filled workspace for run_grouped_argmax (left zero after every call)."""
+    import torch
+    return torch.zeros(batch * FUSED_ARGMAX_WS_WORDS_PER_ROW, dtype=torch.int64, device=device)
 
 
 def argmax(logits, V: int, batch: int, ws, idx, stream=None) -> None:

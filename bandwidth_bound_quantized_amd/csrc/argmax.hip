@@ -11,8 +11,9 @@
 // max and a counter in the caller's workspace (the last slice writes the
 // index and zeroes both words).
 //
-// Order of values: NaN above everything (every NaN equal, so the first NaN
-// wins), then the IEEE order with -0.0 == +0.0.
+// Order of values (argmax_key.h): NaN above everything (every NaN equal, so
+// the first NaN wins), then the IEEE order with -0.0 == +0.0.
+#include "argmax_key.h"
 #include "qgemv_internal.h"
 #include "qgemv.h"
 
@@ -31,20 +32,6 @@ namespace {
 constexpr int kThreads = QGEMV_ARGMAX_THREADS;
 constexpr int64_t kMinSlice = 1024;   // logits per workgroup, bounds of the adaptive slice
 constexpr int64_t kMaxSlice = QGEMV_ARGMAX_MAX_SLICE;
-
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t i) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t ord;
-  if (v != v) {
-    ord = 0xFFFFFFFFu;
-  } else {
-    if (v == 0.0f) u = 0u;                           // -0.0 ties +0.0
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - i);
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __device__ __forceinline__ uint64_t block_max(uint64_t k, uint64_t* red) {
 #pragma unroll
@@ -96,10 +83,10 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
         const int64_t j = j0 + u * kThreads;
         if (j < n4) {
           const uint32_t i = static_cast<uint32_t>(beg + 4 * j);
-          key = umax64(key, make_key(v[u].x, i));
-          key = umax64(key, make_key(v[u].y, i + 1));
-          key = umax64(key, make_key(v[u].z, i + 2));
-          key = umax64(key, make_key(v[u].w, i + 3));
+          key = umax64(key, argmax_key(v[u].x, i));
+          key = umax64(key, argmax_key(v[u].y, i + 1));
+          key = umax64(key, argmax_key(v[u].z, i + 2));
+          key = umax64(key, argmax_key(v[u].w, i + 3));
         }
       }
     }
@@ -115,14 +102,14 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t i = i0 + u * kThreads;
-        if (i < end) key = umax64(key, make_key(v[u], static_cast<uint32_t>(i)));
+        if (i < end) key = umax64(key, argmax_key(v[u], static_cast<uint32_t>(i)));
       }
     }
   }
   key = block_max(key, red);
   if (threadIdx.x != 0) return;
   if (slices == 1) {
-    idx[b] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFu));
+    idx[b] = argmax_index(key);
     return;
   }
   uint64_t* slot = ws + static_cast<int64_t>(b) * QGEMV_ARGMAX_WS_WORDS_PER_ROW;
@@ -132,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
   if (prev == static_cast<uint32_t>(slices - 1)) {
     // every other slice's max happened before its counter increment
     const uint64_t k = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    idx[b] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFu));
+    idx[b] = argmax_index(k);
     __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

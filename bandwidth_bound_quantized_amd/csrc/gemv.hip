@@ -40,6 +40,7 @@
 // contraction.
 #include <algorithm>
 
+#include "argmax_key.h"
 #include "qgemv_internal.h"
 #include "qgemv.h"
 
@@ -592,7 +593,8 @@ template <int N>
 struct GemvTable {
   int n;        // entries
   int total;    // row groups over all entries
-  int pad0, pad1;
+  int am;       // entry whose outputs the fused argmax reads (grouped launch with argmax)
+  int pad;
   TableEntry e[N];
 };
 
@@ -609,9 +611,11 @@ struct GemvTable {
 // once. A wave reloads its x registers when its next row group belongs to
 // another entry, and issues that group's loads before reducing the current
 // one unless the entry's (R, NCH) differs.
-template <int FMT, int NB, int R, int NCH, int N>
+// With AM, every output of entry tab.am a lane stores also goes into the
+// lane's running argmax key (lkey, for batch row lkey_b).
+template <int FMT, int NB, int R, int NCH, int N, bool AM = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
-                                        int batch, int lane) {
+                                        int batch, int lane, uint64_t& lkey, int& lkey_b) {
   using T = Traits<FMT>;
   constexpr int P = T::kPairs;
   constexpr int kShape = xreg_shape(R, NCH);
@@ -711,6 +715,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     // issue the next row group's loads before reducing this one
     const int grp = item - start;
     const int cur_M = M;
+    const int cur_j = j;
     float* cur_Y = Y;
     item += stride;
     bool more = item < tab.total;
@@ -741,7 +746,15 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       const float res = reduce_wave_rows<V>(v, lane, &idx, &owner);
       const int r = idx / NB, b = idx % NB;
       const int row = grp * R + r;
-      if (owner && row < cur_M && b < batch) cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
+      if (owner && row < cur_M && b < batch) {
+        cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
+        if constexpr (AM) {
+          if (cur_j == tab.am) {
+            lkey = umax64(lkey, argmax_key(res, static_cast<uint32_t>(row)));
+            lkey_b = b;
+          }
+        }
+      }
     }
     if (!more) break;
     if (switched) bias_sums();
@@ -763,32 +776,117 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<1> 
   const int item = first_item(stride);
   if (item >= tab.total) return;                 // no barriers in this kernel
   int j = 0;
-  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63);
+  uint64_t lkey = 0;
+  int lkey_b = 0;
+  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, lkey, lkey_b);
+}
+
+constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most workgroups per launch
+constexpr int kFusedPerThread = kFusedSlots / kThreads;
+constexpr int kFusedSpinLimit = 1 << 20;
+
+// The fused argmax's last step, run by the launch's last workgroup after its
+// own GEMV work: wait until every workgroup has published its key for each
+// batch row (slots[b][w], nonzero once written), take the largest, write the
+// index, and clear the slots for the next call. All of a thread's slot loads
+// are in flight together; the wait is bounded (a key never published - which
+// needs a workgroup that never runs - gives idx -1 instead of a hang).
+__device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, int batch,
+                                                  int32_t* __restrict__ idx, uint64_t* red) {
+  const int tid = threadIdx.x;
+  const int grid = gridDim.x;
+  for (int b = 0; b < batch; ++b) {
+    uint64_t* row = slots + static_cast<size_t>(b) * kFusedSlots;
+    uint64_t v[kFusedPerThread];
+#pragma unroll
+    for (int k = 0; k < kFusedPerThread; ++k) v[k] = 0;
+    bool pending = true;
+    for (int spin = 0; pending && spin < kFusedSpinLimit; ++spin) {
+#pragma unroll
+      for (int k = 0; k < kFusedPerThread; ++k) {
+        const int w = tid + k * kThreads;
+        if (w < grid && v[k] == 0) v[k] = __hip_atomic_load(row + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      pending = false;
+#pragma unroll
+      for (int k = 0; k < kFusedPerThread; ++k) pending |= (tid + k * kThreads < grid) && v[k] == 0;
+      if (pending) __builtin_amdgcn_s_sleep(2);
+    }
+    uint64_t key = 1;
+#pragma unroll
+    for (int k = 0; k < kFusedPerThread; ++k) {
+      const int w = tid + k * kThreads;
+      if (w < grid) {
+        key = umax64(key, v[k]);
+        __hip_atomic_store(row + w, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) key = umax64(key, __shfl_xor(key, o));
+    if ((tid & 63) == 0) red[tid >> 6] = key;
+    const int all_arrived = __syncthreads_and(pending ? 0 : 1);
+    if (tid == 0) {
+      uint64_t m = red[0];
+      for (int w = 1; w < kWaves; ++w) m = umax64(m, red[w]);
+      idx[b] = (all_arrived && m > 1) ? argmax_index(m) : -1;
+    }
+    __syncthreads();
+  }
 }
 
 // A table of GEMVs of one format whose entries may differ in (R, NCH): a
 // wave runs the specialization of the entry its row group belongs to and
 // moves to another specialization when its next row group does.
-template <int FMT, int NB, int N>
-__global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTable<N> tab, int batch) {
+//
+// AM: also idx[b] = argmax of row b of entry tab.am's output (the LM-head
+// logits), in the same launch. Every lane folds the outputs it stores into
+// a key; the keys meet in LDS (64-bit max), each workgroup publishes one key
+// per batch row into its own slot of the caller's workspace with a relaxed
+// device-scope store (no two workgroups touch one address: same-address
+// atomics from thousands of workgroups would queue up), and the launch's last
+// workgroup collects the slots (fused_argmax_tail). A workgroup that stored
+// no output of entry am publishes key 1, which never wins.
+template <int FMT, int NB, int N, bool AM>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTable<N> tab, int batch,
+                                                                   uint64_t* __restrict__ slots,
+                                                                   int32_t* __restrict__ idx) {
+  __shared__ uint64_t wg_key[QGEMV_MAX_BATCH];
+  __shared__ uint64_t red[kWaves];
+  if constexpr (AM) {
+    if (threadIdx.x < QGEMV_MAX_BATCH) wg_key[threadIdx.x] = 1;
+    __syncthreads();
+  }
   int stride;
   int item = first_item(stride);
-  if (item >= tab.total) return;                 // no barriers in this kernel
   const int lane = threadIdx.x & 63;
-  int j = 0;
-  while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
-  while (item < tab.total) {
-    switch (tab.e[j].shape) {
+  uint64_t lkey = 0;
+  int lkey_b = 0;
+  if (item < tab.total) {
+    int j = 0;
+    while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
+    while (item < tab.total) {
+      switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
-      case xreg_shape(R_, C_): item = xreg_run<FMT, NB, R_, C_, N>(tab, j, item, stride, batch, lane); break;
-      // the shapes launch_gemv_group produces (the kernel's register budget,
-      // and with it its occupancy, is the largest of theirs)
-      QG_SHAPE(4, 1) QG_SHAPE(2, 1)
-      QG_SHAPE(QGEMV_GROUP_R2, 2)
-      QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
+        case xreg_shape(R_, C_): \
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, lkey, lkey_b); break;
+        // the shapes launch_gemv_group produces (the kernel's register budget,
+        // and with it its occupancy, is the largest of theirs)
+        QG_SHAPE(4, 1) QG_SHAPE(2, 1)
+        QG_SHAPE(QGEMV_GROUP_R2, 2)
+        QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
 #undef QG_SHAPE
-      default: return;                           // not produced by the host
+        default: item = tab.total;               // not produced by the host
+      }
     }
+  }
+  if constexpr (AM) {
+    if (lkey != 0) atomicMax(reinterpret_cast<unsigned long long*>(&wg_key[lkey_b]),
+                             static_cast<unsigned long long>(lkey));
+    __syncthreads();
+    if (threadIdx.x < batch)
+      __hip_atomic_store(slots + static_cast<size_t>(threadIdx.x) * kFusedSlots + blockIdx.x,
+                         wg_key[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
   }
 }
 
@@ -1267,12 +1365,14 @@ hipError_t launch_xreg(const GemvArgs& a, int R, int nch, int grid, hipStream_t 
 
 constexpr int kGroupMax = 64;       // GEMVs per grouped launch (kernel-argument table)
 
-// Entries of one format and batch with their (R, NCH) already chosen.
+// Entries of one format and batch with their (R, NCH) already chosen; am >= 0:
+// also the argmax of entry am's output (into idx, through slots).
 template <int FMT, int NB>
-hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n, int grid,
-                         hipStream_t st) {
+hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n, int grid, int am,
+                         uint64_t* slots, int32_t* idx, hipStream_t st) {
   GemvTable<kGroupMax> tab{};
   tab.n = n;
+  tab.am = am;
   int start = 0;
   for (int i = 0; i < n; ++i) {
     tab.e[i] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
@@ -1280,14 +1380,18 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
     start += (a[i].M + R[i] - 1) / R[i];
   }
   tab.total = start;
-  gemv_xreg_group_kernel<FMT, NB, kGroupMax><<<grid, kThreads, 0, st>>>(tab, a[0].batch);
+  if (am >= 0)
+    gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<grid, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
+  else
+    gemv_xreg_group_kernel<FMT, NB, kGroupMax, false><<<grid, kThreads, 0, st>>>(tab, a[0].batch, nullptr, nullptr);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n, int grid, hipStream_t st) {
-  if (round_batch(a[0].batch) == 1) return launch_group2<FMT, 1>(a, R, nch, n, grid, st);
-  return launch_group2<FMT, 2>(a, R, nch, n, grid, st);
+hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n, int grid, int am,
+                         uint64_t* slots, int32_t* idx, hipStream_t st) {
+  if (round_batch(a[0].batch) == 1) return launch_group2<FMT, 1>(a, R, nch, n, grid, am, slots, idx, st);
+  return launch_group2<FMT, 2>(a, R, nch, n, grid, am, slots, idx, st);
 }
 
 // ---- matrix-core kernel: launch plan
@@ -1467,7 +1571,8 @@ int gemv_group_class(int fmt, int K, int batch) {
 
 int gemv_group_max() { return kGroupMax; }
 
-hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream) {
+hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,
+                             int32_t* idx) {
   const int cus = device_cu_count();
   long rows = 0;
   for (int i = 0; i < n; ++i) rows += a[i].M;
@@ -1483,13 +1588,14 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream) {
     R[i] = nch[i] == 1 ? (r4 ? 4 : 2) : nch[i] == 2 ? QGEMV_GROUP_R2 : QGEMV_GROUP_RLONG;
     total += (a[i].M + R[i] - 1) / R[i];
   }
-  const int grid = static_cast<int>(std::max<long>(1, std::min<long>((total + kWaves - 1) / kWaves,
-                                                                     static_cast<long>(cus) * QGEMV_MAX_WG_PER_CU)));
+  long cap = static_cast<long>(cus) * QGEMV_MAX_WG_PER_CU;
+  if (am >= 0 && cap > kFusedSlots) cap = kFusedSlots;       // one argmax slot per workgroup
+  const int grid = static_cast<int>(std::max<long>(1, std::min<long>((total + kWaves - 1) / kWaves, cap)));
   switch (a[0].fmt) {
-    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, R, nch, n, grid, stream);
-    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, R, nch, n, grid, stream);
-    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, R, nch, n, grid, stream);
-    default: return launch_group1<QGEMV_INT4_G128>(a, R, nch, n, grid, stream);
+    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, R, nch, n, grid, am, slots, idx, stream);
+    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, R, nch, n, grid, am, slots, idx, stream);
+    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, R, nch, n, grid, am, slots, idx, stream);
+    default: return launch_group1<QGEMV_INT4_G128>(a, R, nch, n, grid, am, slots, idx, stream);
   }
 }
 

@@ -254,7 +254,56 @@ int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x,
 }
 
 
-int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stream) {
+namespace {
+
+// The grouped launches of qgemv_run_grouped; am >= 0: entry am's launch also
+// computes the argmax of its output if the small-batch kernel takes it
+// (*fused = true), else the caller launches the argmax.
+int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t s, int am,
+                     uint64_t* slots, int32_t* idx, bool* fused) {
+  // GEMVs the register-x kernel takes are launched together, one launch per
+  // format (up to gemv_group_max() entries) in order of first appearance;
+  // the others are launched one by one.
+  std::vector<qgemv::GemvArgs> todo;
+  std::vector<int> ids;
+  std::vector<char> done(static_cast<size_t>(n), 0);
+  if (fused) *fused = false;
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const qgemv_gemv_desc& g = gemvs[i];
+    const int cls = qgemv::gemv_group_class(g.fmt, g.K, batch);
+    todo.clear();
+    ids.clear();
+    for (int k = i; k < n; ++k) {
+      const qgemv_gemv_desc& h = gemvs[k];
+      if (done[k]) continue;
+      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) == 0))
+        continue;
+      todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
+      ids.push_back(k);
+      done[k] = 1;
+    }
+    const int maxn = cls == 0 ? 1 : qgemv::gemv_group_max();
+    for (size_t off = 0; off < todo.size(); off += maxn) {
+      const int cnt = static_cast<int>(std::min(todo.size() - off, static_cast<size_t>(maxn)));
+      hipError_t e;
+      if (cls == 0) {
+        e = qgemv::launch_gemv(todo[off], s);
+      } else {
+        int local_am = -1;
+        for (int t = 0; t < cnt; ++t)
+          if (ids[off + t] == am) local_am = t;
+        e = qgemv::launch_gemv_group(&todo[off], cnt, s, local_am, slots, idx);
+        if (local_am >= 0 && fused) *fused = true;
+      }
+      const int st = record_hip(e);
+      if (st) return st;
+    }
+  }
+  return QGEMV_OK;
+}
+
+int check_grouped(const qgemv_gemv_desc* gemvs, int n, int batch) {
   if (!gemvs || n < 1) return QGEMV_EINVAL;
   if (n > QGEMV_GROUP_MAX) return QGEMV_ESHAPE;
   for (int i = 0; i < n; ++i) {
@@ -262,35 +311,30 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
     const int st = check_run_args(g.fmt, g.W, g.scales, g.x, g.y, g.M, g.K, batch);
     if (st) return st;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // GEMVs the register-x kernel takes are launched together, one launch per
-  // format (up to gemv_group_max() entries) in order of first appearance;
-  // the others are launched one by one.
-  std::vector<qgemv::GemvArgs> todo;
-  std::vector<char> done(static_cast<size_t>(n), 0);
-  for (int i = 0; i < n; ++i) {
-    if (done[i]) continue;
-    const qgemv_gemv_desc& g = gemvs[i];
-    const int cls = qgemv::gemv_group_class(g.fmt, g.K, batch);
-    todo.clear();
-    for (int k = i; k < n; ++k) {
-      const qgemv_gemv_desc& h = gemvs[k];
-      if (done[k]) continue;
-      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) == 0))
-        continue;
-      todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
-      done[k] = 1;
-    }
-    const int maxn = cls == 0 ? 1 : qgemv::gemv_group_max();
-    for (size_t off = 0; off < todo.size(); off += maxn) {
-      const int cnt = static_cast<int>(std::min(todo.size() - off, static_cast<size_t>(maxn)));
-      const hipError_t e = cls == 0 ? qgemv::launch_gemv(todo[off], s)
-                                    : qgemv::launch_gemv_group(&todo[off], cnt, s);
-      const int st = record_hip(e);
-      if (st) return st;
-    }
-  }
   return QGEMV_OK;
+}
+
+}  // namespace
+
+int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stream) {
+  const int st = check_grouped(gemvs, n, batch);
+  if (st) return st;
+  return run_grouped_impl(gemvs, n, batch, static_cast<hipStream_t>(stream), -1, nullptr, nullptr, nullptr);
+}
+
+int qgemv_run_grouped_argmax(const qgemv_gemv_desc* gemvs, int n, int batch, int argmax_entry,
+                             uint64_t* ws, int32_t* idx, void* stream) {
+  int st = check_grouped(gemvs, n, batch);
+  if (st) return st;
+  if (argmax_entry < 0 || argmax_entry >= n || !ws || !idx) return QGEMV_EINVAL;
+  if (!aligned(ws, 8) || !aligned(idx, 4)) return QGEMV_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool fused = false;
+  st = run_grouped_impl(gemvs, n, batch, s, argmax_entry, ws, idx, &fused);
+  if (st) return st;
+  if (fused) return QGEMV_OK;
+  const qgemv_gemv_desc& g = gemvs[argmax_entry];
+  return record_hip(qgemv::launch_argmax(g.y, g.M, batch, ws, idx, s));
 }
 
 int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,

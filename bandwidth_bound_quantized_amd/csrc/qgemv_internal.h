@@ -49,9 +49,13 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 // of 16-byte units per lane-column of a row (1..4); GEMVs of one format and
 // batch with a nonzero class can share a launch. launch_gemv_group:
 // n <= gemv_group_max() such GEMVs, already validated.
+// am >= 0: the launch also writes idx[b] = argmax of row b of a[am].y, using
+// slots (batch * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW words, zero on entry,
+// zero on exit).
 int gemv_group_class(int fmt, int K, int batch);
 int gemv_group_max();
-hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream);
+hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am = -1,
+                             uint64_t* slots = nullptr, int32_t* idx = nullptr);
 
 // Launch the argmax (one kernel). ws: batch * 2 u64 words, zero on entry.
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,

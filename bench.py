@@ -95,6 +95,8 @@ class Workload:
         self.bytes = [gemv_bytes(qg, g.fmt, g.M, g.K, B) for g in self.gemvs]
         self.argmax_bytes = 4 * B * self.gemvs[-1].M + 4 * B if self.has_argmax else 0
         self.step_bytes = sum(self.bytes) + self.argmax_bytes
+        # with the argmax inside the LM head's launch the logits are not read again
+        self.fused_bytes = sum(self.bytes) + (4 * B if self.has_argmax else 0)
         resident = sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0) for g in self.gemvs)
         self.n_sets = max(1, math.ceil(rotate_bytes / resident))
         dev = "cuda"
@@ -113,7 +115,7 @@ class Workload:
                 Xi = X if i == 0 else X.clone()
                 Y = torch.empty((B, g.M), dtype=torch.float32, device=dev)
                 items.append((Wi, Si, Xi, Y))
-            ws = qg.argmax_workspace(B) if self.has_argmax else None
+            ws = qg.fused_argmax_workspace(B) if self.has_argmax else None
             idx = torch.empty(B, dtype=torch.int32, device=dev) if self.has_argmax else None
             self.sets.append((items, ws, idx))
         torch.cuda.synchronize()
@@ -159,8 +161,25 @@ class Workload:
             if st != qg.OK:
                 raise qg.QgemvError(st, "qgemv_argmax")
 
+    def step_fused(self, i, stream_handle):
+        """The step's GEMVs and the LM-head argmax in one qgemv_run_grouped_argmax call
+        (the argmax runs inside the LM head's launch where the small-batch kernel takes it)."""
+        qg = self.qg
+        p, wsp, ip = self.ptrs[i % self.n_sets]
+        qg.run_grouped_argmax_ptr(self.descs[i % self.n_sets], self.B, len(self.gemvs) - 1, wsp, ip,
+                                  stream_handle)
+
     def launch_class(self, key, i, stream_handle):
-        self.qg.run_grouped_ptr(self.class_descs[i % self.n_sets][key], self.B, stream_handle)
+        """One launch class as the step runs it: with the LM-head argmax fused in if the
+        class holds the LM head."""
+        am = len(self.gemvs) - 1
+        descs = self.class_descs[i % self.n_sets][key]
+        if self.has_argmax and am in self.classes[key]:
+            p, wsp, ip = self.ptrs[i % self.n_sets]
+            self.qg.run_grouped_argmax_ptr(descs, self.B, self.classes[key].index(am), wsp, ip,
+                                           stream_handle)
+        else:
+            self.qg.run_grouped_ptr(descs, self.B, stream_handle)
 
     def class_bytes(self, key):
         return sum(self.bytes[j] for j in self.classes[key])
@@ -275,8 +294,8 @@ def size_sweep(qg, torch, rotate_bytes):
 
 
 def pmc_pass(qg, torch, wl, steps):
-    """Kernels of known traffic for scaling the HBM byte counters, then eager grouped steps
-    (the launches `value` times)."""
+    """Kernels of known traffic for scaling the HBM byte counters, then eager steps as
+    `value` times them."""
     nbytes = 64 << 20
     buf = torch.full((nbytes // 4,), 7, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
@@ -286,7 +305,7 @@ def pmc_pass(qg, torch, wl, steps):
     torch.cuda.synchronize()
     h = torch.cuda.current_stream().cuda_stream
     for i in range(steps):
-        wl.step_grouped(i, h)
+        (wl.step_fused if wl.has_argmax else wl.step_grouped)(i, h)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_pass": True, "calib_bytes": nbytes, "steps": steps,
                       "gemvs": [[g.name, g.M, g.K, b] for g, b in zip(wl.gemvs, wl.bytes)]}), flush=True)
@@ -340,18 +359,23 @@ def main():
     # sequential: one qgemv_run launch per GEMV, as a decode step whose GEMVs
     # depend on each other must run them.
     results = {}
-    for mode, fn in (("sequential", wl.step), ("grouped", wl.step_grouped)):
+    modes = [("sequential", wl.step), ("grouped", wl.step_grouped)]
+    if wl.has_argmax:
+        modes.append(("fused", wl.step_fused))
+    for mode, fn in modes:
         g_warm = capture(torch, fn, max(1, args.warmup))
         time_graph(torch, g_warm)
         g_steps = capture(torch, fn, args.steps)
         ms = time_graph(torch, g_steps) / args.steps
         results[mode] = ms
-        print(f"[bench] {mode}: {ms * 1e3:.2f} us/step, {wl.step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s",
+        nb = wl.fused_bytes if mode == "fused" else wl.step_bytes
+        print(f"[bench] {mode}: {ms * 1e3:.2f} us/step, {nb / (ms * 1e-3) / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
         del g_warm, g_steps
-    ms_per_step = results["grouped"]
-    value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    ms_per_step = results["fused"] if wl.has_argmax else results["grouped"]
+    value = (wl.fused_bytes if wl.has_argmax else wl.step_bytes) / (ms_per_step * 1e-3) / 1e9
     value_seq = wl.step_bytes / (results["sequential"] * 1e-3) / 1e9
+    value_grp = wl.step_bytes / (results["grouped"] * 1e-3) / 1e9
 
     # ---- dominant kernel: the grouped launch with the most bytes, timed alone
     dom_key = max(wl.classes, key=wl.class_bytes)
@@ -396,8 +420,12 @@ def main():
              3: "int8_g32_llama32_1b_gemv_set", 4: "q4_0_g32_tinyllama_decode_step_89_gemvs+argmax",
              5: "int4_g128_ffn+int8_g32_lm_head+argmax"}
     dtypes = {1: "bf16", 2: "q4_0", 3: "int8", 4: "q4_0", 5: "int4/int8"}
-    dom_label = (f"qgemv_run_grouped launch [{wl.class_label(dom_key)}]" if dom_key[0] != "alone"
-                 else f"qgemv_run {wl.gemvs[dom_key[1]].name}")
+    if dom_key[0] == "alone":
+        dom_label = f"qgemv_run {wl.gemvs[dom_key[1]].name}"
+    elif wl.has_argmax and len(wl.gemvs) - 1 in wl.classes[dom_key]:
+        dom_label = f"qgemv_run_grouped_argmax launch [{wl.class_label(dom_key)}+argmax]"
+    else:
+        dom_label = f"qgemv_run_grouped launch [{wl.class_label(dom_key)}]"
     traffic = recorded_traffic(dom_label, names[cfg], B)
     out = {
         "metric": "fused-dequant GEMV achieved HBM GB/s and % of peak (bf16/int8/Q4_0, batch 1)",
@@ -409,6 +437,8 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "value_sequential": round(value_seq, 1),
         "ms_per_step_sequential": round(results["sequential"], 6),
+        "value_grouped_separate_argmax": round(value_grp, 1) if wl.has_argmax else None,
+        "ms_per_step_grouped_separate_argmax": round(results["grouped"], 6) if wl.has_argmax else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -417,11 +447,14 @@ def main():
         "config": {"workload": names[cfg], "batch": B,
                    "gemvs": [[g.name, g.M, g.K] for g in wl.gemvs][:6] + (
                        [["...", len(wl.gemvs)]] if len(wl.gemvs) > 6 else []),
-                   "bytes_per_step": wl.step_bytes, "rotation_sets": wl.n_sets,
+                   "bytes_per_step": wl.fused_bytes if wl.has_argmax else wl.step_bytes,
+                   "rotation_sets": wl.n_sets,
                    "rotation_bytes": wl.n_sets * sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0)
                                                      for g in wl.gemvs),
-                   "execution": "value: the step's independent GEMVs in one qgemv_run_grouped call "
-                                "(one launch per format) + qgemv_argmax; "
+                   "execution": "value: the step's independent GEMVs (one launch per format) and, "
+                                "with an LM head, its argmax in one qgemv_run_grouped_argmax call "
+                                "(the argmax inside the LM head's launch at batch <= 2); "
+                                "value_grouped_separate_argmax: qgemv_run_grouped + qgemv_argmax; "
                                 "value_sequential: one qgemv_run launch per GEMV + qgemv_argmax",
                    "timing": "HIP graph of exactly `steps` steps, events on the launch stream"},
         "pct_of_spec_8TBps": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -179,11 +179,43 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
  * every call leaves it all zero again, so one zero-fill at allocation time
  * suffices. Calls that may run concurrently need distinct ws buffers.
  * 1 <= batch <= 8, 1 <= V <= 2^31 - 1. One kernel launch; asynchronous.
- * A row of up to 32768 logits is reduced by one workgroup without touching
- * ws; longer rows are split into slices that meet in ws with atomics.
+ * Rows are split into slices of 1-16 Ki logits (about 32 workgroups per
+ * launch); a row of one slice is reduced by one workgroup without touching
+ * ws, the slices of a longer row meet in ws with atomics.
  */
 int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                  void* stream);
+
+/* u64 words of workspace qgemv_run_grouped_argmax needs per batch row */
+#define QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW 4096
+
+/*
+ * qgemv_run_grouped_argmax - a decode step's end in one call: the GEMVs of
+ * qgemv_run_grouped, then idx[b] = the argmax of row b of
+ * gemvs[argmax_entry].y (the LM-head logits, V = that entry's M), with
+ * qgemv_argmax's semantics ("infer": the decode pipeline figure ends the
+ * step with the LM head and the argmax; its design notes fuse work into the
+ * producing kernel to save launches).
+ * When the small-batch kernel computes the argmax entry (batch <= 2, row
+ * length as in qgemv_run_grouped), the argmax runs inside that launch: each
+ * workgroup folds the logits it writes into one key per batch row and
+ * publishes it in its own word of ws, and the launch's last workgroup takes
+ * the largest; no separate launch and no second pass over the logits.
+ * Otherwise the argmax is a qgemv_argmax launch after the GEMVs, on the same
+ * stream, with the same ws. The logits (gemvs[argmax_entry].y) are written
+ * in full either way.
+ * ws: device, batch * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW u64 words (8-byte
+ * aligned), owned by the caller, all zero before its first use; every call
+ * leaves it all zero. Calls that may run concurrently need distinct ws.
+ * idx: device int32 [batch], 4-byte aligned. (idx -1 would mean a workgroup
+ * never published its key, which a launch that runs to completion rules
+ * out; the last workgroup's wait for the others is bounded.)
+ * Errors: as qgemv_run_grouped; EINVAL for argmax_entry outside [0, n) or a
+ * null ws or idx; EALIGN for misaligned ws or idx. Nothing is launched on
+ * error.
+ */
+int qgemv_run_grouped_argmax(const qgemv_gemv_desc* gemvs, int n, int batch, int argmax_entry,
+                             uint64_t* ws, int32_t* idx, void* stream);
 
 /*
  * qgemv_stream_read - measurement helper: read `bytes` bytes of device

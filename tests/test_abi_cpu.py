@@ -234,3 +234,23 @@ def test_grouped_validation_errors_before_any_launch():
                       ({"y": FAKE + 4}, qg.EALIGN), ({"scales": None}, qg.EINVAL), ({"M": 0}, qg.ESHAPE)]:
         arr = descs({}, {}, bad, {})
         assert L.qgemv_run_grouped(ctypes.cast(arr, ctypes.c_void_p), 4, 1, None) == want, bad
+
+
+def test_grouped_argmax_validation_errors_before_any_launch():
+    L = qg.lib()
+    arr = (qg.GemvDesc * 2)()
+    for i in range(2):
+        arr[i] = qg.GemvDesc(W=FAKE, scales=FAKE, x=FAKE, y=FAKE, fmt=qg.Q4_0_G32, M=64, K=2048, reserved=0)
+    a = ctypes.cast(arr, ctypes.c_void_p)
+    ws, idx = FAKE, FAKE
+    f = L.qgemv_run_grouped_argmax
+    assert f(None, 1, 1, 0, ws, idx, None) == qg.EINVAL
+    assert f(a, 2, 9, 0, ws, idx, None) == qg.ESHAPE
+    assert f(a, 2, 1, 2, ws, idx, None) == qg.EINVAL          # entry out of range
+    assert f(a, 2, 1, -1, ws, idx, None) == qg.EINVAL
+    assert f(a, 2, 1, 1, None, idx, None) == qg.EINVAL
+    assert f(a, 2, 1, 1, ws, None, None) == qg.EINVAL
+    assert f(a, 2, 1, 1, ws + 4, idx, None) == qg.EALIGN
+    assert f(a, 2, 1, 1, ws, idx + 2, None) == qg.EALIGN
+    arr[1].K = 40                                              # a bad GEMV still fails first
+    assert f(a, 2, 1, 1, ws, idx, None) == qg.ESHAPE

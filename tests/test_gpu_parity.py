@@ -386,3 +386,83 @@ def test_mfma_path_all_codes_extreme(fmt):
     x = synth.bf16_normal(rng, (B, K), 1.0) & np.uint16(0x7FFF)     # |x|: sign bit cleared
     y = gpu_gemv(fmt, w, s, x, M, K, B)
     assert_parity(fmt, w, s, x, M, K, B, y, what="extreme")
+
+
+# ------------------------------------------------- grouped GEMVs + fused argmax
+def _grouped_argmax(gemvs, B, am, ws=None):
+    """Upload, run all gemvs + the argmax of entry am in one qgemv_run_grouped_argmax call."""
+    dev_items = []
+    for g in gemvs:
+        W = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+        S = dev(g.s.reshape(-1)) if g.s is not None else None
+        X = dev(np.ascontiguousarray(g.x).reshape(B, g.K))
+        Y = torch.full((B, g.M), float("nan"), dtype=torch.float32, device=DEV)
+        dev_items.append((g.fmt, W, S, X, Y, g.M, g.K))
+    descs = qg.grouped_descs(dev_items)
+    ws = qg.fused_argmax_workspace(B) if ws is None else ws
+    idx = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    print(f"[gpu] qgemv_run_grouped_argmax n={len(gemvs)} B={B} am={am}", flush=True)
+    qg.run_grouped_argmax(descs, B, am, ws, idx)
+    torch.cuda.synchronize()
+    return [it[4].cpu().numpy() for it in dev_items], idx.cpu().numpy(), ws
+
+
+@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (5, 1), (5, 2), (2, 4), (5, 8)])
+def test_grouped_argmax_workloads(cfg, B):
+    """The step's GEMVs and the LM-head argmax in one call (fused into the LM head's launch
+    at B <= 2, a separate argmax launch otherwise): logits within the GEMV tolerance, the
+    index bit-exact against the oracle's argmax of the GPU's own logits, ws back to zero."""
+    gemvs = [synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+             for sp in synth.workload_specs(cfg)]
+    am = len(gemvs) - 1
+    ys, idx, ws = _grouped_argmax(gemvs, B, am)
+    for g, y in zip(gemvs, ys):
+        assert np.isfinite(y).all(), g.name
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"fused {g.name}")
+    assert (idx == oracle.argmax_ref(ys[am])).all(), (idx, oracle.argmax_ref(ys[am]))
+    assert (ws.cpu().numpy() == 0).all()
+
+
+def test_grouped_argmax_ties_across_workgroups():
+    """bf16 LM head whose rows give exactly 0 except rows made negative: the maximum 0.0 is
+    tied at rows far apart (different waves and workgroups); the lowest index must win,
+    with the LM head in the middle of the entry table."""
+    M, K, B = 20000, 2048, 2
+    rng = np.random.default_rng(21)
+    x = synth.bf16_normal(rng, (B, K), 1.0)
+    x[1] = x[0]
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    w = np.zeros((M, K), np.uint16)
+    neg = np.ones(M, bool)
+    neg[[5003, 7777, 19999]] = False                      # the zero rows
+    # negative rows: w = -0.01 * sign(x), so the dot product is -0.01 * sum|x| < 0
+    wrow = synth.round_f32_to_bf16_bits((-0.01 * np.sign(xf[0])).astype(np.float32))
+    w[neg] = wrow
+    lm = synth.Gemv("lm", synth.BF16, M, K, B, w, None, x, (0, 0, 0))
+    other = synth.make_gemv("o", synth.BF16, 2048, 2048, B, 9, 1, "o")
+    tail = synth.make_gemv("t", synth.BF16, 100, 1024, B, 9, 2, "qkv")
+    ys, idx, ws = _grouped_argmax([other, lm, tail], B, 1)
+    y = ys[1]
+    assert (y[:, ~neg] == 0).all() and (y[:, neg] < 0).all()
+    assert (idx == [5003, 5003]).all(), idx
+    assert (ws.cpu().numpy() == 0).all()
+
+
+def test_grouped_argmax_nan_logit_and_workspace_reuse():
+    """A NaN scale makes that row's logits NaN: the first NaN row wins (NumPy semantics).
+    Five calls reuse one workspace, which is zero after each."""
+    B = 2
+    sp = synth.workload_specs(2)[-1]
+    g = synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
+    ws = qg.fused_argmax_workspace(B)
+    for rows in ([], [30001], [12345, 30001], [0], [31999, 4]):
+        s = g.s.copy()
+        for r in rows:
+            s[r, 7] = 0x7E00                                   # binary16 NaN
+        gg = synth.Gemv(g.name, g.fmt, g.M, g.K, B, g.w, s, g.x, g.seeds)
+        ys, idx, ws = _grouped_argmax([gg], B, 0, ws)
+        want = oracle.argmax_ref(ys[0])
+        assert (idx == want).all(), (rows, idx, want)
+        if rows:
+            assert (idx == min(rows)).all()
+        assert (ws.cpu().numpy() == 0).all()
