@@ -614,11 +614,50 @@ struct GemvTable {
 // once. A wave reloads its x registers when its next row group belongs to
 // another entry, and issues that group's loads before reducing the current
 // one unless the entry's (R, NCH) differs.
+// Fused-argmax state of a lane (see gemv_xreg_group_kernel): its running key
+// over the LM-head outputs it stored, their batch row, and whether its wave
+// has already handed its keys to the workgroup.
+struct AmLane {
+  uint64_t key = 0;
+  int b = 0;
+  bool left = false;
+};
+
+// Fused-argmax LDS of a workgroup: the key per batch row and the number of
+// waves that have left the LM-head entry.
+struct AmShared {
+  uint64_t key[QGEMV_MAX_BATCH];
+  int left;
+};
+
+// A wave is done with the LM-head entry: fold its lanes' keys into the
+// workgroup's, count itself; the workgroup's last wave publishes the keys in
+// the workgroup's own workspace words (relaxed device-scope stores).
+__device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __restrict__ slots,
+                                         int batch, int lane) {
+  if (am.key != 0)
+    atomicMax(reinterpret_cast<unsigned long long*>(&sh->key[am.b]), static_cast<unsigned long long>(am.key));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&sh->left, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  prev = __shfl(prev, 0);
+  if (prev == kWaves - 1) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (lane < batch)
+      __hip_atomic_store(slots + static_cast<size_t>(lane) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + blockIdx.x,
+                         sh->key[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  am.left = true;
+}
+
 // With AM, every output of entry tab.am a lane stores also goes into the
-// lane's running argmax key (lkey, for batch row lkey_b).
+// lane's running argmax key, and after the wave's last row group of that
+// entry the wave hands its keys over (am_leave).
 template <int FMT, int NB, int R, int NCH, int N, bool AM = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
-                                        int batch, int lane, uint64_t& lkey, int& lkey_b) {
+                                        int batch, int lane, AmLane& am, AmShared* am_sh,
+                                        uint64_t* am_slots) {
   using T = Traits<FMT>;
   constexpr int P = T::kPairs;
   constexpr int kShape = xreg_shape(R, NCH);
@@ -753,11 +792,17 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
         cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
         if constexpr (AM) {
           if (cur_j == tab.am) {
-            lkey = umax64(lkey, argmax_key(res, static_cast<uint32_t>(row)));
-            lkey_b = b;
+            am.key = umax64(am.key, argmax_key(res, static_cast<uint32_t>(row)));
+            am.b = b;
           }
         }
       }
+    }
+    if constexpr (AM) {
+      // the entry's row groups are one contiguous range of items
+      const int am_end = tab.am + 1 < tab.n ? tab.e[tab.am + 1].start : tab.total;
+      if (cur_j == tab.am && !am.left && (item >= am_end || item >= tab.total))
+        am_leave(am, am_sh, am_slots, batch, lane);
     }
     if (!more) break;
     if (switched) bias_sums();
@@ -779,9 +824,8 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<1> 
   const int item = first_item(stride);
   if (item >= tab.total) return;                 // no barriers in this kernel
   int j = 0;
-  uint64_t lkey = 0;
-  int lkey_b = 0;
-  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, lkey, lkey_b);
+  AmLane am;
+  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, am, nullptr, nullptr);
 }
 
 constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most workgroups per launch
@@ -842,36 +886,43 @@ __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, 
 // moves to another specialization when its next row group does.
 //
 // AM: also idx[b] = argmax of row b of entry tab.am's output (the LM-head
-// logits), in the same launch. Every lane folds the outputs it stores into
-// a key; the keys meet in LDS (64-bit max), each workgroup publishes one key
-// per batch row into its own slot of the caller's workspace with a relaxed
-// device-scope store (no two workgroups touch one address: same-address
-// atomics from thousands of workgroups would queue up), and the launch's last
-// workgroup collects the slots (fused_argmax_tail). A workgroup that stored
-// no output of entry am publishes key 1, which never wins.
+// logits), in the same launch. The host puts that entry first, so its row
+// groups are taken in the first rounds. Every lane folds the outputs it
+// stores into a key; when a wave is done with the entry its keys meet the
+// workgroup's in LDS (64-bit max), and the workgroup's last such wave
+// publishes one key per batch row into the workgroup's own word of the
+// caller's workspace with a relaxed device-scope store (no two workgroups
+// touch one address: same-address atomics from hundreds of workgroups would
+// queue up). The launch's last workgroup collects the words at its end
+// (fused_argmax_tail), by which time they are normally all there. A
+// workgroup that stored no output of the entry publishes key 1, which never
+// wins.
 template <int FMT, int NB, int N, bool AM>
 __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTable<N> tab, int batch,
                                                                    uint64_t* __restrict__ slots,
                                                                    int32_t* __restrict__ idx) {
-  __shared__ uint64_t wg_key[QGEMV_MAX_BATCH];
+  __shared__ AmShared am_sh;
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
-    if (threadIdx.x < QGEMV_MAX_BATCH) wg_key[threadIdx.x] = 1;
+    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
+    if (threadIdx.x == 0) am_sh.left = 0;
     __syncthreads();
   }
   int stride;
   int item = first_item(stride);
   const int lane = threadIdx.x & 63;
-  uint64_t lkey = 0;
-  int lkey_b = 0;
+  AmLane am;
   if (item < tab.total) {
     int j = 0;
     while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
     while (item < tab.total) {
+      if constexpr (AM) {
+        if (j != tab.am && !am.left) am_leave(am, &am_sh, slots, batch, lane);
+      }
       switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
         case xreg_shape(R_, C_): \
-          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, lkey, lkey_b); break;
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots); break;
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
@@ -883,12 +934,8 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
     }
   }
   if constexpr (AM) {
-    if (lkey != 0) atomicMax(reinterpret_cast<unsigned long long*>(&wg_key[lkey_b]),
-                             static_cast<unsigned long long>(lkey));
+    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
     __syncthreads();
-    if (threadIdx.x < batch)
-      __hip_atomic_store(slots + static_cast<size_t>(threadIdx.x) * kFusedSlots + blockIdx.x,
-                         wg_key[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
   }
 }
@@ -1384,10 +1431,11 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
                          uint64_t* slots, int32_t* idx, hipStream_t st) {
   GemvTable<kGroupMax> tab{};
   tab.n = n;
-  tab.am = am;
+  tab.am = am >= 0 ? 0 : -1;            // the argmax entry goes first (its row groups first)
   int start = 0;
-  for (int i = 0; i < n; ++i) {
-    tab.e[i] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
+  for (int t = 0; t < n; ++t) {
+    const int i = am < 0 ? t : t == 0 ? am : (t <= am ? t - 1 : t);
+    tab.e[t] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
                           a[i].M, a[i].K, start, xreg_shape(R[i], nch[i])};
     start += (a[i].M + R[i] - 1) / R[i];
   }
