@@ -972,8 +972,10 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
 // Work split: a workgroup has TW x KS waves; each of TW tiles of 16 rows is
 // shared by KS waves that take equal contiguous ranges of the row's steps
 // (a step is kSlices 64-byte slices). The KS partial tiles are added in LDS
-// in a fixed order. Workgroups loop over tiles; every wave issues the loads
-// of its next step before computing the current one.
+// in a fixed order. A "unit" is TW consecutive tiles; a workgroup takes a
+// contiguous range of units (of one GEMV, or of several GEMVs of one K in a
+// grouped launch); every wave issues the loads of its next step before
+// computing the current one.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1093,17 +1095,46 @@ __device__ __forceinline__ float scale_of(const uint32_t* s, int g) {
 
 constexpr int kMfmaMaxThreads = 1024;
 
+// One GEMV of a matrix-core launch. Its tiles are taken in "units" of TW
+// tiles (TW = waves per workgroup / KS); ustart numbers the entry's first
+// unit in the launch.
+struct MfmaEntry {
+  const uint8_t* W;
+  const uint16_t* S;
+  const uint16_t* X;
+  float* Y;
+  int M;
+  int K;
+  int ustart;
+  int pad;
+};
+
+// Up to N GEMVs of one format, K and batch (by value: kernel arguments).
+template <int N>
+struct MfmaTable {
+  int n;
+  int units;    // over all entries
+  int KS;       // waves sharing a tile
+  int pad;
+  MfmaEntry e[N];
+};
+
+// Units [g0, g1) of one entry (the body of the matrix-core kernel).
 template <int FMT, int NB>
-__global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
-    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
-    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch, int KS, int iters) {
+__device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1, int batch, int KS,
+                                           u32x4* lds_v4) {
   using F = MfmaFmt<FMT>;
   constexpr int kCPS = F::kChunksPerSlice;
   constexpr int kChunks = F::kSlices * kCPS;          // chunks per step
   constexpr int kSW = F::kGroups > 0 ? F::kGroups / 2 : 1;   // scale dwords per step
   constexpr int kOutLanes = 4 * NB;                    // lanes holding real batch rows
-  extern __shared__ u32x4 lds_v4[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds_v4);
+  const uint8_t* __restrict__ W = ent.W;
+  const uint16_t* __restrict__ S = ent.S;
+  const uint16_t* __restrict__ X = ent.X;
+  float* __restrict__ Y = ent.Y;
+  const int M = ent.M, K = ent.K;
+  const int iters = g1 - g0;                           // units of this call
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1130,15 +1161,15 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
   u32x4 wa[F::kSlices], wb[F::kSlices];
   uint32_t sa[kSW], sb[kSW];
 
-  // loads of step s (of this wave's range) of the tile of iteration n;
-  // rows past M (and whole tiles past the end) read as zero
+  // loads of step s (of this wave's range) of the tile of unit g0 + n;
+  // rows past M, and units past g1, read as zero
   auto load = [&](u32x4 (&w)[F::kSlices], uint32_t (&s)[kSW], int n, int st_local) {
-    const int tile = (n * gridDim.x + blockIdx.x) * TW + tg;
+    const int tile = (g0 + n) * TW + tg;
     const int row0 = tile * 16;
     // (written as a select and a min: a clamp would be selected as a vector
     // med3, and a buffer resource built from a vector register is looped
     // over lanes)
-    const int rows = row0 < M ? min(16, M - row0) : 0;
+    const int rows = (n < iters && row0 < M) ? min(16, M - row0) : 0;
     const int st = ks * Lw + st_local;
     // The lane's offset (row i, byte 16q) is the VGPR offset, which the
     // range check covers: rows past M read as zero. The step's offset along
@@ -1237,7 +1268,7 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
 
   // D tile -> y: lane (i, q) holds batch rows 4q..4q+3 of row i of the tile
   auto store = [&](const f32x4& v, int n) {
-    const int tile = (n * gridDim.x + blockIdx.x) * TW + tg;
+    const int tile = (g0 + n) * TW + tg;
     const int row = tile * 16 + i;
     if (row < M) {
 #pragma unroll
@@ -1345,6 +1376,28 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(
     if (s1 + 1 == Lw) finish(n1, acc, bacc);
     n = n2;
     s = s2;
+  }
+}
+
+// A table of GEMVs of one format, K and batch. Workgroup w takes the
+// contiguous units [w*units/G, (w+1)*units/G), entry by entry (x is staged
+// again when the entry changes), so most workgroups stage x once.
+template <int FMT, int NB, int N>
+__global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch) {
+  extern __shared__ u32x4 lds_v4[];
+  const long U = tab.units, G = gridDim.x;
+  const int u0 = static_cast<int>(blockIdx.x * U / G);
+  const int u1 = static_cast<int>((blockIdx.x + 1) * U / G);
+  if (u0 >= u1) return;                          // the whole workgroup (no barrier reached)
+  int j = 0;
+  if constexpr (N > 1) {
+    while (j + 1 < tab.n && u0 >= tab.e[j + 1].ustart) ++j;
+  }
+  for (int u = u0; u < u1; ++j) {
+    const int uend = min(u1, (N > 1 && j + 1 < tab.n) ? tab.e[j + 1].ustart : tab.units);
+    if (u != u0) __syncthreads();                // the previous entry's LDS is no longer read
+    mfma_units<FMT, NB>(tab.e[j], u - tab.e[j].ustart, uend - tab.e[j].ustart, batch, tab.KS, lds_v4);
+    u = uend;
   }
 }
 
@@ -1486,7 +1539,7 @@ size_t mfma_lds_bytes(int fmt, int K, int NB, int KS, int TW) {
 }
 
 struct MfmaPlan {
-  int KS = 0, TW = 0, grid = 0, iters = 0;
+  int KS = 0, TW = 0, grid = 0;
   size_t lds = 0;
 };
 
@@ -1526,7 +1579,6 @@ bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
         best.KS = KS;
         best.TW = TW;
         best.grid = grid;
-        best.iters = (ntiles + grid * TW - 1) / (grid * TW);
         best.lds = lds;
       }
     }
@@ -1536,25 +1588,47 @@ bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
   return true;
 }
 
-template <int FMT, int NB>
-hipError_t launch_mfma2(const GemvArgs& a, const MfmaPlan& p, hipStream_t st) {
+// n GEMVs of one format, K and batch on the matrix cores with plan p (made
+// for their tiles together; one entry for qgemv_run).
+template <int FMT, int NB, int N>
+hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
+  MfmaTable<N> tab{};
+  tab.n = n;
+  tab.KS = p.KS;
+  int u = 0;
+  for (int i = 0; i < n; ++i) {
+    const int tiles = (a[i].M + 15) / 16;
+    tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
+                         a[i].M, a[i].K, u, 0};
+    u += (tiles + p.TW - 1) / p.TW;
+  }
+  tab.units = u;
+  const int grid = std::max(1, std::min(p.grid, u));
   if (p.lds > 64 * 1024) {
     static const hipError_t once = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB>),
+        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
     if (once != hipSuccess) return once;
   }
-  gemv_mfma_kernel<FMT, NB><<<p.grid, 64 * p.KS * p.TW, p.lds, st>>>(
-      static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, a.batch, p.KS, p.iters);
+  gemv_mfma_kernel<FMT, NB, N><<<grid, 64 * p.KS * p.TW, p.lds, st>>>(tab, a[0].batch);
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_mfma(const GemvArgs& a, const MfmaPlan& p, hipStream_t st) {
-  if (round_batch(a.batch) == 4) return launch_mfma2<FMT, 4>(a, p, st);
-  return launch_mfma2<FMT, 8>(a, p, st);
+template <int FMT, int N>
+hipError_t launch_mfma(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
+  if (round_batch(a[0].batch) == 4) return launch_mfma_table<FMT, 4, N>(a, n, p, st);
+  return launch_mfma_table<FMT, 8, N>(a, n, p, st);
 }
 
+template <int N>
+hipError_t launch_mfma_fmt(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
+  switch (a[0].fmt) {
+    case QGEMV_BF16: return launch_mfma<QGEMV_BF16, N>(a, n, p, st);
+    case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32, N>(a, n, p, st);
+    case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32, N>(a, n, p, st);
+    default: return launch_mfma<QGEMV_INT4_G128, N>(a, n, p, st);
+  }
+}
 }  // namespace
 
 FmtInfo fmt_info(int fmt) {
@@ -1599,14 +1673,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     }
   }
   MfmaPlan plan;
-  if (plan_mfma(a.fmt, a.M, a.K, a.batch, cus, &plan)) {
-    switch (a.fmt) {
-      case QGEMV_BF16: return launch_mfma<QGEMV_BF16>(a, plan, stream);
-      case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32>(a, plan, stream);
-      case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32>(a, plan, stream);
-      default: return launch_mfma<QGEMV_INT4_G128>(a, plan, stream);
-    }
-  }
+  if (plan_mfma(a.fmt, a.M, a.K, a.batch, cus, &plan)) return launch_mfma_fmt<1>(&a, 1, plan, stream);
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
@@ -1643,6 +1710,21 @@ int gemv_group_class(int fmt, int K, int batch) {
 }
 
 int gemv_group_max() { return kGroupMax; }
+
+bool gemv_mfma_groupable(int fmt, int K, int batch) {
+  MfmaPlan p;
+  return plan_mfma(fmt, 16, K, batch, device_cu_count(), &p);
+}
+
+hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream) {
+  long rows = 0;
+  for (int i = 0; i < n; ++i) rows += static_cast<long>((a[i].M + 15) / 16) * 16;
+  MfmaPlan plan;
+  if (!plan_mfma(a[0].fmt, static_cast<int>(std::min<long>(rows, 1L << 30)), a[0].K, a[0].batch,
+                 device_cu_count(), &plan))
+    return hipErrorInvalidValue;                   // the caller checked gemv_mfma_groupable
+  return launch_mfma_fmt<kGroupMax>(a, n, plan, stream);
+}
 
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,
                              int32_t* idx) {

@@ -263,21 +263,31 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
                      uint64_t* slots, int32_t* idx, bool* fused) {
   // GEMVs the register-x kernel takes are launched together, one launch per
   // format (up to gemv_group_max() entries) in order of first appearance;
+  // so are those the matrix-core kernel takes, one launch per format and K;
   // the others are launched one by one.
   std::vector<qgemv::GemvArgs> todo;
   std::vector<int> ids;
   std::vector<char> done(static_cast<size_t>(n), 0);
   if (fused) *fused = false;
+  // kind of launch an entry goes to: 1 register-x group (by format),
+  // 2 matrix-core group (by format and K), 0 alone
+  std::vector<int> kind(static_cast<size_t>(n));
+  for (int i = 0; i < n; ++i) {
+    const qgemv_gemv_desc& h = gemvs[i];
+    kind[i] = qgemv::gemv_group_class(h.fmt, h.K, batch) != 0 ? 1
+              : qgemv::gemv_mfma_groupable(h.fmt, h.K, batch) ? 2 : 0;
+  }
   for (int i = 0; i < n; ++i) {
     if (done[i]) continue;
     const qgemv_gemv_desc& g = gemvs[i];
-    const int cls = qgemv::gemv_group_class(g.fmt, g.K, batch);
+    const int cls = kind[i];
     todo.clear();
     ids.clear();
     for (int k = i; k < n; ++k) {
       const qgemv_gemv_desc& h = gemvs[k];
       if (done[k]) continue;
-      if (cls == 0 ? k != i : (h.fmt != g.fmt || qgemv::gemv_group_class(h.fmt, h.K, batch) == 0))
+      if (cls == 0 ? k != i
+                   : (h.fmt != g.fmt || kind[k] != cls || (cls == 2 && h.K != g.K)))
         continue;
       todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
       ids.push_back(k);
@@ -289,6 +299,8 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
       hipError_t e;
       if (cls == 0) {
         e = qgemv::launch_gemv(todo[off], s);
+      } else if (cls == 2) {
+        e = qgemv::launch_gemv_mfma_group(&todo[off], cnt, s);
       } else {
         int local_am = -1;
         for (int t = 0; t < cnt; ++t)

@@ -57,6 +57,13 @@ int gemv_group_max();
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am = -1,
                              uint64_t* slots = nullptr, int32_t* idx = nullptr);
 
+// Grouped launches on the matrix cores (batch 3..8): whether qgemv_run runs
+// a GEMV of this (fmt, K, batch) on the matrix-core kernel; GEMVs of one
+// format, K and batch for which it does can share a launch
+// (n <= gemv_group_max(), already validated).
+bool gemv_mfma_groupable(int fmt, int K, int batch);
+hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream);
+
 // Launch the argmax (one kernel). ws: batch * 2 u64 words, zero on entry.
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                          hipStream_t stream);

@@ -156,9 +156,11 @@ typedef struct {
  * mixture-of-experts layer are another).
  * Entries of one format that the small-batch kernel handles (batch <= 2 and
  * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit)
- * share launches (one per format, up to 64 entries each), so the
- * per-launch start-up cost is paid once per format instead of once per
- * GEMV; other entries are launched one by one. All validation
+ * share launches (one per format, up to 64 entries each), and so do entries
+ * of one format and K that the matrix-core kernel handles (batch 3..8, K a
+ * multiple of 256 for Q4_0, 128 for int8 and bf16, 512 for int4-g128, x in
+ * LDS), so the per-launch start-up cost is paid once per group instead of
+ * once per GEMV; other entries are launched one by one. All validation
  * happens before anything is launched. Errors as qgemv_run; ESHAPE also
  * for n > QGEMV_GROUP_MAX.
  */

@@ -308,7 +308,8 @@ def _grouped(gemvs, B):
     return [it[4].cpu().numpy() for it in dev_items]
 
 
-@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (3, 1), (5, 1), (5, 2), (1, 2)])
+@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (3, 1), (5, 1), (5, 2), (1, 2),
+                                   (2, 4), (2, 8), (3, 4), (5, 8), (1, 8)])
 def test_grouped_workload_parity(cfg, B):
     gemvs = [synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
              for sp in synth.workload_specs(cfg)]
@@ -318,9 +319,10 @@ def test_grouped_workload_parity(cfg, B):
         assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"grouped {g.name}")
 
 
-def test_grouped_decode_step_stream_89_gemvs():
-    """All 89 GEMVs of the TinyLlama decode-step stream in one call (B=1): 64 sampled rows each."""
-    B = 1
+@pytest.mark.parametrize("B", [1, 8])
+def test_grouped_decode_step_stream_89_gemvs(B):
+    """All 89 GEMVs of the TinyLlama decode-step stream in one call: 64 sampled rows each
+    (B=1: one register-x launch; B=8: matrix-core launches by K, 64 entries at most)."""
     gemvs = synth.make_workload(4, B)
     ys = _grouped(gemvs, B)
     rng = np.random.default_rng(5)
@@ -330,10 +332,11 @@ def test_grouped_decode_step_stream_89_gemvs():
         assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=rows, what=f"grouped {g.name}")
 
 
-@pytest.mark.parametrize("B", [1, 2, 3])
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
 def test_grouped_mixed_formats_ragged_and_fallback(B):
-    """Formats and row lengths mixed in one call, ragged M, entries the grouped kernel
-    does not take (int8 K=8192, and every entry at B=3) launched one by one."""
+    """Formats and row lengths mixed in one call, ragged M, entries no grouped kernel
+    takes launched one by one (int8 K=8192 at B <= 2; K not a multiple of the
+    matrix-core step at B >= 3)."""
     shapes = [(synth.Q4_0_G32, 1, 2048), (synth.BF16, 65, 256), (synth.INT8_G32, 1000, 2048),
               (synth.Q4_0_G32, 63, 5632), (synth.INT4_G128, 300, 8192), (synth.INT8_G32, 70, 8192),
               (synth.Q4_0_G32, 4097, 2048), (synth.BF16, 7, 2048), (synth.INT4_G128, 129, 384),
