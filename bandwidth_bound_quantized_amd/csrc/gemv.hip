@@ -73,6 +73,12 @@
 #ifndef QGEMV_MFMA_MAX_WAVES_PER_CU
 #define QGEMV_MFMA_MAX_WAVES_PER_CU 16     // ... and the most that fit (register budget)
 #endif
+#ifndef QGEMV_MFMA_COPY_BEFORE_SWAP
+#define QGEMV_MFMA_COPY_BEFORE_SWAP 0      // see mfma_units (compute)
+#endif
+#ifndef QGEMV_MFMA_SCALE_SHFL
+#define QGEMV_MFMA_SCALE_SHFL 1            // see mfma_units (scale loads)
+#endif
 #ifndef QGEMV_MFMA_FORCE_KS
 #define QGEMV_MFMA_FORCE_KS 0              // nonzero: fixed K split (if it divides the steps)
 #endif
@@ -1157,36 +1163,53 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
 
   const uint32_t woff = i * row_bytes + 16 * q;
   const uint32_t soff = i * ngroups * 2;
+  // Scales: lane l loads dword l % kSW of row l / kSW of the step's
+  // 16 x kSW-dword block (one coalesced load), and the lanes of a row fetch
+  // their dwords from those lanes (ds_bpermute). Loading each row's dwords in
+  // every lane of the row instead repeats every address 4 times across the
+  // wave, which measured 20 % slower on the int8 LM head.
+  constexpr bool kScaleShfl = QGEMV_MFMA_SCALE_SHFL && F::kGroups > 0 && kSW <= 4;
+  const uint32_t soff_lin = lane < 16 * kSW ? (lane / kSW) * ngroups * 2 + 4 * (lane % kSW) : 0x80000000u;
+  constexpr int kSR = kScaleShfl ? 1 : kSW;            // scale registers per buffer
 
   u32x4 wa[F::kSlices], wb[F::kSlices];
-  uint32_t sa[kSW], sb[kSW];
+  uint32_t sa[kSR], sb[kSR];
 
   // loads of step s (of this wave's range) of the tile of unit g0 + n;
   // rows past M, and units past g1, read as zero
-  auto load = [&](u32x4 (&w)[F::kSlices], uint32_t (&s)[kSW], int n, int st_local) {
-    const int tile = (g0 + n) * TW + tg;
-    const int row0 = tile * 16;
-    // (written as a select and a min: a clamp would be selected as a vector
-    // med3, and a buffer resource built from a vector register is looped
-    // over lanes)
-    const int rows = (n < iters && row0 < M) ? min(16, M - row0) : 0;
+  // buffer resources of the tile of unit g0 + rn (recomputed when the tile changes)
+  int rn = -1;
+  __amdgpu_buffer_rsrc_t rw = make_rsrc(W, 0), rs = make_rsrc(S, 0);
+  auto load = [&](u32x4 (&w)[F::kSlices], uint32_t (&s)[kSR], int n, int st_local) {
+    if (n != rn) {
+      rn = n;
+      const int tile = (g0 + n) * TW + tg;
+      const int row0 = tile * 16;
+      // (written as a select and a min: a clamp would be selected as a
+      // vector med3, and a buffer resource built from a vector register is
+      // looped over lanes)
+      const int rows = (n < iters && row0 < M) ? min(16, M - row0) : 0;
+      rw = make_rsrc(W + (rows ? static_cast<size_t>(row0) * row_bytes : 0), static_cast<uint32_t>(rows) * row_bytes);
+      if constexpr (F::kGroups > 0)
+        rs = make_rsrc(S + (rows ? static_cast<size_t>(row0) * ngroups : 0), static_cast<uint32_t>(rows * ngroups * 2));
+    }
     const int st = ks * Lw + st_local;
     // The lane's offset (row i, byte 16q) is the VGPR offset, which the
     // range check covers: rows past M read as zero. The step's offset along
     // the row is the SGPR offset (not range checked, always inside the row),
     // so no vector register is computed here.
-    const uint8_t* base = W + (rows ? static_cast<size_t>(row0) * row_bytes : 0);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(base, static_cast<uint32_t>(rows) * row_bytes);
     const int so = st * (F::kSlices * 64);
 #pragma unroll
     for (int l = 0; l < F::kSlices; ++l)
       w[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 64 * l, so, kWeightAux));
     if constexpr (F::kGroups > 0) {
-      const uint16_t* sbase = S + (rows ? static_cast<size_t>(row0) * ngroups : 0);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, static_cast<uint32_t>(rows * ngroups * 2));
       const int sso = st * (F::kGroups * 2);
       static_assert(kSW == 2 || kSW % 4 == 0, "scale dwords per step");
-      if constexpr (kSW % 4 == 0) {
+      if constexpr (kScaleShfl) {
+        // one dword per lane, consecutive lanes on consecutive addresses;
+        // lanes past the tile's 16 x kSW dwords read out of range (zero)
+        s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff_lin, sso, 0);
+      } else if constexpr (kSW % 4 == 0) {
 #pragma unroll
         for (int u = 0; u < kSW / 4; ++u) {
           const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * u, sso, 0));
@@ -1200,22 +1223,35 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
   };
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const u32x4 (&w)[F::kSlices], const uint32_t (&s)[kSW], int st_local,
+  // per step: one D tile per scale group (all of them issued before any is scaled)
+  constexpr int kDch = FMT == QGEMV_BF16 ? 1 : F::kGroups;
+  auto compute = [&](const u32x4 (&w)[F::kSlices], const uint32_t (&sr)[kSR], int st_local,
                      f32x4& acc, f32x4& bacc) {
     const int st = ks * Lw + st_local;
     const int c0 = st * kChunks;
+    f32x4 dch[kDch];
+    uint32_t s[kSW];
+    if constexpr (kScaleShfl) {
+#pragma unroll
+      for (int k = 0; k < kSW; ++k) s[k] = __shfl(sr[0], i * kSW + k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSW; ++k) s[k] = sr[k];
+    }
 #pragma unroll
     for (int l = 0; l < F::kSlices; ++l) {
       uint32_t r[4] = {w[l].x, w[l].y, w[l].z, w[l].w};
+#if QGEMV_MFMA_COPY_BEFORE_SWAP
       if constexpr (FMT != QGEMV_BF16) {
         // The swaps below overwrite both of their registers. Swapping copies
         // leaves the loaded registers untouched, so they stay where the next
         // prefetch into this buffer puts them (otherwise the register
-        // allocator rotates them and has to copy in-flight load results,
+        // allocator may rotate them and have to copy in-flight load results,
         // which waits for the prefetch).
 #pragma unroll
         for (int k = 0; k < 4; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(r[k]) : "v"(r[k]));
       }
+#endif
       if constexpr (FMT == QGEMV_INT8_G32) {
         swap32(r[0], r[2]);
         swap32(r[1], r[3]);
@@ -1234,23 +1270,24 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
         if constexpr (FMT == QGEMV_BF16) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, w[l]), acc, 0, 0, 0);
         } else if constexpr (FMT == QGEMV_INT8_G32) {
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), zero, 0, 0, 0);
-          const float sc = scale_of(s, l * kCPS + ch);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, d[j], acc[j]);
+          dch[l * kCPS + ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), zero, 0, 0, 0);
         } else if constexpr (FMT == QGEMV_Q4_0_G32) {
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), zero, 0, 0, 0);
-          const float sc = scale_of(s, l * kCPS + ch);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, d[j], acc[j]);
+          dch[l * kCPS + ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), zero, 0, 0, 0);
         } else {
           dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), dg, 0, 0, 0);
         }
       }
-      if constexpr (FMT == QGEMV_INT4_G128) {
-        const float sc = scale_of(s, l);
+      if constexpr (FMT == QGEMV_INT4_G128) dch[l] = dg;
+    }
+    // group scales, applied after all of the step's matrix instructions are
+    // issued (each scale FMA waits for its MFMA's result; interleaving them
+    // stalls on every chunk)
+    if constexpr (FMT != QGEMV_BF16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, dg[j], acc[j]);
+      for (int g = 0; g < kDch; ++g) {
+        const float sc = scale_of(s, g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, dch[g][j], acc[j]);
       }
     }
     if constexpr (kBiasSums) {
