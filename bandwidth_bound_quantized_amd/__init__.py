@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_packed_size": (c_int, [c_int, c_i64, c_i64, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]),
         "qgemv_pack": (c_int, [c_int, c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
         "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
+        "qgemv_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
         "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
@@ -71,7 +72,7 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_run", "qgemv_run_grouped",
+EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_grouped",
            "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
@@ -115,6 +116,20 @@ def pack(fmt: int, src_kind: int, src_w: np.ndarray, src_scales: Optional[np.nda
 
 
 # ---------------------------------------------------------------- device side
+def quantize(fmt: int, w, M: int, K: int, codes, scales, err=None, stream=None) -> None:
+    """Device quantizer (qgemv_quantize): w bf16 bits [M][K] (int16/uint16/bfloat16), codes
+    (uint8, packed_size's w_bytes), scales (int16/uint16, s_bytes / 2), err (int32 [1]) or None."""
+    import torch
+    wp = _dev_ptr(w, "w", (torch.int16, torch.uint16, torch.bfloat16))
+    cp = _dev_ptr(codes, "codes")
+    sp = _dev_ptr(scales, "scales", (torch.int16, torch.uint16))
+    ep = _dev_ptr(err, "err", torch.int32) if err is not None else None
+    wb, sb = packed_size(fmt, M, K)
+    if w.numel() < M * K or codes.numel() * codes.element_size() < wb or scales.numel() * 2 < sb:
+        raise ValueError("w, codes or scales too small for (fmt, M, K)")
+    _check(_lib.qgemv_quantize(fmt, wp, M, K, cp, sp, ep, _stream_handle(stream)), "qgemv_quantize")
+
+
 def _stream_handle(stream) -> Optional[int]:
     import torch
     if stream is None:

@@ -245,6 +245,17 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
   return QGEMV_OK;
 }
 
+int qgemv_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
+                   int32_t* err, void* stream) {
+  if (fmt != QGEMV_INT8_G32 && fmt != QGEMV_Q4_0_G32 && fmt != QGEMV_INT4_G128) return QGEMV_EINVAL;
+  if (!w || !codes || !scales) return QGEMV_EINVAL;
+  const int st = check_shape(fmt, M, K);
+  if (st) return st;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || (err && !aligned(err, 4)))
+    return QGEMV_EALIGN;
+  return record_hip(qgemv::launch_quantize(fmt, w, M, K, codes, scales, err, static_cast<hipStream_t>(stream)));
+}
+
 int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
               int64_t M, int64_t K, int batch, void* stream) {
   const int st = check_run_args(fmt, W, scales, x, y, M, K, batch);

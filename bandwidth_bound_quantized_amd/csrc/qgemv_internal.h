@@ -68,6 +68,10 @@ hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream);
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                          hipStream_t stream);
 
+// Quantizer (bf16 -> codes + scales) on the device; err may be null.
+hipError_t launch_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
+                           int32_t* err, hipStream_t stream);
+
 // Streaming-read measurement kernel.
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
                               hipStream_t stream);

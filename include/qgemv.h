@@ -114,6 +114,24 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
                int64_t M, int64_t K, void* dst_w, uint16_t* dst_scales);
 
 /*
+ * qgemv_quantize - the quantizer of qgemv_pack (src_kind BF16) on the
+ * device: bf16 weights w [M][K] -> codes and binary16 scales in the layout
+ * above, bit-identical to what qgemv_pack writes for the same weights (the
+ * rule and its readings as documented there: the Rust page, "Is the 4-bit
+ * model still good?"; "infer", design notes and its quantizer tests).
+ * fmt: INT8_G32, Q4_0_G32 or INT4_G128 (EINVAL for BF16). Device pointers:
+ * w 16-byte aligned; codes (qgemv_packed_size's w_bytes) 16-byte aligned;
+ * scales (s_bytes) 4-byte aligned; err: a device int32 or NULL. A group
+ * with a non-finite weight or a scale past binary16's range stores
+ * unspecified codes and scale and sets *err = QGEMV_ERANGE (err is never
+ * cleared: zero it before the call and read it after synchronizing).
+ * Asynchronous on `stream`; one kernel, one thread per group.
+ * Errors (returned): EINVAL, ESHAPE, EALIGN, EHIP.
+ */
+int qgemv_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
+                   int32_t* err, void* stream);
+
+/*
  * qgemv_run - y[b][m] = sum_k weight(m,k) * x[b][k], 0 <= b < batch.
  * Device pointers. W / scales in the layout above (scales may be NULL for
  * bf16); x: bf16 [batch][K]; y: float32 [batch][M], overwritten (not

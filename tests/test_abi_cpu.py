@@ -254,3 +254,19 @@ def test_grouped_argmax_validation_errors_before_any_launch():
     assert f(a, 2, 1, 1, ws, idx + 2, None) == qg.EALIGN
     arr[1].K = 40                                              # a bad GEMV still fails first
     assert f(a, 2, 1, 1, ws, idx, None) == qg.ESHAPE
+
+
+def test_quantize_validation_errors_before_any_launch():
+    f = qg.lib().qgemv_quantize
+    assert f(qg.BF16, FAKE, 4, 64, FAKE, FAKE, None, None) == qg.EINVAL
+    assert f(7, FAKE, 4, 64, FAKE, FAKE, None, None) == qg.EINVAL
+    assert f(qg.Q4_0_G32, None, 4, 64, FAKE, FAKE, None, None) == qg.EINVAL
+    assert f(qg.Q4_0_G32, FAKE, 4, 64, None, FAKE, None, None) == qg.EINVAL
+    assert f(qg.Q4_0_G32, FAKE, 4, 64, FAKE, None, None, None) == qg.EINVAL
+    assert f(qg.Q4_0_G32, FAKE, 0, 64, FAKE, FAKE, None, None) == qg.ESHAPE
+    assert f(qg.Q4_0_G32, FAKE, 4, 48, FAKE, FAKE, None, None) == qg.ESHAPE
+    assert f(qg.INT4_G128, FAKE, 4, 64, FAKE, FAKE, None, None) == qg.ESHAPE
+    assert f(qg.Q4_0_G32, FAKE + 8, 4, 64, FAKE, FAKE, None, None) == qg.EALIGN
+    assert f(qg.Q4_0_G32, FAKE, 4, 64, FAKE + 4, FAKE, None, None) == qg.EALIGN
+    assert f(qg.Q4_0_G32, FAKE, 4, 64, FAKE, FAKE + 2, None, None) == qg.EALIGN
+    assert f(qg.Q4_0_G32, FAKE, 4, 64, FAKE, FAKE, FAKE + 2, None) == qg.EALIGN

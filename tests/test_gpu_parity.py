@@ -469,3 +469,78 @@ def test_grouped_argmax_nan_logit_and_workspace_reuse():
         if rows:
             assert (idx == min(rows)).all()
         assert (ws.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------ device quantizer
+def gpu_quantize(fmt, w, M, K):
+    wb, sb = qg.packed_size(fmt, M, K)
+    Wd = dev(np.ascontiguousarray(w))
+    C = torch.zeros(wb, dtype=torch.uint8, device=DEV)
+    S = torch.zeros(sb // 2, dtype=torch.int16, device=DEV)
+    E = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print(f"[gpu] qgemv_quantize fmt={qg.FMT_NAMES[fmt]} M={M} K={K}", flush=True)
+    qg.quantize(fmt, Wd, M, K, C, S, E)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), S.cpu().numpy().view(np.uint16), int(E.cpu().numpy()[0])
+
+
+def _quant_edge_inputs():
+    rng = np.random.default_rng(99)
+    w = synth.bf16_normal(rng, (64, 512), 0.02)
+    w[0, :128] = 0
+    w[1, :32] = synth.round_f32_to_bf16_bits(np.zeros(32, np.float32))
+    w[1, 32:64] = 0x8000                                     # all -0.0
+    t = np.zeros(32, np.float32); t[3] = -0.5; t[9] = 0.5
+    w[2, :32] = synth.round_f32_to_bf16_bits(t)              # |w| tie: the first (negative) wins
+    w[2, 32:64] = synth.round_f32_to_bf16_bits(-t)
+    w[3, 32:64] = synth.round_f32_to_bf16_bits(np.linspace(-0.3, 0.75, 32).astype(np.float32))
+    w[4, :32] = synth.round_f32_to_bf16_bits(np.full(32, 1e-9, np.float32))           # scale rounds to 0
+    w[5, :32] = synth.round_f32_to_bf16_bits(np.linspace(-3e-5, 2e-5, 32).astype(np.float32))  # subnormal d
+    w[6, :128] = synth.round_f32_to_bf16_bits(np.linspace(-500000, 400000, 128).astype(np.float32))
+    w[7, :64] = synth.round_f32_to_bf16_bits(np.arange(64).astype(np.float32) * 0.0625 - 2.0)  # exact halves
+    w[8, :128] = synth.round_f32_to_bf16_bits((np.arange(128) - 64).astype(np.float32) * 2.5)  # rint ties
+    return w
+
+
+@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128], ids=["int8", "q4_0", "int4"])
+def test_device_quantizer_bit_exact(fmt):
+    """qgemv_quantize against the oracle quantizer (and so against qgemv_pack, which the CPU
+    tests hold bit-exact to it) on edge groups and on the 2048x2048 workload shape."""
+    for w in (_quant_edge_inputs(), synth.bf16_normal(np.random.default_rng(fmt + 1000), (2048, 2048), 0.02)):
+        M, K = w.shape
+        codes, scales, err = gpu_quantize(fmt, w, M, K)
+        o_codes, o_scales = oracle.quantize_from_bf16(fmt, w, M, K)
+        assert err == 0
+        assert (scales == o_scales.reshape(-1)).all()
+        assert (codes == o_codes.reshape(-1).view(np.uint8)).all()
+
+
+def test_device_quantizer_range_errors_flagged():
+    w = synth.bf16_normal(np.random.default_rng(5), (4, 128), 0.02)
+    _, _, err = gpu_quantize(qg.Q4_0_G32, w, 4, 128)
+    assert err == 0
+    bad = w.copy(); bad[2, 70] = 0x7F80                          # +inf
+    _, _, err = gpu_quantize(qg.Q4_0_G32, bad, 4, 128)
+    assert err == qg.ERANGE
+    bad = w.copy(); bad[1, 5] = 0x7FC1                           # NaN
+    _, _, err = gpu_quantize(qg.INT4_G128, bad, 4, 128)
+    assert err == qg.ERANGE
+    big = synth.round_f32_to_bf16_bits(np.full((1, 32), 1e7, np.float32))   # scale > 65504
+    _, _, err = gpu_quantize(qg.INT8_G32, big, 1, 32)
+    assert err == qg.ERANGE
+
+
+def test_device_quantizer_then_run():
+    """Quantize on the device, run the GEMV on those codes: within tolerance of the oracle
+    run on the oracle's codes (batch 1 and 8)."""
+    rng = np.random.default_rng(17)
+    M, K = 1024, 2048
+    wbf = synth.bf16_normal(rng, (M, K), 0.02)
+    for fmt in (qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128):
+        codes, scales, err = gpu_quantize(fmt, wbf, M, K)
+        assert err == 0
+        for B in (1, 8):
+            x = synth.bf16_normal(rng, (B, K), 1.0)
+            y = gpu_gemv(fmt, codes, scales, x, M, K, B)
+            o_codes, o_scales = oracle.quantize_from_bf16(fmt, wbf, M, K)
+            assert_parity(fmt, o_codes, o_scales, x, M, K, B, y)
