@@ -25,6 +25,7 @@ BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
 SRC_CANONICAL, SRC_BF16 = 0, 1
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
 MAX_BATCH = 8
+FLAG_BATCH_INVARIANT = 1
 ARGMAX_WS_WORDS_PER_ROW = 2
 FUSED_ARGMAX_WS_WORDS_PER_ROW = 4096
 GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
@@ -56,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_pack": (c_int, [c_int, c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
         "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
         "qgemv_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+        "qgemv_run_flags": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp]),
         "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
@@ -72,7 +74,8 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_grouped",
+EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_flags",
+           "qgemv_run_grouped",
            "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
@@ -164,6 +167,19 @@ def run(fmt: int, W, scales, x, y, M: int, K: int, batch: int, stream=None) -> N
         raise ValueError("x or y too small for (batch, M, K)")
     st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, _stream_handle(stream))
     _check(st, "qgemv_run")
+
+
+def run_flags(fmt: int, W, scales, x, y, M: int, K: int, batch: int, flags: int, stream=None) -> None:
+    """run() with qgemv_run_flags options (FLAG_BATCH_INVARIANT)."""
+    import torch
+    wp = _dev_ptr(W, "W")
+    sp = _dev_ptr(scales, "scales") if scales is not None else None
+    xp = _dev_ptr(x, "x", (torch.int16, torch.uint16, torch.bfloat16))
+    yp = _dev_ptr(y, "y", torch.float32)
+    if y.numel() < batch * M or x.numel() < batch * K:
+        raise ValueError("x or y too small for (batch, M, K)")
+    _check(_lib.qgemv_run_flags(fmt, wp, sp, xp, yp, M, K, batch, flags, _stream_handle(stream)),
+           "qgemv_run_flags")
 
 
 def run_ptr(fmt: int, wp: int, sp: Optional[int], xp: int, yp: int, M: int, K: int, batch: int,

@@ -1452,8 +1452,8 @@ hipError_t launch_fr(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t
 }
 
 template <int FMT>
-hipError_t launch_f(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t st) {
-  switch (round_batch(a.batch)) {
+hipError_t launch_f(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t st, int nb) {
+  switch (nb) {
     case 1: return launch_fr<FMT, 1>(a, R, grid, lds, st);
     case 2: return launch_fr<FMT, 2>(a, R, grid, lds, st);
     case 4: return launch_fr<FMT, 4>(a, R, grid, lds, st);
@@ -1651,19 +1651,20 @@ hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStr
   return hipGetLastError();
 }
 
+// nb: batch rows the kernel is compiled for (4 or 8; >= batch)
 template <int FMT, int N>
-hipError_t launch_mfma(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
-  if (round_batch(a[0].batch) == 4) return launch_mfma_table<FMT, 4, N>(a, n, p, st);
+hipError_t launch_mfma(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st, int nb) {
+  if (nb == 4) return launch_mfma_table<FMT, 4, N>(a, n, p, st);
   return launch_mfma_table<FMT, 8, N>(a, n, p, st);
 }
 
 template <int N>
-hipError_t launch_mfma_fmt(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
+hipError_t launch_mfma_fmt(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st, int nb) {
   switch (a[0].fmt) {
-    case QGEMV_BF16: return launch_mfma<QGEMV_BF16, N>(a, n, p, st);
-    case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32, N>(a, n, p, st);
-    case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32, N>(a, n, p, st);
-    default: return launch_mfma<QGEMV_INT4_G128, N>(a, n, p, st);
+    case QGEMV_BF16: return launch_mfma<QGEMV_BF16, N>(a, n, p, st, nb);
+    case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32, N>(a, n, p, st, nb);
+    case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32, N>(a, n, p, st, nb);
+    default: return launch_mfma<QGEMV_INT4_G128, N>(a, n, p, st, nb);
   }
 }
 }  // namespace
@@ -1678,7 +1679,7 @@ FmtInfo fmt_info(int fmt) {
 }
 
 size_t gemv_lds_bytes(int fmt, int K, int batch) {
-  const int nb = round_batch(batch);
+  const int nb = round_batch(batch);             // (batch 8 for the invariant mode's size)
   size_t bytes = static_cast<size_t>(nb) * K * 2;
   if (fmt == QGEMV_Q4_0_G32 || fmt == QGEMV_INT4_G128) bytes += static_cast<size_t>(nb) * (K / 32) * 4;
   return bytes;
@@ -1690,11 +1691,17 @@ bool gemv_uses_lds(int fmt, int K, int batch) {
   return !(round_batch(batch) <= 2 && nch <= 4);
 }
 
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
   const int cus = device_cu_count();
   const int U = a.K / fmt_info(a.fmt).elems_per_unit;
   const int nch = (U + 63) / 64;
-  if (!gemv_uses_lds(a.fmt, a.K, a.batch)) {
+  // batch invariance: every batch runs the kernels compiled for 8 batch rows
+  // with launch shapes chosen from (fmt, M, K) alone, so a row's arithmetic
+  // is the same at every batch (the register-x kernel is never used: its
+  // reduction tree depends on the batch)
+  const bool inv = (flags & QGEMV_FLAG_BATCH_INVARIANT) != 0;
+  const int nb = inv ? 8 : round_batch(a.batch);
+  if (!inv && !gemv_uses_lds(a.fmt, a.K, a.batch)) {
     // rows per step: up to 8 / NCH units in flight per lane, while keeping
     // at least two workgroups per CU
     int R = std::min(QGEMV_XREG_MAX_R, nch == 1 ? 4 : nch == 2 ? 4 : 2);
@@ -1710,8 +1717,8 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     }
   }
   MfmaPlan plan;
-  if (plan_mfma(a.fmt, a.M, a.K, a.batch, cus, &plan)) return launch_mfma_fmt<1>(&a, 1, plan, stream);
-  const size_t lds = gemv_lds_bytes(a.fmt, a.K, a.batch);
+  if (plan_mfma(a.fmt, a.M, a.K, inv ? 8 : a.batch, cus, &plan)) return launch_mfma_fmt<1>(&a, 1, plan, stream, nb);
+  const size_t lds = gemv_lds_bytes(a.fmt, a.K, nb);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
   while (R > 1 && (a.M + R - 1) / R < QGEMV_MIN_WAVES_PER_CU * cus) R >>= 1;
@@ -1733,10 +1740,10 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     (void)once;
   }
   switch (a.fmt) {
-    case QGEMV_BF16: return launch_f<QGEMV_BF16>(a, R, grid, lds, stream);
-    case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream);
-    case QGEMV_Q4_0_G32: return launch_f<QGEMV_Q4_0_G32>(a, R, grid, lds, stream);
-    default: return launch_f<QGEMV_INT4_G128>(a, R, grid, lds, stream);
+    case QGEMV_BF16: return launch_f<QGEMV_BF16>(a, R, grid, lds, stream, nb);
+    case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream, nb);
+    case QGEMV_Q4_0_G32: return launch_f<QGEMV_Q4_0_G32>(a, R, grid, lds, stream, nb);
+    default: return launch_f<QGEMV_INT4_G128>(a, R, grid, lds, stream, nb);
   }
 }
 
@@ -1760,7 +1767,7 @@ hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream) 
   if (!plan_mfma(a[0].fmt, static_cast<int>(std::min<long>(rows, 1L << 30)), a[0].K, a[0].batch,
                  device_cu_count(), &plan))
     return hipErrorInvalidValue;                   // the caller checked gemv_mfma_groupable
-  return launch_mfma_fmt<kGroupMax>(a, n, plan, stream);
+  return launch_mfma_fmt<kGroupMax>(a, n, plan, stream, round_batch(a[0].batch));
 }
 
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,

@@ -264,6 +264,18 @@ int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x,
   return record_hip(qgemv::launch_gemv(a, static_cast<hipStream_t>(stream)));
 }
 
+int qgemv_run_flags(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+                    int64_t M, int64_t K, int batch, int flags, void* stream) {
+  if (flags & ~QGEMV_FLAG_BATCH_INVARIANT) return QGEMV_EINVAL;
+  int st = check_run_args(fmt, W, scales, x, y, M, K, batch);
+  if (st) return st;
+  // the invariant mode runs every batch as 8 rows: x of 8 rows must fit in LDS
+  if ((flags & QGEMV_FLAG_BATCH_INVARIANT) && qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), 8) > 160 * 1024)
+    return QGEMV_ESHAPE;
+  qgemv::GemvArgs a{fmt, W, scales, x, y, static_cast<int>(M), static_cast<int>(K), batch};
+  return record_hip(qgemv::launch_gemv(a, static_cast<hipStream_t>(stream), flags));
+}
+
 
 namespace {
 

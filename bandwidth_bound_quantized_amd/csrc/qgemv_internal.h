@@ -41,8 +41,9 @@ size_t gemv_lds_bytes(int fmt, int K, int batch);
 // otherwise each lane keeps its share of x in registers and no LDS is used.
 bool gemv_uses_lds(int fmt, int K, int batch);
 
-// Launch the GEMV on `stream`. Shapes have been validated by the caller.
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+// Launch the GEMV on `stream` (flags: QGEMV_FLAG_*). Shapes have been
+// validated by the caller.
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags = 0);
 
 // Grouped launches of independent GEMVs (register-x kernel only).
 // gemv_group_class: 0 if (fmt, K, batch) needs another kernel, else the number

@@ -148,6 +148,24 @@ int qgemv_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes
 int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
               int64_t M, int64_t K, int batch, void* stream);
 
+/* qgemv_run_flags flag: batch-invariant results (see qgemv_run_flags). */
+#define QGEMV_FLAG_BATCH_INVARIANT 1
+
+/*
+ * qgemv_run_flags - qgemv_run with options. QGEMV_FLAG_BATCH_INVARIANT:
+ * row b of y is bit-identical to what a batch-1 call on x[b] alone returns
+ * with the same flag, for every batch 1..8 - the fixed per-row summation
+ * order that lets a batched pass (e.g. speculative verification of several
+ * draft tokens, the Rust page's speculative-decoding section) be checked
+ * against single-token decoding with exact equality. Every batch then runs
+ * the kernels of batch 8 with launch shapes chosen from (fmt, M, K) only,
+ * so it costs the batch-8 time even at batch 1, and x of 8 rows must fit in
+ * LDS (K as for batch 5..8 in qgemv_run, else ESHAPE). flags 0 is qgemv_run.
+ * Errors: as qgemv_run; EINVAL for unknown flag bits.
+ */
+int qgemv_run_flags(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+                    int64_t M, int64_t K, int batch, int flags, void* stream);
+
 /* One GEMV of a grouped call (same meaning and layout rules as qgemv_run). */
 typedef struct {
   const void* W;          /* device: codes (or bf16 weights) */

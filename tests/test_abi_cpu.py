@@ -161,6 +161,21 @@ def _run(fmt=qg.Q4_0_G32, W=FAKE, S=FAKE, x=FAKE, y=FAKE, M=64, K=2048, batch=1)
     return qg.lib().qgemv_run(fmt, W, S, x, y, M, K, batch, None)
 
 
+def _run_flags(flags, fmt=qg.Q4_0_G32, M=64, K=2048, batch=1):
+    return qg.lib().qgemv_run_flags(fmt, FAKE, FAKE, FAKE, FAKE, M, K, batch, flags, None)
+
+
+def test_run_flags_validation_errors_before_any_launch():
+    assert _run_flags(2) == qg.EINVAL                        # unknown flag bit
+    assert _run_flags(-1) == qg.EINVAL
+    assert _run_flags(qg.FLAG_BATCH_INVARIANT, batch=0) == qg.ESHAPE
+    assert _run_flags(qg.FLAG_BATCH_INVARIANT, batch=9) == qg.ESHAPE
+    # the invariant mode stages x as 8 rows at every batch: K that batch 1
+    # takes can be too long for it
+    assert _run_flags(qg.FLAG_BATCH_INVARIANT, fmt=qg.BF16, K=10272, batch=1) == qg.ESHAPE
+    assert _run_flags(qg.FLAG_BATCH_INVARIANT, fmt=qg.Q4_0_G32, K=9664, batch=1) == qg.ESHAPE
+
+
 def test_run_validation_errors_before_any_launch():
     assert _run(fmt=7) == qg.EINVAL
     assert _run(W=None) == qg.EINVAL

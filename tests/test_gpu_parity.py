@@ -544,3 +544,56 @@ def test_device_quantizer_then_run():
             y = gpu_gemv(fmt, codes, scales, x, M, K, B)
             o_codes, o_scales = oracle.quantize_from_bf16(fmt, wbf, M, K)
             assert_parity(fmt, o_codes, o_scales, x, M, K, B, y)
+
+
+# ------------------------------------------------------------ batch invariance
+def gpu_gemv_inv(fmt, Wd, Sd, x, M, K, B):
+    Xd = dev(np.ascontiguousarray(x).reshape(B, K))
+    Yd = torch.full((B, M), float("nan"), dtype=torch.float32, device=DEV)
+    print(f"[gpu] qgemv_run_flags invariant fmt={qg.FMT_NAMES[fmt]} M={M} K={K} B={B}", flush=True)
+    qg.run_flags(fmt, Wd, Sd, Xd, Yd, M, K, B, qg.FLAG_BATCH_INVARIANT)
+    torch.cuda.synchronize()
+    return Yd.cpu().numpy()
+
+
+# Matrix-core shapes (K a multiple of the format's step) and shapes the
+# dot-product kernel takes (short or ragged K), small and large M.
+INV_SHAPES = [(2048, 2048), (4100, 1024), (32000, 2048), (65, 384), (1000, 5632), (7, 9216)]
+
+
+@pytest.mark.parametrize("M,K", INV_SHAPES, ids=[f"{m}x{k}" for m, k in INV_SHAPES])
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128],
+                         ids=["bf16", "int8", "q4_0", "int4"])
+def test_batch_invariant_rows_bitwise_equal(fmt, M, K):
+    """With the batch-invariant flag, row b of a batch-B call equals the
+    batch-1 call on x[b] bit for bit, for B = 8, 5, 3, 2 (and matches the
+    oracle within the usual bound)."""
+    if K % synth.GROUP[fmt]:
+        K = (K // 128 + 1) * 128
+    if 8 * K * 2 + (K if fmt in (qg.Q4_0_G32, qg.INT4_G128) else 0) > 160 * 1024:
+        pytest.skip("x of 8 rows does not fit in LDS")
+    g = synth.make_gemv("t", fmt, M, K, 8, 13, (3 * M + K) % 983, "gate_up")
+    Wd = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+    Sd = dev(g.s.reshape(-1)) if g.s is not None else None
+    x = g.x.reshape(8, K)
+    singles = np.stack([gpu_gemv_inv(fmt, Wd, Sd, x[b:b + 1], M, K, 1)[0] for b in range(8)])
+    assert np.isfinite(singles).all()
+    assert_parity(fmt, g.w, g.s, x, M, K, 8, singles, rows=sample_rows(M), what="singles")
+    for B, rows in ((8, range(8)), (5, (7, 0, 3, 6, 1)), (3, (2, 5, 4)), (2, (6, 6))):
+        xb = x[list(rows)]
+        y = gpu_gemv_inv(fmt, Wd, Sd, xb, M, K, B)
+        want = singles[list(rows)]
+        assert (y.view(np.uint32) == want.view(np.uint32)).all(), f"B={B} rows={rows}"
+
+
+def test_batch_invariant_flag_zero_is_run():
+    """flags 0 is qgemv_run: same bits."""
+    fmt, M, K, B = qg.Q4_0_G32, 2048, 2048, 2
+    g = synth.make_gemv("t", fmt, M, K, B, 13, 5, "gate_up")
+    y_run = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B)
+    Wd = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+    Xd = dev(np.ascontiguousarray(g.x).reshape(B, K))
+    Yd = torch.full((B, M), float("nan"), dtype=torch.float32, device=DEV)
+    qg.run_flags(fmt, Wd, dev(g.s.reshape(-1)), Xd, Yd, M, K, B, 0)
+    torch.cuda.synchronize()
+    assert (Yd.cpu().numpy().view(np.uint32) == y_run.view(np.uint32)).all()
