@@ -19,10 +19,14 @@ Modules
   quantize  the bf16 -> int8-g32 / 4-bit quantizers (largest-magnitude
             value maps to code -8)
   argmax    the first index of the maximum, with NaN handling
+  fused     the operations fused on either side of a GEMV: RMSNorm of the
+            float32 residual stream into the bf16 GEMV input, the residual
+            add, SwiGLU of paired gate/up rows, and their tolerances
 
 Parity status: every function here is pinned by tests that do not re-use it
 (library conversions, hand-built blocks with closed-form dot products,
-exact rational brute force, quantizer error bounds); there is no unpinned
+exact rational brute force, quantizer error bounds, torch's rms_norm and
+silu, closed-form normalizations and activations); there is no unpinned
 function.
 """
 from .formats import (BF16, INT8_G32, Q4_0_G32, INT4_G128, GROUP, bf16_to_f64, f16_to_f64,
