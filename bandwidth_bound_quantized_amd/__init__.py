@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_run": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp]),
         "qgemv_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
         "qgemv_run_flags": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp]),
+        "qgemv_run_fused": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp]),
         "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
@@ -75,7 +76,7 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_flags",
-           "qgemv_run_grouped",
+           "qgemv_run_fused", "qgemv_run_grouped",
            "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
@@ -188,6 +189,58 @@ def run_ptr(fmt: int, wp: int, sp: Optional[int], xp: int, yp: int, M: int, K: i
     st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, stream_handle)
     if st != OK:
         raise QgemvError(st, "qgemv_run")
+
+
+class Fusion(ctypes.Structure):
+    """Mirror of qgemv_fusion (device pointers as integers; 0/None = unused)."""
+    _fields_ = [("norm_input", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("residual", ctypes.c_void_p),
+                ("swiglu_out", ctypes.c_void_p), ("argmax_idx", ctypes.c_void_p),
+                ("argmax_ws", ctypes.c_void_p)]
+
+
+def run_fused(fmt: int, W, scales, x, y, M: int, K: int, batch: int, *, norm_input=None,
+              norm_weight=None, eps: float = 1e-5, residual=None, swiglu_out=None, argmax_idx=None,
+              argmax_ws=None, stream=None) -> None:
+    """qgemv_run_fused: the GEMV with RMSNorm of norm_input as its input (x None), a
+    residual add or SwiGLU of paired rows in its epilogue, and optionally the argmax."""
+    import torch
+    f = Fusion()
+    if norm_input is not None:
+        f.norm_input = _dev_ptr(norm_input, "norm_input", torch.float32)
+        f.norm_weight = _dev_ptr(norm_weight, "norm_weight", (torch.int16, torch.uint16, torch.bfloat16))
+        if norm_input.numel() < batch * K or norm_weight.numel() < K:
+            raise ValueError("norm_input or norm_weight too small")
+    f.norm_eps = eps
+    if residual is not None:
+        f.residual = _dev_ptr(residual, "residual", torch.float32)
+        if residual.numel() < batch * M:
+            raise ValueError("residual too small")
+    if swiglu_out is not None:
+        f.swiglu_out = _dev_ptr(swiglu_out, "swiglu_out", (torch.int16, torch.uint16, torch.bfloat16))
+        if swiglu_out.numel() < batch * (M // 2):
+            raise ValueError("swiglu_out too small")
+    if argmax_idx is not None:
+        f.argmax_idx = _dev_ptr(argmax_idx, "argmax_idx", torch.int32)
+        f.argmax_ws = _dev_ptr(argmax_ws, "argmax_ws", (torch.int64, torch.uint64))
+        if argmax_ws.numel() < batch * FUSED_ARGMAX_WS_WORDS_PER_ROW or argmax_idx.numel() < batch:
+            raise ValueError("argmax_ws or argmax_idx too small")
+    wp = _dev_ptr(W, "W")
+    sp = _dev_ptr(scales, "scales") if scales is not None else None
+    xp = _dev_ptr(x, "x", (torch.int16, torch.uint16, torch.bfloat16)) if x is not None else None
+    yp = _dev_ptr(y, "y", torch.float32) if y is not None else None
+    if (x is not None and x.numel() < batch * K) or (y is not None and y.numel() < batch * M):
+        raise ValueError("x or y too small for (batch, M, K)")
+    _check(_lib.qgemv_run_fused(fmt, wp, sp, xp, yp, M, K, batch, ctypes.byref(f), _stream_handle(stream)),
+           "qgemv_run_fused")
+
+
+def run_fused_ptr(fmt: int, wp: int, sp: Optional[int], xp: Optional[int], yp: Optional[int], M: int, K: int,
+                  batch: int, fusion: "Fusion", stream_handle) -> None:
+    """Raw-pointer form of run_fused() for timing loops (no tensor checks)."""
+    st = _lib.qgemv_run_fused(fmt, wp, sp, xp, yp, M, K, batch, ctypes.byref(fusion), stream_handle)
+    if st != OK:
+        raise QgemvError(st, "qgemv_run_fused")
 
 
 class GemvDesc(ctypes.Structure):

@@ -114,6 +114,36 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
+// float32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+}
+// the two bf16 values of a packed pair, as float32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// SwiGLU's gate activation t * sigmoid(t) (for t -> -inf, t / inf = -0)
+__device__ __forceinline__ float silu(float t) { return t / (1.f + expf(-t)); }
+
+// Epilogue of one output y[b][m] = v (see Fusion): a plain store, a residual
+// add, or, on the even row of each gate/up pair, the SwiGLU activation of
+// the pair (partner = the odd row's value). Returns the value stored in y.
+__device__ __forceinline__ float epi_store(const Fusion& f, float* __restrict__ Y, int M, int b, int m,
+                                           float v, float partner) {
+  const size_t o = static_cast<size_t>(b) * M + m;
+  if (f.epi == kEpiSwiglu) {
+    if ((m & 1) == 0) f.act[static_cast<size_t>(b) * (M >> 1) + (m >> 1)] = to_bf16(silu(v) * partner);
+    return v;
+  }
+  if (f.epi == kEpiResidual) v = f.res[o] + v;
+  Y[o] = v;
+  return v;
+}
+
 template <int FMT> struct Traits;
 template <> struct Traits<QGEMV_BF16> {
   static constexpr int kElems = 8;      // weights per 16-byte unit
@@ -306,182 +336,6 @@ __device__ __forceinline__ float bias_start(const uint32_t (&xv)[Traits<FMT>::kP
   return -8.f * s;
 }
 
-// Reduce acc[R][NB] over the wave and store row group `grp`'s outputs.
-template <int R, int NB>
-__device__ __forceinline__ void reduce_store(float (&acc)[R][NB], int lane, int grp, int M,
-                                             int batch, float* __restrict__ Y) {
-  constexpr int V = R * NB;
-  float v[V];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
-  const float res = reduce_wave<V>(v, lane);
-  constexpr int SH = 6 - ilog2(V);
-  if ((lane & ((1 << SH) - 1)) == 0) {
-    const int idx = lane >> SH;
-    const int r = idx / NB, b = idx % NB;
-    const int row = grp * R + r;
-    if (row < M && b < batch) Y[static_cast<size_t>(b) * M + row] = res;
-  }
-}
-
-template <int FMT, int NB, int R>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(
-    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
-    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch) {
-  using T = Traits<FMT>;
-  constexpr int UC = T::kUC;
-  constexpr int P = T::kPairs;
-  extern __shared__ u32x4 lds_v4[];
-  uint32_t* lds = reinterpret_cast<uint32_t*>(lds_v4);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int KD = K >> 1;                              // x dwords per batch row
-  const int U = K / T::kElems;                        // 16-byte units per row
-  const size_t row_bytes = static_cast<size_t>(U) * 16;
-  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
-  const int groups = (M + R - 1) / R;
-  const int waves_total = gridDim.x * kWaves;
-  const int nchunk = (U + 64 * UC - 1) / (64 * UC);
-
-  uint32_t* xs = lds;                                        // [NB][KD]
-  float* sxs = reinterpret_cast<float*>(lds + NB * KD);      // [NB][U] (4-bit only)
-
-  u32x4 wv[R][UC];
-  uint32_t sv[R][UC];   // binary16 scale bits, one per 32-bit register
-
-  // Issue the loads of one step (R rows x UC units per lane), branch-free:
-  // lanes past the end of a ragged row re-load the row's last unit (an
-  // in-bounds address on a line the wave reads anyway) and skip it when
-  // computing; rows past M re-load row M-1 and are not stored.
-  auto load_step = [&](int grp, int ch) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(grp * R + r, M - 1);
-      const u32x4* wrow = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(row) * row_bytes);
-#pragma unroll
-      for (int u = 0; u < UC; ++u) {
-        const int t = min(ch * 64 * UC + u * 64 + lane, U - 1);
-        wv[r][u] = load_weights(wrow + t);
-        if constexpr (T::kUnitsPerScale > 0)
-          sv[r][u] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
-      }
-    }
-  };
-
-  // ---- stage x. The first chunks are loaded before this wave's first
-  // weight loads are issued, so waiting for them does not wait for weights.
-  constexpr int kXPre = 4;
-  const int row_chunks = K / 8;                      // 16-byte chunks per x row
-  const int nxc = NB * row_chunks;                   // chunks staged (NB rows)
-  const int valid_xc = batch * row_chunks;           // chunks that exist in X
-  u32x4 xpre[kXPre];
-#pragma unroll
-  for (int j = 0; j < kXPre; ++j) {
-    const int i = tid + j * kThreads;
-    xpre[j] = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
-  }
-
-  int grp = blockIdx.x * kWaves + wave;
-  int ch = 0;
-  load_step(min(grp, groups - 1), 0);
-
-#pragma unroll
-  for (int j = 0; j < kXPre; ++j) {
-    const int i = tid + j * kThreads;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (i < nxc) reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? xpre[j] : zero;
-  }
-  for (int i = tid + kXPre * kThreads; i < nxc; i += kThreads) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const u32x4 v = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
-    reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? v : zero;
-  }
-  __syncthreads();
-
-  if constexpr (T::kBias) {
-    // per-unit sums of x, pre-multiplied by -8 (the dot chain's start value)
-    constexpr uint32_t kOnes = 0x3f803f80u;          // bf16 pair (1.0, 1.0)
-    for (int i = tid; i < NB * U; i += kThreads) {
-      const int b = i / U, t = i - b * U;
-      uint32_t xv[P];
-      read_x<FMT>(xs + b * KD, t, xv);
-      float s = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) s = dot2(xv[p], kOnes, s);
-      sxs[i] = -8.f * s;
-    }
-    __syncthreads();
-  }
-
-  float acc[R][NB];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-
-  while (grp < groups) {
-    // compute the step whose loads are in flight
-#pragma unroll
-    for (int u = 0; u < UC; ++u) {
-      const int t = ch * 64 * UC + u * 64 + lane;
-      if (t < U) {
-        uint32_t pr[R][P];
-        float dsc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          unpack<FMT>(wv[r][u], pr[r]);
-          dsc[r] = unit_scale<FMT>(sv[r][u]);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          uint32_t xv[P];
-          read_x<FMT>(xs + b * KD, t, xv);
-          const float init = T::kBias ? sxs[b * U + t] : 0.f;
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if constexpr (FMT == QGEMV_BF16) {
-              float a = acc[r][b];
-#pragma unroll
-              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
-              acc[r][b] = a;
-            } else {
-              float a = init;
-#pragma unroll
-              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
-              acc[r][b] = __builtin_fmaf(dsc[r], a, acc[r][b]);
-            }
-          }
-        }
-      }
-    }
-
-    const int cur = grp;
-    if (++ch == nchunk) { ch = 0; grp += waves_total; }
-    if (grp < groups) load_step(grp, ch);
-
-    if (ch == 0) {
-      constexpr int V = R * NB;
-      float v[V];
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
-      const float res = reduce_wave<V>(v, lane);
-      constexpr int SH = 6 - ilog2(V);
-      if ((lane & ((1 << SH) - 1)) == 0) {
-        const int idx = lane >> SH;
-        const int r = idx / NB, b = idx % NB;
-        const int row = cur * R + r;
-        if (row < M && b < batch) Y[static_cast<size_t>(b) * M + row] = res;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Wave reduction without LDS round trips (for R * NB <= 8 partial sums).
 // v_permlane32_swap / v_permlane16_swap exchange whole 16-lane rows between
@@ -580,6 +434,68 @@ constexpr int kWeightAux = 2;         // non-temporal
 constexpr int kWeightAux = 0;
 #endif
 
+// ---- RMSNorm prologue of the register-x kernel. A wave's lanes together
+// own every unit of a row, so the wave sees all of h: each lane sums the
+// squares of the h values its units pair with, the wave adds the lanes'
+// sums (in a fixed order, identical in every wave), and each lane then
+// writes its x registers as bf16(h * r * g) with r = 1 / sqrt(sum / K + eps).
+//
+// Dword (bf16 pair) p of the x values unit t pairs with (the order read_x uses).
+template <int FMT>
+__device__ __forceinline__ int x_dword(int t, int p) {
+  int lo, hi;
+  x_offsets<FMT>(t, lo, hi);
+  constexpr int P = Traits<FMT>::kPairs;
+  if constexpr (FMT == QGEMV_BF16) return lo + p;
+  else return p < P / 2 ? lo + p : hi + (p - P / 2);
+}
+
+template <int FMT>
+__device__ __forceinline__ float unit_sumsq(const float* __restrict__ hb, int t) {
+  float s = 0.f;
+#pragma unroll
+  for (int p = 0; p < Traits<FMT>::kPairs; ++p) {
+    const float2 v = *reinterpret_cast<const float2*>(hb + 2 * x_dword<FMT>(t, p));
+    s = __builtin_fmaf(v.x, v.x, s);
+    s = __builtin_fmaf(v.y, v.y, s);
+  }
+  return s;
+}
+
+template <int FMT>
+__device__ __forceinline__ void norm_x(const float* __restrict__ hb, const uint32_t* __restrict__ g, int t,
+                                       float r, uint32_t (&xv)[Traits<FMT>::kPairs]) {
+#pragma unroll
+  for (int p = 0; p < Traits<FMT>::kPairs; ++p) {
+    const int dw = x_dword<FMT>(t, p);
+    const float2 v = *reinterpret_cast<const float2*>(hb + 2 * dw);
+    const uint32_t gg = g[dw];
+    xv[p] = pack_bf16(v.x * r * bf16_lo(gg), v.y * r * bf16_hi(gg));
+  }
+}
+
+// Sum over the 64 lanes, the same value in every lane, in a fixed order.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_allreduce(x);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ float rms_factor(float sumsq, int K, float eps) {
+  return 1.f / sqrtf(sumsq / static_cast<float>(K) + eps);
+}
+
+// The lane that holds the value of index idx + NB after reduce_wave_rows<V>
+// (the next row of a gate/up pair, same batch row) is lane ^ pair_xor: index
+// bit log2(NB) lives in lane bit 5 (V = 2); 4, 5 (V = 4); 0, 4, 5 (V = 8).
+template <int V, int NB>
+constexpr int pair_xor() {
+  return V == 2 ? 32 : V == 4 ? (NB == 1 ? 16 : 32) : (NB == 1 ? 1 : NB == 2 ? 16 : 32);
+}
+
 // One GEMV of a table walked by the register-x kernel. `start` is the index of
 // the GEMV's first row group in the concatenation of all the table's groups.
 struct TableEntry {
@@ -660,11 +576,13 @@ __device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __r
 // With AM, every output of entry tab.am a lane stores also goes into the
 // lane's running argmax key, and after the wave's last row group of that
 // entry the wave hands its keys over (am_leave).
-template <int FMT, int NB, int R, int NCH, int N, bool AM = false>
+// FUSED: the RMSNorm prologue and the epilogue of fu (one-entry tables).
+template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
                                         int batch, int lane, AmLane& am, AmShared* am_sh,
-                                        uint64_t* am_slots) {
+                                        uint64_t* am_slots, const Fusion& fu) {
   using T = Traits<FMT>;
+  static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
   constexpr int P = T::kPairs;
   constexpr int kShape = xreg_shape(R, NCH);
   const uint8_t* W;
@@ -689,6 +607,23 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       const int t = min(c * 64 + lane, U - 1);
       woff[c] = t * 16;
       soff[c] = T::kUnitsPerScale ? (t / T::kUnitsPerScale) * 2 : 0;
+    }
+    if constexpr (FUSED) {
+      if (fu.h != nullptr) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float* hb = fu.h + static_cast<size_t>(min(b, batch - 1)) * e.K;
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            if (c * 64 + lane < U) ss += unit_sumsq<FMT>(hb, c * 64 + lane);
+          const float r = rms_factor(wave_sum(ss), e.K, fu.eps);
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            norm_x<FMT>(hb, reinterpret_cast<const uint32_t*>(fu.g), min(c * 64 + lane, U - 1), r, xr[b][c]);
+        }
+        return;
+      }
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -794,11 +729,17 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       const float res = reduce_wave_rows<V>(v, lane, &idx, &owner);
       const int r = idx / NB, b = idx % NB;
       const int row = grp * R + r;
+      float partner = 0.f;
+      if constexpr (FUSED) {
+        if (fu.epi == kEpiSwiglu) partner = __shfl_xor(res, pair_xor<V, NB>());
+      }
       if (owner && row < cur_M && b < batch) {
-        cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
+        float out = res;
+        if constexpr (FUSED) out = epi_store(fu, cur_Y, cur_M, b, row, res, partner);
+        else cur_Y[static_cast<size_t>(b) * cur_M + row] = res;
         if constexpr (AM) {
           if (cur_j == tab.am) {
-            am.key = umax64(am.key, argmax_key(res, static_cast<uint32_t>(row)));
+            am.key = umax64(am.key, argmax_key(out, static_cast<uint32_t>(row)));
             am.b = b;
           }
         }
@@ -831,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<1> 
   if (item >= tab.total) return;                 // no barriers in this kernel
   int j = 0;
   AmLane am;
-  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, am, nullptr, nullptr);
+  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, am, nullptr, nullptr, Fusion{});
 }
 
 constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most workgroups per launch
@@ -928,7 +869,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
       switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
         case xreg_shape(R_, C_): \
-          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots); break;
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots, Fusion{}); break;
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
@@ -938,6 +879,38 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         default: item = tab.total;               // not produced by the host
       }
     }
+  }
+  if constexpr (AM) {
+    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
+    __syncthreads();
+    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
+  }
+}
+
+
+// qgemv_run_fused at batch <= 2 with short rows: one GEMV of one (R, NCH)
+// with the RMSNorm prologue and the epilogue of fu, and with AM the argmax
+// of its output fused in as in the grouped launch (one kernel per shape, so
+// each shape gets its own register budget).
+template <int FMT, int NB, int R, int NCH, bool AM>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTable<1> tab, int batch,
+                                                                   uint64_t* __restrict__ slots,
+                                                                   int32_t* __restrict__ idx,
+                                                                   const Fusion fu) {
+  __shared__ AmShared am_sh;
+  __shared__ uint64_t red[kWaves];
+  if constexpr (AM) {
+    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
+    if (threadIdx.x == 0) am_sh.left = 0;
+    __syncthreads();
+  }
+  int stride;
+  int item = first_item(stride);
+  const int lane = threadIdx.x & 63;
+  AmLane am;
+  if (item < tab.total) {
+    int j = 0;
+    xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, &am_sh, slots, fu);
   }
   if constexpr (AM) {
     if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
@@ -1125,10 +1098,52 @@ struct MfmaTable {
   MfmaEntry e[N];
 };
 
+constexpr int kNormFactorOff = (kMfmaMaxThreads / 64) * QGEMV_MAX_BATCH;   // floats
+static_assert((kNormFactorOff + QGEMV_MAX_BATCH) * 4 <= static_cast<int>(kNormScratchBytes), "norm scratch");
+
+// Block-wide RMSNorm factors of the fused prologue: scr[kNormFactorOff + b]
+// = 1 / sqrt(mean of h[b][:]^2 + eps) for b < batch (scr: kNormScratchBytes
+// of LDS): thread partials over k = 4t, 4t + 4 * threads, ..., then the
+// waves' sums in wave order. Ends with a barrier; every thread must call it.
+__device__ __forceinline__ void block_rms_factors(const Fusion& fu, int K, int batch, float* scr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = static_cast<int>(blockDim.x >> 6);
+  for (int b = 0; b < batch; ++b) {
+    const float* hb = fu.h + static_cast<size_t>(b) * K;
+    float s = 0.f;
+    for (int k = 4 * tid; k < K; k += 4 * static_cast<int>(blockDim.x)) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(hb + k);
+      s = __builtin_fmaf(v.x, v.x, s);
+      s = __builtin_fmaf(v.y, v.y, s);
+      s = __builtin_fmaf(v.z, v.z, s);
+      s = __builtin_fmaf(v.w, v.w, s);
+    }
+    s = wave_sum(s);
+    if (lane == 0) scr[wave * QGEMV_MAX_BATCH + b] = s;
+  }
+  __syncthreads();
+  if (tid < batch) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += scr[w * QGEMV_MAX_BATCH + tid];
+    scr[kNormFactorOff + tid] = rms_factor(s, K, fu.eps);
+  }
+  __syncthreads();
+}
+
+// Four consecutive normalized inputs h[e..e+3] * r * g[e..e+3] as bf16 pairs.
+__device__ __forceinline__ u32x2 norm4(const float* __restrict__ h, const uint16_t* __restrict__ g, int e, float r) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(h + e);
+  const u32x2 gg = *reinterpret_cast<const u32x2*>(g + e);
+  return u32x2{pack_bf16(v.x * r * bf16_lo(gg.x), v.y * r * bf16_hi(gg.x)),
+               pack_bf16(v.z * r * bf16_lo(gg.y), v.w * r * bf16_hi(gg.y))};
+}
+
 // Units [g0, g1) of one entry (the body of the matrix-core kernel).
-template <int FMT, int NB>
+// FUSED: the operations of fu fused in (prologue in the x staging, epilogue
+// in the store); the LDS then ends with kNormScratchBytes of scratch.
+template <int FMT, int NB, bool FUSED = false>
 __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1, int batch, int KS,
-                                           u32x4* lds_v4) {
+                                           u32x4* lds_v4, const Fusion& fu) {
   using F = MfmaFmt<FMT>;
   constexpr int kCPS = F::kChunksPerSlice;
   constexpr int kChunks = F::kSlices * kCPS;          // chunks per step
@@ -1304,9 +1319,25 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
   };
 
   // D tile -> y: lane (i, q) holds batch rows 4q..4q+3 of row i of the tile
+  // (the paired row of a gate/up pair is in lane i ^ 1, same q)
   auto store = [&](const f32x4& v, int n) {
     const int tile = (g0 + n) * TW + tg;
     const int row = tile * 16 + i;
+    if constexpr (FUSED) {
+      f32x4 pv = v;
+      if (fu.epi == kEpiSwiglu) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[j] = __shfl_xor(v[j], 1);
+      }
+      if (row < M) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = 4 * q + j;
+          if (b < batch) epi_store(fu, Y, M, b, row, v[j], pv[j]);
+        }
+      }
+      return;
+    }
     if (row < M) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1346,7 +1377,29 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
 
   // ---- stage x (all K, NB rows; rows >= batch as zero) in chunk order,
   // four 16-byte slots per thread per round so the loads overlap
-  {
+  bool staged = false;
+  if constexpr (FUSED) {
+    if (fu.h != nullptr) {
+      // RMSNorm prologue: the same slots, written from h and g
+      float* scr = reinterpret_cast<float*>(red + (KS > 1 ? 2 * TW * KS * kOutLanes : 0));
+      block_rms_factors(fu, K, batch, scr);
+      const int nslots = nchunk * NB * 4;
+      for (int sl = tid; sl < nslots; sl += static_cast<int>(blockDim.x)) {
+        const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (b < batch) {
+          const float* hr = fu.h + static_cast<size_t>(b) * K;
+          const float r = scr[kNormFactorOff + b];
+          const u32x2 lo = norm4(hr, fu.g, chunk_elem<FMT>(c, 8 * qq), r);
+          const u32x2 hi = norm4(hr, fu.g, chunk_elem<FMT>(c, 8 * qq + 4), r);
+          v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        reinterpret_cast<u32x4*>(xs)[sl] = v;
+      }
+      staged = true;
+    }
+  }
+  if (!staged) {
     const int nslots = nchunk * NB * 4;
     for (int base = tid; base < nslots; base += 4 * static_cast<int>(blockDim.x)) {
       u32x2 r0[4], r1[4];
@@ -1416,11 +1469,204 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
   }
 }
 
+// The LDS dot2 kernel: x for all batch rows staged once per workgroup in
+// LDS, then the dot2 streaming loop over row groups of R rows. FUSED: the
+// operations of fu fused in (prologue in the staging, epilogue in the
+// store); the LDS then ends with kNormScratchBytes of scratch.
+template <int FMT, int NB, int R, bool FUSED = false>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(
+    const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ X, float* __restrict__ Y, int M, int K, int batch, const Fusion fu) {
+  static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
+  using T = Traits<FMT>;
+  constexpr int UC = T::kUC;
+  constexpr int P = T::kPairs;
+  extern __shared__ u32x4 lds_v4[];
+  uint32_t* lds = reinterpret_cast<uint32_t*>(lds_v4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int KD = K >> 1;                              // x dwords per batch row
+  const int U = K / T::kElems;                        // 16-byte units per row
+  const size_t row_bytes = static_cast<size_t>(U) * 16;
+  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
+  const int groups = (M + R - 1) / R;
+  const int waves_total = gridDim.x * kWaves;
+  const int nchunk = (U + 64 * UC - 1) / (64 * UC);
+
+  uint32_t* xs = lds;                                        // [NB][KD]
+  float* sxs = reinterpret_cast<float*>(lds + NB * KD);      // [NB][U] (4-bit only)
+
+  u32x4 wv[R][UC];
+  uint32_t sv[R][UC];   // binary16 scale bits, one per 32-bit register
+
+  // Issue the loads of one step (R rows x UC units per lane), branch-free:
+  // lanes past the end of a ragged row re-load the row's last unit (an
+  // in-bounds address on a line the wave reads anyway) and skip it when
+  // computing; rows past M re-load row M-1 and are not stored.
+  auto load_step = [&](int grp, int ch) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(grp * R + r, M - 1);
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(row) * row_bytes);
+#pragma unroll
+      for (int u = 0; u < UC; ++u) {
+        const int t = min(ch * 64 * UC + u * 64 + lane, U - 1);
+        wv[r][u] = load_weights(wrow + t);
+        if constexpr (T::kUnitsPerScale > 0)
+          sv[r][u] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
+      }
+    }
+  };
+
+  // ---- stage x. The first chunks are loaded before this wave's first
+  // weight loads are issued, so waiting for them does not wait for weights.
+  constexpr int kXPre = 4;
+  const int row_chunks = K / 8;                      // 16-byte chunks per x row
+  const int nxc = NB * row_chunks;                   // chunks staged (NB rows)
+  const int valid_xc = batch * row_chunks;           // chunks that exist in X
+  bool norm = false;
+  if constexpr (FUSED) norm = fu.h != nullptr;
+  u32x4 xpre[kXPre];
+  if (!norm) {
+#pragma unroll
+    for (int j = 0; j < kXPre; ++j) {
+      const int i = tid + j * kThreads;
+      xpre[j] = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
+    }
+  }
+
+  int grp = blockIdx.x * kWaves + wave;
+  int ch = 0;
+  load_step(min(grp, groups - 1), 0);
+
+  if (!norm) {
+#pragma unroll
+    for (int j = 0; j < kXPre; ++j) {
+      const int i = tid + j * kThreads;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (i < nxc) reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? xpre[j] : zero;
+    }
+    for (int i = tid + kXPre * kThreads; i < nxc; i += kThreads) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 v = reinterpret_cast<const u32x4*>(X)[min(i, valid_xc - 1)];
+      reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? v : zero;
+    }
+  } else {
+    // RMSNorm prologue: x = bf16(h * r * g), 8 elements per 16-byte chunk
+    float* scr = reinterpret_cast<float*>(lds + NB * KD + (T::kBias ? NB * U : 0));
+    block_rms_factors(fu, K, batch, scr);
+    for (int i = tid; i < nxc; i += kThreads) {
+      const int b = i / row_chunks, c = i - b * row_chunks;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (b < batch) {
+        const float* hr = fu.h + static_cast<size_t>(b) * K;
+        const float r = scr[kNormFactorOff + b];
+        const u32x2 lo = norm4(hr, fu.g, 8 * c, r);
+        const u32x2 hi = norm4(hr, fu.g, 8 * c + 4, r);
+        v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      reinterpret_cast<u32x4*>(xs)[i] = v;
+    }
+  }
+  __syncthreads();
+
+  if constexpr (T::kBias) {
+    // per-unit sums of x, pre-multiplied by -8 (the dot chain's start value)
+    constexpr uint32_t kOnes = 0x3f803f80u;          // bf16 pair (1.0, 1.0)
+    for (int i = tid; i < NB * U; i += kThreads) {
+      const int b = i / U, t = i - b * U;
+      uint32_t xv[P];
+      read_x<FMT>(xs + b * KD, t, xv);
+      float s = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) s = dot2(xv[p], kOnes, s);
+      sxs[i] = -8.f * s;
+    }
+    __syncthreads();
+  }
+
+  float acc[R][NB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  while (grp < groups) {
+    // compute the step whose loads are in flight
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
+      const int t = ch * 64 * UC + u * 64 + lane;
+      if (t < U) {
+        uint32_t pr[R][P];
+        float dsc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          unpack<FMT>(wv[r][u], pr[r]);
+          dsc[r] = unit_scale<FMT>(sv[r][u]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          uint32_t xv[P];
+          read_x<FMT>(xs + b * KD, t, xv);
+          const float init = T::kBias ? sxs[b * U + t] : 0.f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if constexpr (FMT == QGEMV_BF16) {
+              float a = acc[r][b];
+#pragma unroll
+              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+              acc[r][b] = a;
+            } else {
+              float a = init;
+#pragma unroll
+              for (int p = 0; p < P; ++p) a = dot2(pr[r][p], xv[p], a);
+              acc[r][b] = __builtin_fmaf(dsc[r], a, acc[r][b]);
+            }
+          }
+        }
+      }
+    }
+
+    const int cur = grp;
+    if (++ch == nchunk) { ch = 0; grp += waves_total; }
+    if (grp < groups) load_step(grp, ch);
+
+    if (ch == 0) {
+      constexpr int V = R * NB;
+      float v[V];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { v[r * NB + b] = acc[r][b]; acc[r][b] = 0.f; }
+      const float res = reduce_wave<V>(v, lane);
+      constexpr int SH = 6 - ilog2(V);
+      // every lane of a 2^SH-lane segment holds the segment's value; the
+      // paired row of a gate/up pair (index + NB) is NB segments further
+      float partner = 0.f;
+      if constexpr (FUSED) {
+        if (fu.epi == kEpiSwiglu) partner = __shfl_xor(res, NB << SH);
+      }
+      if ((lane & ((1 << SH) - 1)) == 0) {
+        const int idx = lane >> SH;
+        const int r = idx / NB, b = idx % NB;
+        const int row = cur * R + r;
+        if (row < M && b < batch) {
+          if constexpr (FUSED) epi_store(fu, Y, M, b, row, res, partner);
+          else Y[static_cast<size_t>(b) * M + row] = res;
+        }
+      }
+    }
+  }
+}
+
 // A table of GEMVs of one format, K and batch. Workgroup w takes the
 // contiguous units [w*units/G, (w+1)*units/G), entry by entry (x is staged
 // again when the entry changes), so most workgroups stage x once.
-template <int FMT, int NB, int N>
-__global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch) {
+template <int FMT, int NB, int N, bool FUSED = false>
+__global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch,
+                                                                    const Fusion fu) {
   extern __shared__ u32x4 lds_v4[];
   const long U = tab.units, G = gridDim.x;
   const int u0 = static_cast<int>(blockIdx.x * U / G);
@@ -1433,7 +1679,7 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTa
   for (int u = u0; u < u1; ++j) {
     const int uend = min(u1, (N > 1 && j + 1 < tab.n) ? tab.e[j + 1].ustart : tab.units);
     if (u != u0) __syncthreads();                // the previous entry's LDS is no longer read
-    mfma_units<FMT, NB>(tab.e[j], u - tab.e[j].ustart, uend - tab.e[j].ustart, batch, tab.KS, lds_v4);
+    mfma_units<FMT, NB, FUSED>(tab.e[j], u - tab.e[j].ustart, uend - tab.e[j].ustart, batch, tab.KS, lds_v4, fu);
     u = uend;
   }
 }
@@ -1444,9 +1690,9 @@ template <int FMT, int NB>
 hipError_t launch_fr(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t st) {
   const uint8_t* W = static_cast<const uint8_t*>(a.W);
   switch (R) {
-    case 1: gemv_kernel<FMT, NB, 1><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
-    case 2: gemv_kernel<FMT, NB, 2><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
-    default: gemv_kernel<FMT, NB, 4><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch); break;
+    case 1: gemv_kernel<FMT, NB, 1><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch, Fusion{}); break;
+    case 2: gemv_kernel<FMT, NB, 2><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch, Fusion{}); break;
+    default: gemv_kernel<FMT, NB, 4><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch, Fusion{}); break;
   }
   return hipGetLastError();
 }
@@ -1461,9 +1707,9 @@ hipError_t launch_f(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t 
   }
 }
 
-template <int FMT, int NB, int R>
+template <int FMT, int NB, int R, bool FUSED = false>
 void allow_big_lds() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, NB, R>),
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, NB, R, FUSED>),
                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
@@ -1586,7 +1832,7 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 // tiles per workgroup (TW) that keep the most waves busy on real tiles, up
 // to the target per CU; among equals, the fewest workgroups (each stages x
 // once), then the smallest workgroup.
-bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
+bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out, size_t extra_lds = 0) {
   const int NB = round_batch(batch);
   if (NB < 4) return false;
   const int step = mfma_step_elems(fmt);
@@ -1600,7 +1846,7 @@ bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
     if (QGEMV_MFMA_FORCE_KS && KS != QGEMV_MFMA_FORCE_KS) continue;
     for (int TW = 1; TW * KS <= 16; TW *= 2) {
       if (QGEMV_MFMA_FORCE_TW && TW != QGEMV_MFMA_FORCE_TW) continue;
-      const size_t lds = mfma_lds_bytes(fmt, K, NB, KS, TW);
+      const size_t lds = mfma_lds_bytes(fmt, K, NB, KS, TW) + extra_lds;
       if (lds > kLdsPerCu) continue;
       const int wg_cu = std::min(static_cast<int>(kLdsPerCu / lds), QGEMV_MFMA_MAX_WAVES_PER_CU / (KS * TW));
       if (wg_cu < 1) continue;
@@ -1627,8 +1873,9 @@ bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out) {
 
 // n GEMVs of one format, K and batch on the matrix cores with plan p (made
 // for their tiles together; one entry for qgemv_run).
-template <int FMT, int NB, int N>
-hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st) {
+template <int FMT, int NB, int N, bool FUSED = false>
+hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st,
+                             const Fusion& fu = Fusion{}) {
   MfmaTable<N> tab{};
   tab.n = n;
   tab.KS = p.KS;
@@ -1643,11 +1890,11 @@ hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStr
   const int grid = std::max(1, std::min(p.grid, u));
   if (p.lds > 64 * 1024) {
     static const hipError_t once = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N>),
+        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N, FUSED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
     if (once != hipSuccess) return once;
   }
-  gemv_mfma_kernel<FMT, NB, N><<<grid, 64 * p.KS * p.TW, p.lds, st>>>(tab, a[0].batch);
+  gemv_mfma_kernel<FMT, NB, N, FUSED><<<grid, 64 * p.KS * p.TW, p.lds, st>>>(tab, a[0].batch, fu);
   return hipGetLastError();
 }
 
@@ -1795,6 +2042,111 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int a
     case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, R, nch, n, grid, am, slots, idx, stream);
     case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, R, nch, n, grid, am, slots, idx, stream);
     default: return launch_group1<QGEMV_INT4_G128>(a, R, nch, n, grid, am, slots, idx, stream);
+  }
+}
+
+// ---- qgemv_run_fused: one GEMV with the RMSNorm prologue and an epilogue.
+// Batch <= 2 with short rows: the register-x table kernel with one entry
+// (rows per step >= 2, so the rows of a gate/up pair share a wave; the
+// argmax fused in as in the grouped launch); otherwise the matrix-core or
+// LDS dot2 kernel, followed by the argmax kernel when asked for.
+template <int FMT, int NB, int R, int NCH>
+hipError_t launch_fused_xreg(const GemvArgs& a, const Fusion& f, uint64_t* slots, int32_t* idx, hipStream_t st) {
+  GemvTable<1> tab{};
+  tab.n = 1;
+  tab.am = idx ? 0 : -1;
+  tab.total = (a.M + R - 1) / R;
+  tab.e[0] = TableEntry{static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, 0, xreg_shape(R, NCH)};
+  const int cus = device_cu_count();
+  int grid = (tab.total + kWaves - 1) / kWaves;
+  if (idx) {
+    static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
+        &gemv_xreg_fused_kernel<FMT, NB, R, NCH, true>));
+    grid = std::max(1, std::min({grid, cus * per_cu, static_cast<int>(kFusedSlots)}));
+    gemv_xreg_fused_kernel<FMT, NB, R, NCH, true><<<grid, kThreads, 0, st>>>(tab, a.batch, slots, idx, f);
+  } else {
+    static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
+        &gemv_xreg_fused_kernel<FMT, NB, R, NCH, false>));
+    grid = std::max(1, std::min(grid, cus * per_cu));
+    gemv_xreg_fused_kernel<FMT, NB, R, NCH, false><<<grid, kThreads, 0, st>>>(tab, a.batch, nullptr, nullptr, f);
+  }
+  return hipGetLastError();
+}
+
+// rows per step: 4 at one unit per lane-column while every CU's waves still
+// get work, else 2 (the rows of a gate/up pair must share a row group)
+template <int FMT, int NB>
+hipError_t launch_fused_xreg_shape(const GemvArgs& a, int nch, bool r4, const Fusion& f, uint64_t* slots,
+                                   int32_t* idx, hipStream_t st) {
+  switch (nch) {
+    case 1: return r4 ? launch_fused_xreg<FMT, NB, 4, 1>(a, f, slots, idx, st)
+                      : launch_fused_xreg<FMT, NB, 2, 1>(a, f, slots, idx, st);
+    case 2: return launch_fused_xreg<FMT, NB, 2, 2>(a, f, slots, idx, st);
+    case 3: return launch_fused_xreg<FMT, NB, 2, 3>(a, f, slots, idx, st);
+    default: return launch_fused_xreg<FMT, NB, 2, 4>(a, f, slots, idx, st);
+  }
+}
+
+template <int FMT>
+hipError_t launch_fused_fmt(const GemvArgs& a, const Fusion& f, uint64_t* slots, int32_t* idx,
+                            hipStream_t st) {
+  const int cus = device_cu_count();
+  const int nb = round_batch(a.batch);
+  if (!gemv_uses_lds(FMT, a.K, a.batch)) {
+    const int nch = gemv_group_class(FMT, a.K, a.batch);
+    const bool r4 = a.M / 4 >= QGEMV_MIN_WAVES_PER_CU * cus;
+    if (nb == 1) return launch_fused_xreg_shape<FMT, 1>(a, nch, r4, f, slots, idx, st);
+    return launch_fused_xreg_shape<FMT, 2>(a, nch, r4, f, slots, idx, st);
+  }
+  hipError_t e;
+  MfmaPlan plan;
+  if (plan_mfma(FMT, a.M, a.K, a.batch, cus, &plan, kNormScratchBytes)) {
+    e = nb == 4 ? launch_mfma_table<FMT, 4, 1, true>(&a, 1, plan, st, f)
+                : launch_mfma_table<FMT, 8, 1, true>(&a, 1, plan, st, f);
+  } else {
+    const size_t lds = gemv_lds_bytes(FMT, a.K, a.batch) + kNormScratchBytes;
+    int R = 4;
+    while (R > 2 && (a.M + R - 1) / R < QGEMV_MIN_WAVES_PER_CU * cus) R >>= 1;
+    const int groups = (a.M + R - 1) / R;
+    const int wg_needed = (groups + kWaves - 1) / kWaves;
+    const int wg_per_cu = std::max(1, static_cast<int>(std::min<size_t>(QGEMV_MAX_WG_PER_CU, (160 * 1024) / lds)));
+    const int grid = std::max(1, std::min(wg_needed, cus * wg_per_cu));
+    if (lds > 64 * 1024) {
+      static bool once = [] {
+        allow_big_lds<FMT, 1, 2, true>(); allow_big_lds<FMT, 1, 4, true>();
+        allow_big_lds<FMT, 2, 2, true>(); allow_big_lds<FMT, 2, 4, true>();
+        allow_big_lds<FMT, 4, 2, true>(); allow_big_lds<FMT, 4, 4, true>();
+        allow_big_lds<FMT, 8, 2, true>(); allow_big_lds<FMT, 8, 4, true>();
+        return true;
+      }();
+      (void)once;
+    }
+    const uint8_t* W = static_cast<const uint8_t*>(a.W);
+#define QG_FUSED_LDS(NB_)                                                                          \
+    if (R == 2)                                                                                    \
+      gemv_kernel<FMT, NB_, 2, true><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch, f); \
+    else                                                                                           \
+      gemv_kernel<FMT, NB_, 4, true><<<grid, kThreads, lds, st>>>(W, a.scales, a.x, a.y, a.M, a.K, a.batch, f);
+    switch (nb) {
+      case 1: QG_FUSED_LDS(1) break;
+      case 2: QG_FUSED_LDS(2) break;
+      case 4: QG_FUSED_LDS(4) break;
+      default: QG_FUSED_LDS(8) break;
+    }
+#undef QG_FUSED_LDS
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && idx) e = launch_argmax(a.y, a.M, a.batch, slots, idx, st);
+  return e;
+}
+
+hipError_t launch_gemv_fused(const GemvArgs& a, const Fusion& f, uint64_t* slots, int32_t* idx,
+                             hipStream_t stream) {
+  switch (a.fmt) {
+    case QGEMV_BF16: return launch_fused_fmt<QGEMV_BF16>(a, f, slots, idx, stream);
+    case QGEMV_INT8_G32: return launch_fused_fmt<QGEMV_INT8_G32>(a, f, slots, idx, stream);
+    case QGEMV_Q4_0_G32: return launch_fused_fmt<QGEMV_Q4_0_G32>(a, f, slots, idx, stream);
+    default: return launch_fused_fmt<QGEMV_INT4_G128>(a, f, slots, idx, stream);
   }
 }
 

@@ -264,6 +264,42 @@ int qgemv_run(int fmt, const void* W, const uint16_t* scales, const uint16_t* x,
   return record_hip(qgemv::launch_gemv(a, static_cast<hipStream_t>(stream)));
 }
 
+int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+                    int64_t M, int64_t K, int batch, const qgemv_fusion* f, void* stream) {
+  if (!f) return QGEMV_EINVAL;
+  const bool norm = f->norm_input != nullptr;
+  const bool swiglu = f->swiglu_out != nullptr;
+  const bool am = f->argmax_idx != nullptr;
+  if (!valid_fmt(fmt) || !W || (fmt != QGEMV_BF16 && !scales)) return QGEMV_EINVAL;
+  if (norm == (x != nullptr)) return QGEMV_EINVAL;            // exactly one input
+  if (norm && (!f->norm_weight || !std::isfinite(f->norm_eps) || !(f->norm_eps >= 0.f))) return QGEMV_EINVAL;
+  if (swiglu && (y || f->residual || am)) return QGEMV_EINVAL;
+  if (!swiglu && !y) return QGEMV_EINVAL;
+  if (am != (f->argmax_ws != nullptr)) return QGEMV_EINVAL;
+  int st = check_shape(fmt, M, K);
+  if (st) return st;
+  if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
+  if (swiglu && (M % 2) != 0) return QGEMV_ESHAPE;
+  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch) &&
+      qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) + qgemv::kNormScratchBytes > 160 * 1024)
+    return QGEMV_ESHAPE;
+  if (!aligned(W, 16) || (fmt != QGEMV_BF16 && !aligned(scales, 4))) return QGEMV_EALIGN;
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16))) return QGEMV_EALIGN;
+  if (norm && (!aligned(f->norm_input, 16) || !aligned(f->norm_weight, 16))) return QGEMV_EALIGN;
+  if (f->residual && !aligned(f->residual, 16)) return QGEMV_EALIGN;
+  if (swiglu && !aligned(f->swiglu_out, 4)) return QGEMV_EALIGN;
+  if (am && (!aligned(f->argmax_ws, 8) || !aligned(f->argmax_idx, 4))) return QGEMV_EALIGN;
+  qgemv::Fusion fu;
+  fu.h = f->norm_input;
+  fu.g = f->norm_weight;
+  fu.eps = f->norm_eps;
+  fu.epi = swiglu ? qgemv::kEpiSwiglu : f->residual ? qgemv::kEpiResidual : qgemv::kEpiStore;
+  fu.res = f->residual;
+  fu.act = f->swiglu_out;
+  qgemv::GemvArgs a{fmt, W, scales, x, y, static_cast<int>(M), static_cast<int>(K), batch};
+  return record_hip(qgemv::launch_gemv_fused(a, fu, f->argmax_ws, f->argmax_idx, static_cast<hipStream_t>(stream)));
+}
+
 int qgemv_run_flags(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
                     int64_t M, int64_t K, int batch, int flags, void* stream) {
   if (flags & ~QGEMV_FLAG_BATCH_INVARIANT) return QGEMV_EINVAL;

@@ -33,6 +33,23 @@ struct GemvArgs {
   int batch;
 };
 
+// Operations fused into one GEMV (qgemv_run_fused): the RMSNorm prologue
+// (x = bf16(h / sqrt(mean(h^2) + eps) * g) when h is set) and one epilogue.
+constexpr int kEpiStore = 0;      // y = W x
+constexpr int kEpiResidual = 1;   // y = res + W x (res may be y)
+constexpr int kEpiSwiglu = 2;     // act[b][i] = bf16(silu(y[b][2i]) * y[b][2i+1]); y not written
+struct Fusion {
+  const float* h = nullptr;       // [batch][K] float32, or nullptr (x is the input)
+  const uint16_t* g = nullptr;    // [K] bf16 norm weight
+  float eps = 0.f;
+  int epi = kEpiStore;
+  const float* res = nullptr;     // [batch][M]
+  uint16_t* act = nullptr;        // [batch][M/2] bf16
+};
+
+// LDS the fused prologue adds to a workgroup that stages x in LDS.
+constexpr size_t kNormScratchBytes = 1024;
+
 // Bytes of LDS the GEMV kernel stages per workgroup for this shape
 // (x as bf16 for the compiled batch, plus per-unit x sums for 4-bit formats).
 size_t gemv_lds_bytes(int fmt, int K, int batch);
@@ -44,6 +61,12 @@ bool gemv_uses_lds(int fmt, int K, int batch);
 // Launch the GEMV on `stream` (flags: QGEMV_FLAG_*). Shapes have been
 // validated by the caller.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags = 0);
+
+// One GEMV with the operations of f fused in; idx != nullptr: also the
+// argmax of each row of y into idx (slots as for launch_gemv_group; not with
+// kEpiSwiglu). Shapes and pointers have been validated by the caller.
+hipError_t launch_gemv_fused(const GemvArgs& a, const Fusion& f, uint64_t* slots, int32_t* idx,
+                             hipStream_t stream);
 
 // Grouped launches of independent GEMVs (register-x kernel only).
 // gemv_group_class: 0 if (fmt, K, batch) needs another kernel, else the number

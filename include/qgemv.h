@@ -256,6 +256,58 @@ int qgemv_run_grouped_argmax(const qgemv_gemv_desc* gemvs, int n, int batch, int
                              uint64_t* ws, int32_t* idx, void* stream);
 
 /*
+ * Operations fused into one GEMV by qgemv_run_fused ("infer": the decode
+ * pipeline figure and design notes apply RMSNorm while the GEMV stages its
+ * input, add the residual in the GEMV's epilogue and compute SwiGLU from
+ * paired gate/up rows; the Rust page's layer walk-through names the same
+ * normalize / feed-forward steps). NULL fields are unused.
+ *
+ * norm_input  device float32 h[batch][K], 16-byte aligned: the GEMV's input
+ *             becomes x[b][k] = bf16(h[b][k] / sqrt(mean_k h[b][k]^2 + eps)
+ *             * norm_weight[k]) (round to nearest even; the call's x must be
+ *             NULL). Must not overlap y or swiglu_out.
+ * norm_weight device bf16 g[K], 16-byte aligned (required with norm_input).
+ * norm_eps    eps >= 0, finite.
+ * residual    device float32 [batch][M], 16-byte aligned: y = residual + W x
+ *             (one float32 add per output). May be y itself (the residual
+ *             stream updated in place); must not overlap it otherwise.
+ * swiglu_out  device bf16 act[batch][M/2], 4-byte aligned: with the gate|up
+ *             matrix storing gate row i as row 2i and up row i as row 2i+1,
+ *             act[b][i] = bf16(silu(y[b][2i]) * y[b][2i+1]), silu(t) =
+ *             t / (1 + exp(-t)); y itself is not written (the call's y must
+ *             be NULL), M must be even. Not with residual or the argmax.
+ * argmax_idx, argmax_ws  as idx and ws of qgemv_run_grouped_argmax for the
+ *             argmax of each row of y (fused into the launch at batch <= 2
+ *             with short rows, a separate launch otherwise).
+ */
+typedef struct qgemv_fusion {
+  const float* norm_input;
+  const uint16_t* norm_weight;
+  float norm_eps;
+  const float* residual;
+  uint16_t* swiglu_out;
+  int32_t* argmax_idx;
+  uint64_t* argmax_ws;
+} qgemv_fusion;
+
+/*
+ * qgemv_run_fused - qgemv_run with the operations of *fusion fused in: the
+ * RMSNorm prologue while x is staged, then one epilogue (plain store,
+ * residual add, or SwiGLU), optionally followed by the argmax of y. One
+ * launch (plus an argmax launch where it is not fused). x: bf16 [batch][K]
+ * or NULL with norm_input; y: float32 [batch][M] or NULL with swiglu_out.
+ * Errors: as qgemv_run; EINVAL for a null fusion, both or neither of x and
+ * norm_input, norm_input without norm_weight, a negative or non-finite eps,
+ * swiglu_out together with y, residual or the argmax, a missing y
+ * otherwise, or only one of argmax_idx / argmax_ws; ESHAPE for odd M with
+ * swiglu_out, or x of the batch plus 1 KiB of scratch not fitting in LDS
+ * where x is staged there; EALIGN for misaligned pointers. Nothing is
+ * launched on error.
+ */
+int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
+                    int64_t M, int64_t K, int batch, const qgemv_fusion* fusion, void* stream);
+
+/*
  * qgemv_stream_read - measurement helper: read `bytes` bytes of device
  * memory at `buf` once with 16-byte loads and write one checksum word per
  * workgroup to sink[0 .. grid-1] (so the reads cannot be elided). This is the

@@ -176,6 +176,36 @@ def test_run_flags_validation_errors_before_any_launch():
     assert _run_flags(qg.FLAG_BATCH_INVARIANT, fmt=qg.Q4_0_G32, K=9664, batch=1) == qg.ESHAPE
 
 
+def _fused(fmt=qg.Q4_0_G32, x=FAKE, y=FAKE, M=64, K=2048, batch=1, **kw):
+    f = qg.Fusion()
+    for k, v in kw.items():
+        setattr(f, k, v)
+    return qg.lib().qgemv_run_fused(fmt, FAKE, FAKE, x, y, M, K, batch, ctypes.byref(f), None)
+
+
+def test_run_fused_validation_errors_before_any_launch():
+    assert qg.lib().qgemv_run_fused(qg.Q4_0_G32, FAKE, FAKE, FAKE, FAKE, 64, 2048, 1, None, None) == qg.EINVAL
+    assert _fused(x=None) == qg.EINVAL                                  # no input at all
+    assert _fused(norm_input=FAKE, norm_weight=FAKE) == qg.EINVAL       # x and norm_input
+    assert _fused(x=None, norm_input=FAKE) == qg.EINVAL                 # no norm weight
+    assert _fused(x=None, norm_input=FAKE, norm_weight=FAKE, norm_eps=-1.0) == qg.EINVAL
+    assert _fused(x=None, norm_input=FAKE, norm_weight=FAKE, norm_eps=float("nan")) == qg.EINVAL
+    assert _fused(swiglu_out=FAKE) == qg.EINVAL                         # swiglu with y
+    assert _fused(y=None) == qg.EINVAL                                  # no output
+    assert _fused(y=None, swiglu_out=FAKE, residual=FAKE) == qg.EINVAL
+    assert _fused(y=None, swiglu_out=FAKE, argmax_idx=FAKE, argmax_ws=FAKE) == qg.EINVAL
+    assert _fused(argmax_idx=FAKE) == qg.EINVAL                         # idx without ws
+    assert _fused(y=None, swiglu_out=FAKE, M=63) == qg.ESHAPE           # odd M
+    assert _fused(batch=9) == qg.ESHAPE
+    assert _fused(K=48) == qg.ESHAPE
+    # x plus the prologue's scratch must fit in LDS where x is staged there
+    assert _fused(fmt=qg.BF16, batch=5, K=10240) == qg.ESHAPE
+    assert _fused(x=None, norm_input=FAKE + 4, norm_weight=FAKE) == qg.EALIGN
+    assert _fused(residual=FAKE + 4) == qg.EALIGN
+    assert _fused(y=None, swiglu_out=FAKE + 2) == qg.EALIGN
+    assert _fused(argmax_idx=FAKE, argmax_ws=FAKE + 4) == qg.EALIGN
+
+
 def test_run_validation_errors_before_any_launch():
     assert _run(fmt=7) == qg.EINVAL
     assert _run(W=None) == qg.EINVAL
