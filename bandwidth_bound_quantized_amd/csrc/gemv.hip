@@ -39,6 +39,7 @@
 // No MFMA: at batch <= 8 this is a matrix-vector product, not a dense
 // contraction.
 #include <algorithm>
+#include <type_traits>
 
 #include "argmax_key.h"
 #include "qgemv_internal.h"
@@ -434,46 +435,6 @@ constexpr int kWeightAux = 2;         // non-temporal
 constexpr int kWeightAux = 0;
 #endif
 
-// ---- RMSNorm prologue of the register-x kernel. A wave's lanes together
-// own every unit of a row, so the wave sees all of h: each lane sums the
-// squares of the h values its units pair with, the wave adds the lanes'
-// sums (in a fixed order, identical in every wave), and each lane then
-// writes its x registers as bf16(h * r * g) with r = 1 / sqrt(sum / K + eps).
-//
-// Dword (bf16 pair) p of the x values unit t pairs with (the order read_x uses).
-template <int FMT>
-__device__ __forceinline__ int x_dword(int t, int p) {
-  int lo, hi;
-  x_offsets<FMT>(t, lo, hi);
-  constexpr int P = Traits<FMT>::kPairs;
-  if constexpr (FMT == QGEMV_BF16) return lo + p;
-  else return p < P / 2 ? lo + p : hi + (p - P / 2);
-}
-
-template <int FMT>
-__device__ __forceinline__ float unit_sumsq(const float* __restrict__ hb, int t) {
-  float s = 0.f;
-#pragma unroll
-  for (int p = 0; p < Traits<FMT>::kPairs; ++p) {
-    const float2 v = *reinterpret_cast<const float2*>(hb + 2 * x_dword<FMT>(t, p));
-    s = __builtin_fmaf(v.x, v.x, s);
-    s = __builtin_fmaf(v.y, v.y, s);
-  }
-  return s;
-}
-
-template <int FMT>
-__device__ __forceinline__ void norm_x(const float* __restrict__ hb, const uint32_t* __restrict__ g, int t,
-                                       float r, uint32_t (&xv)[Traits<FMT>::kPairs]) {
-#pragma unroll
-  for (int p = 0; p < Traits<FMT>::kPairs; ++p) {
-    const int dw = x_dword<FMT>(t, p);
-    const float2 v = *reinterpret_cast<const float2*>(hb + 2 * dw);
-    const uint32_t gg = g[dw];
-    xv[p] = pack_bf16(v.x * r * bf16_lo(gg), v.y * r * bf16_hi(gg));
-  }
-}
-
 // Sum over the 64 lanes, the same value in every lane, in a fixed order.
 __device__ __forceinline__ float wave_sum(float x) {
   x = row_allreduce(x);
@@ -580,7 +541,8 @@ __device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __r
 template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
                                         int batch, int lane, AmLane& am, AmShared* am_sh,
-                                        uint64_t* am_slots, const Fusion& fu) {
+                                        uint64_t* am_slots, const Fusion& fu,
+                                        const uint32_t* xn = nullptr) {
   using T = Traits<FMT>;
   static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
   constexpr int P = T::kPairs;
@@ -608,27 +570,14 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       woff[c] = t * 16;
       soff[c] = T::kUnitsPerScale ? (t / T::kUnitsPerScale) * 2 : 0;
     }
+    // (fused prologue: x was normalized into LDS by the workgroup, xn)
+    const uint32_t* xsrc = reinterpret_cast<const uint32_t*>(e.X);
     if constexpr (FUSED) {
-      if (fu.h != nullptr) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float* hb = fu.h + static_cast<size_t>(min(b, batch - 1)) * e.K;
-          float ss = 0.f;
-#pragma unroll
-          for (int c = 0; c < NCH; ++c)
-            if (c * 64 + lane < U) ss += unit_sumsq<FMT>(hb, c * 64 + lane);
-          const float r = rms_factor(wave_sum(ss), e.K, fu.eps);
-#pragma unroll
-          for (int c = 0; c < NCH; ++c)
-            norm_x<FMT>(hb, reinterpret_cast<const uint32_t*>(fu.g), min(c * 64 + lane, U - 1), r, xr[b][c]);
-        }
-        return;
-      }
+      if (xn != nullptr) xsrc = xn;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint32_t* xb = reinterpret_cast<const uint32_t*>(e.X) +
-                           static_cast<size_t>(min(b, batch - 1)) * (e.K >> 1);
+      const uint32_t* xb = xsrc + static_cast<size_t>(min(b, batch - 1)) * (e.K >> 1);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) read_x<FMT>(xb, min(c * 64 + lane, U - 1), xr[b][c]);
     }
@@ -888,38 +837,6 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
 }
 
 
-// qgemv_run_fused at batch <= 2 with short rows: one GEMV of one (R, NCH)
-// with the RMSNorm prologue and the epilogue of fu, and with AM the argmax
-// of its output fused in as in the grouped launch (one kernel per shape, so
-// each shape gets its own register budget).
-template <int FMT, int NB, int R, int NCH, bool AM>
-__global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTable<1> tab, int batch,
-                                                                   uint64_t* __restrict__ slots,
-                                                                   int32_t* __restrict__ idx,
-                                                                   const Fusion fu) {
-  __shared__ AmShared am_sh;
-  __shared__ uint64_t red[kWaves];
-  if constexpr (AM) {
-    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
-    if (threadIdx.x == 0) am_sh.left = 0;
-    __syncthreads();
-  }
-  int stride;
-  int item = first_item(stride);
-  const int lane = threadIdx.x & 63;
-  AmLane am;
-  if (item < tab.total) {
-    int j = 0;
-    xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, &am_sh, slots, fu);
-  }
-  if constexpr (AM) {
-    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
-    __syncthreads();
-    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // Batch 3..8: matrix cores.
 //
@@ -1103,39 +1020,85 @@ static_assert((kNormFactorOff + QGEMV_MAX_BATCH) * 4 <= static_cast<int>(kNormSc
 
 // Block-wide RMSNorm factors of the fused prologue: scr[kNormFactorOff + b]
 // = 1 / sqrt(mean of h[b][:]^2 + eps) for b < batch (scr: kNormScratchBytes
-// of LDS): thread partials over k = 4t, 4t + 4 * threads, ..., then the
-// waves' sums in wave order. Ends with a barrier; every thread must call it.
+// of LDS). Thread t sums k = 4t, 4t + 4 * threads, ... of every batch row
+// (the loads of all rows issued together), the waves' sums are added in
+// wave order. Ends with a barrier; every thread must call it.
+template <int NB>
 __device__ __forceinline__ void block_rms_factors(const Fusion& fu, int K, int batch, float* scr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = static_cast<int>(blockDim.x >> 6);
-  for (int b = 0; b < batch; ++b) {
-    const float* hb = fu.h + static_cast<size_t>(b) * K;
-    float s = 0.f;
-    for (int k = 4 * tid; k < K; k += 4 * static_cast<int>(blockDim.x)) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(hb + k);
-      s = __builtin_fmaf(v.x, v.x, s);
-      s = __builtin_fmaf(v.y, v.y, s);
-      s = __builtin_fmaf(v.z, v.z, s);
-      s = __builtin_fmaf(v.w, v.w, s);
+  float s[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) s[b] = 0.f;
+  for (int k = 4 * tid; k < K; k += 4 * static_cast<int>(blockDim.x)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // rows past the batch re-read the last row (in bounds; not used)
+      const f32x4 v = *reinterpret_cast<const f32x4*>(fu.h + static_cast<size_t>(min(b, batch - 1)) * K + k);
+      s[b] = __builtin_fmaf(v.x, v.x, s[b]);
+      s[b] = __builtin_fmaf(v.y, v.y, s[b]);
+      s[b] = __builtin_fmaf(v.z, v.z, s[b]);
+      s[b] = __builtin_fmaf(v.w, v.w, s[b]);
     }
-    s = wave_sum(s);
-    if (lane == 0) scr[wave * QGEMV_MAX_BATCH + b] = s;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float t = wave_sum(s[b]);
+    if (lane == 0) scr[wave * QGEMV_MAX_BATCH + b] = t;
   }
   __syncthreads();
   if (tid < batch) {
-    float s = 0.f;
-    for (int w = 0; w < nw; ++w) s += scr[w * QGEMV_MAX_BATCH + tid];
-    scr[kNormFactorOff + tid] = rms_factor(s, K, fu.eps);
+    float t = 0.f;
+    for (int w = 0; w < nw; ++w) t += scr[w * QGEMV_MAX_BATCH + tid];
+    scr[kNormFactorOff + tid] = rms_factor(t, K, fu.eps);
   }
   __syncthreads();
 }
 
-// Four consecutive normalized inputs h[e..e+3] * r * g[e..e+3] as bf16 pairs.
-__device__ __forceinline__ u32x2 norm4(const float* __restrict__ h, const uint16_t* __restrict__ g, int e, float r) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(h + e);
-  const u32x2 gg = *reinterpret_cast<const u32x2*>(g + e);
-  return u32x2{pack_bf16(v.x * r * bf16_lo(gg.x), v.y * r * bf16_hi(gg.x)),
-               pack_bf16(v.z * r * bf16_lo(gg.y), v.w * r * bf16_hi(gg.y))};
+// The fused prologue for kernels that keep x rows contiguous: LDS
+// xs[b][0..K) = bf16(h[b][k] * r_b * g[k]) for b < NB (rows past the batch
+// zero), 8 elements per 16-byte chunk. Barriers inside; every thread must
+// call it.
+template <int NB>
+__device__ __forceinline__ void stage_norm_rows(const Fusion& fu, int K, int batch, uint32_t* xs, float* scr) {
+  block_rms_factors<NB>(fu, K, batch, scr);
+  const int row_chunks = K / 8, nxc = NB * row_chunks;
+  const int nt = static_cast<int>(blockDim.x);
+  // rounds of four chunks per thread (their loads issued together) while
+  // all four exist, then one chunk per round
+  int base = threadIdx.x;
+  auto round = [&](auto width) {
+    constexpr int kW = decltype(width)::value;
+    f32x4 h0[kW], h1[kW];
+    u32x4 gg[kW];
+    float r[kW];
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+      const int i = base + u * nt;
+      const int b = i / row_chunks, c = i - b * row_chunks;
+      const float* hr = fu.h + static_cast<size_t>(min(b, batch - 1)) * K + 8 * c;
+      h0[u] = *reinterpret_cast<const f32x4*>(hr);
+      h1[u] = *reinterpret_cast<const f32x4*>(hr + 4);
+      gg[u] = *reinterpret_cast<const u32x4*>(fu.g + 8 * c);
+      r[u] = b < batch ? scr[kNormFactorOff + b] : -1.f;      // -1: a row past the batch
+    }
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+      const int i = base + u * nt;
+      {
+        u32x4 v = {pack_bf16(h0[u].x * r[u] * bf16_lo(gg[u].x), h0[u].y * r[u] * bf16_hi(gg[u].x)),
+                         pack_bf16(h0[u].z * r[u] * bf16_lo(gg[u].y), h0[u].w * r[u] * bf16_hi(gg[u].y)),
+                         pack_bf16(h1[u].x * r[u] * bf16_lo(gg[u].z), h1[u].y * r[u] * bf16_hi(gg[u].z)),
+                         pack_bf16(h1[u].z * r[u] * bf16_lo(gg[u].w), h1[u].w * r[u] * bf16_hi(gg[u].w))};
+        if (r[u] < 0.f) v = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4*>(xs)[i] = v;
+      }
+    }
+    base += kW * nt;
+  };
+  while (base + 3 * nt < nxc) round(std::integral_constant<int, 4>{});
+  while (base < nxc) round(std::integral_constant<int, 1>{});
+  __syncthreads();
 }
 
 // Units [g0, g1) of one entry (the body of the matrix-core kernel).
@@ -1382,20 +1345,46 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
     if (fu.h != nullptr) {
       // RMSNorm prologue: the same slots, written from h and g
       float* scr = reinterpret_cast<float*>(red + (KS > 1 ? 2 * TW * KS * kOutLanes : 0));
-      block_rms_factors(fu, K, batch, scr);
+      block_rms_factors<NB>(fu, K, batch, scr);
       const int nslots = nchunk * NB * 4;
-      for (int sl = tid; sl < nslots; sl += static_cast<int>(blockDim.x)) {
-        const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (b < batch) {
-          const float* hr = fu.h + static_cast<size_t>(b) * K;
-          const float r = scr[kNormFactorOff + b];
-          const u32x2 lo = norm4(hr, fu.g, chunk_elem<FMT>(c, 8 * qq), r);
-          const u32x2 hi = norm4(hr, fu.g, chunk_elem<FMT>(c, 8 * qq + 4), r);
-          v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      const int nt = static_cast<int>(blockDim.x);
+      // rounds of four slots per thread (their loads issued together) while
+      // all four exist, then one slot per round; rows past the batch re-read
+      // the last row (in bounds) and store zero
+      int base = tid;
+      auto round = [&](auto width) {
+        constexpr int kW = decltype(width)::value;
+        f32x4 h0[kW], h1[kW];
+        u32x2 g0[kW], g1[kW];
+        float r[kW];
+#pragma unroll
+        for (int u = 0; u < kW; ++u) {
+          const int sl = base + u * nt;
+          const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
+          const float* hr = fu.h + static_cast<size_t>(min(b, batch - 1)) * K;
+          const int e0 = chunk_elem<FMT>(c, 8 * qq), e1 = chunk_elem<FMT>(c, 8 * qq + 4);
+          h0[u] = *reinterpret_cast<const f32x4*>(hr + e0);
+          h1[u] = *reinterpret_cast<const f32x4*>(hr + e1);
+          g0[u] = *reinterpret_cast<const u32x2*>(fu.g + e0);
+          g1[u] = *reinterpret_cast<const u32x2*>(fu.g + e1);
+          r[u] = b < batch ? scr[kNormFactorOff + b] : -1.f;  // -1: a row past the batch
         }
-        reinterpret_cast<u32x4*>(xs)[sl] = v;
-      }
+#pragma unroll
+        for (int u = 0; u < kW; ++u) {
+          const int sl = base + u * nt;
+          {
+            u32x4 v = {pack_bf16(h0[u].x * r[u] * bf16_lo(g0[u].x), h0[u].y * r[u] * bf16_hi(g0[u].x)),
+                             pack_bf16(h0[u].z * r[u] * bf16_lo(g0[u].y), h0[u].w * r[u] * bf16_hi(g0[u].y)),
+                             pack_bf16(h1[u].x * r[u] * bf16_lo(g1[u].x), h1[u].y * r[u] * bf16_hi(g1[u].x)),
+                             pack_bf16(h1[u].z * r[u] * bf16_lo(g1[u].y), h1[u].w * r[u] * bf16_hi(g1[u].y))};
+            if (r[u] < 0.f) v = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4*>(xs)[sl] = v;
+          }
+        }
+        base += kW * nt;
+      };
+      while (base + 3 * nt < nslots) round(std::integral_constant<int, 4>{});
+      while (base < nslots) round(std::integral_constant<int, 1>{});
       staged = true;
     }
   }
@@ -1468,6 +1457,49 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
     s = s2;
   }
 }
+
+// qgemv_run_fused at batch <= 2 with short rows: one GEMV of one (R, NCH)
+// with the RMSNorm prologue and the epilogue of fu, and with AM the argmax
+// of its output fused in as in the grouped launch (one kernel per shape, so
+// each shape gets its own register budget). With the prologue, the
+// workgroup first normalizes x once into LDS (dynamic LDS: NB * K bf16 +
+// kNormScratchBytes) and its waves read their x registers from there: done
+// per wave, every wave would read all of h and g again.
+template <int FMT, int NB, int R, int NCH, bool AM>
+__global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTable<1> tab, int batch,
+                                                                   uint64_t* __restrict__ slots,
+                                                                   int32_t* __restrict__ idx,
+                                                                   const Fusion fu) {
+  extern __shared__ u32x4 lds_v4[];
+  __shared__ AmShared am_sh;
+  __shared__ uint64_t red[kWaves];
+  const uint32_t* xn = nullptr;
+  if (fu.h != nullptr) {
+    uint32_t* xs = reinterpret_cast<uint32_t*>(lds_v4);
+    const int K = tab.e[0].K;
+    stage_norm_rows<NB>(fu, K, batch, xs, reinterpret_cast<float*>(xs + NB * (K >> 1)));
+    xn = xs;
+  }
+  if constexpr (AM) {
+    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
+    if (threadIdx.x == 0) am_sh.left = 0;
+    __syncthreads();
+  }
+  int stride;
+  int item = first_item(stride);
+  const int lane = threadIdx.x & 63;
+  AmLane am;
+  if (item < tab.total) {
+    int j = 0;
+    xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, &am_sh, slots, fu, xn);
+  }
+  if constexpr (AM) {
+    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
+    __syncthreads();
+    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
+  }
+}
+
 
 // The LDS dot2 kernel: x for all batch rows staged once per workgroup in
 // LDS, then the dot2 streaming loop over row groups of R rows. FUSED: the
@@ -1554,21 +1586,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       reinterpret_cast<u32x4*>(xs)[i] = (i < valid_xc) ? v : zero;
     }
   } else {
-    // RMSNorm prologue: x = bf16(h * r * g), 8 elements per 16-byte chunk
-    float* scr = reinterpret_cast<float*>(lds + NB * KD + (T::kBias ? NB * U : 0));
-    block_rms_factors(fu, K, batch, scr);
-    for (int i = tid; i < nxc; i += kThreads) {
-      const int b = i / row_chunks, c = i - b * row_chunks;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (b < batch) {
-        const float* hr = fu.h + static_cast<size_t>(b) * K;
-        const float r = scr[kNormFactorOff + b];
-        const u32x2 lo = norm4(hr, fu.g, 8 * c, r);
-        const u32x2 hi = norm4(hr, fu.g, 8 * c + 4, r);
-        v = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-      reinterpret_cast<u32x4*>(xs)[i] = v;
-    }
+    // RMSNorm prologue: x = bf16(h * r * g)
+    stage_norm_rows<NB>(fu, K, batch, xs, reinterpret_cast<float*>(lds + NB * KD + (T::kBias ? NB * U : 0)));
   }
   __syncthreads();
 
@@ -2059,16 +2078,20 @@ hipError_t launch_fused_xreg(const GemvArgs& a, const Fusion& f, uint64_t* slots
   tab.e[0] = TableEntry{static_cast<const uint8_t*>(a.W), a.scales, a.x, a.y, a.M, a.K, 0, xreg_shape(R, NCH)};
   const int cus = device_cu_count();
   int grid = (tab.total + kWaves - 1) / kWaves;
+  // LDS of the prologue (at most 2 rows x 8192 bf16 + scratch: under the
+  // default 64 KiB), which can also bound the workgroups per CU
+  const size_t lds = f.h ? static_cast<size_t>(NB) * a.K * 2 + kNormScratchBytes : 0;
+  const int lds_cap = lds ? static_cast<int>((160 * 1024) / lds) : 1 << 20;
   if (idx) {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_fused_kernel<FMT, NB, R, NCH, true>));
-    grid = std::max(1, std::min({grid, cus * per_cu, static_cast<int>(kFusedSlots)}));
-    gemv_xreg_fused_kernel<FMT, NB, R, NCH, true><<<grid, kThreads, 0, st>>>(tab, a.batch, slots, idx, f);
+    grid = std::max(1, std::min({grid, cus * std::min(per_cu, lds_cap), static_cast<int>(kFusedSlots)}));
+    gemv_xreg_fused_kernel<FMT, NB, R, NCH, true><<<grid, kThreads, lds, st>>>(tab, a.batch, slots, idx, f);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_fused_kernel<FMT, NB, R, NCH, false>));
-    grid = std::max(1, std::min(grid, cus * per_cu));
-    gemv_xreg_fused_kernel<FMT, NB, R, NCH, false><<<grid, kThreads, 0, st>>>(tab, a.batch, nullptr, nullptr, f);
+    grid = std::max(1, std::min(grid, cus * std::min(per_cu, lds_cap)));
+    gemv_xreg_fused_kernel<FMT, NB, R, NCH, false><<<grid, kThreads, lds, st>>>(tab, a.batch, nullptr, nullptr, f);
   }
   return hipGetLastError();
 }

@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--peak-gib", type=float, default=4.0)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--per-kernel", action="store_true", help="also time every GEMV of the step alone")
+    p.add_argument("--no-fused-layer", action="store_true",
+                   help="skip the fused decode-layer chain (workload 2)")
     p.add_argument("--pmc-pass", action="store_true",
                    help="only run calibration kernels (a 64 MiB streaming read, a 64 MiB fill) and "
                         "--steps eager steps, for hardware-counter collection")
@@ -193,6 +195,73 @@ class Workload:
         g = self.gemvs[j]
         wp, sp, xp, yp = self.ptrs[i % self.n_sets][0][j]
         self.qg.run_ptr(g.fmt, wp, sp, xp, yp, g.M, g.K, self.B, stream_handle)
+
+
+class FusedLayer:
+    """The decode-layer chain of the TinyLlama set with the fused prologue and
+    epilogues ("infer": pipeline figure): qkv = W_qkv RMSNorm(h); h += W_o attn;
+    act = SwiGLU(W_gate|up RMSNorm(h)); h += W_down act; logits = W_lm RMSNorm(h)
+    and their argmax: five dependent qgemv_run_fused launches. Uses the
+    workload's rotation sets (qkv, o, gate_up with gate/up rows paired, down,
+    lm_head); h is a float32 residual stream per set, updated in place."""
+
+    def __init__(self, qg, torch, wl):
+        assert [g.name for g in wl.gemvs] == ["qkv", "o", "gate_up", "down", "lm_head"]
+        self.qg, self.wl, self.B = qg, wl, wl.B
+        B, K = wl.B, wl.gemvs[0].K
+        rng = np.random.default_rng(77)
+        dev = "cuda"
+        self.norm_w = [torch.from_numpy(synth.round_f32_to_bf16_bits(
+            rng.uniform(0.5, 1.5, K).astype(np.float32)).view(np.int16)).to(dev) for _ in range(3)]
+        F = wl.gemvs[2].M // 2
+        self.bufs = []
+        for items, ws, idx in wl.sets:
+            h = torch.from_numpy(rng.standard_normal((B, K)).astype(np.float32)).to(dev)
+            act = torch.zeros((B, F), dtype=torch.int16, device=dev)
+            self.bufs.append((h, act))
+        torch.cuda.synchronize()
+        g = wl.gemvs
+        w = lambda j: sum(qg.packed_size(g[j].fmt, g[j].M, g[j].K))     # noqa: E731
+        self.bytes = (w(0) + 4 * B * K + 2 * K + 4 * B * g[0].M             # qkv: h, g in; y out
+                      + w(1) + 2 * B * g[1].K + 8 * B * g[1].M              # o: x in; h read + written
+                      + w(2) + 4 * B * K + 2 * K + 2 * B * F                # gate_up: h, g in; act out
+                      + w(3) + 2 * B * g[3].K + 8 * B * g[3].M              # down: act in; h read + written
+                      + w(4) + 4 * B * K + 2 * K + 4 * B * g[4].M + 4 * B)  # lm_head: h, g in; logits, idx
+        self.fusions = []
+        for (items, ws, idx), (h, act) in zip(wl.sets, self.bufs):
+            f = []
+            for kind in range(5):
+                fu = qg.Fusion()
+                if kind in (0, 2, 4):
+                    fu.norm_input = h.data_ptr()
+                    fu.norm_weight = self.norm_w[kind // 2].data_ptr()
+                    fu.norm_eps = 1e-5
+                if kind in (1, 3):
+                    fu.residual = h.data_ptr()
+                if kind == 2:
+                    fu.swiglu_out = act.data_ptr()
+                if kind == 4:
+                    fu.argmax_idx = idx.data_ptr()
+                    fu.argmax_ws = ws.data_ptr()
+                f.append(fu)
+            self.fusions.append(f)
+
+    NAMES = ["qkv+norm", "o+residual", "gate_up+norm+swiglu", "down+residual", "lm_head+norm+argmax"]
+
+    def op(self, k, i, stream_handle):
+        """Launch op k (0..4) of the chain on rotation set i."""
+        qg, wl, B = self.qg, self.wl, self.B
+        s = i % wl.n_sets
+        wp, sp, xp, yp = wl.ptrs[s][0][k]
+        h, act = self.bufs[s]
+        g = wl.gemvs[k]
+        x = {1: xp, 3: act.data_ptr()}.get(k)
+        y = {0: yp, 1: h.data_ptr(), 3: h.data_ptr(), 4: yp}.get(k)
+        qg.run_fused_ptr(g.fmt, wp, sp, x, y, g.M, g.K, B, self.fusions[s][k], stream_handle)
+
+    def step(self, i, stream_handle):
+        for k in range(5):
+            self.op(k, i, stream_handle)
 
 
 def capture(torch, fn, count):
@@ -372,6 +441,37 @@ def main():
         print(f"[bench] {mode}: {ms * 1e3:.2f} us/step, {nb / (ms * 1e-3) / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
         del g_warm, g_steps
+    fused_layer = None
+    if cfg == 2 and not args.no_fused_layer:
+        fl = FusedLayer(qg, torch, wl)
+        g_warm = capture(torch, fl.step, max(1, args.warmup))
+        time_graph(torch, g_warm)
+        g_steps = capture(torch, fl.step, args.steps)
+        ms_fl = time_graph(torch, g_steps) / args.steps
+        del g_warm, g_steps
+        per_op = []
+        if args.per_kernel:
+            for k in range(5):
+                n = max(wl.n_sets * 4, 64)
+                gk = capture(torch, lambda i, h, k=k: fl.op(k, i, h), n)
+                time_graph(torch, gk)
+                us = time_graph(torch, gk, reps=3) * 1e3 / n
+                gp = capture(torch, lambda i, h, k=k: wl.launch_one(k, i, h), n)
+                time_graph(torch, gp)
+                us_p = time_graph(torch, gp, reps=3) * 1e3 / n
+                per_op.append({"op": FusedLayer.NAMES[k], "fused_us": round(us, 3), "plain_gemv_us": round(us_p, 3)})
+                del gk, gp
+        fused_layer = {
+            "chain": "qkv(RMSNorm) -> o(+=residual) -> gate_up(RMSNorm, SwiGLU of paired rows) -> "
+                     "down(+=residual) -> lm_head(RMSNorm, argmax): 5 dependent qgemv_run_fused launches",
+            "us_per_step": round(ms_fl * 1e3, 3), "bytes_per_step": fl.bytes,
+            "GBps": round(fl.bytes / (ms_fl * 1e-3) / 1e9, 1),
+            "plain_sequential_us_per_step": round(results["sequential"] * 1e3, 3),
+            "plain_sequential_launches": len(wl.gemvs) + 1}
+        if per_op:
+            fused_layer["per_op"] = per_op
+        print(f"[bench] fused layer chain: {ms_fl * 1e3:.2f} us/step, {fused_layer['GBps']} GB/s",
+              file=sys.stderr, flush=True)
     ms_per_step = results["fused"] if wl.has_argmax else results["grouped"]
     value = (wl.fused_bytes if wl.has_argmax else wl.step_bytes) / (ms_per_step * 1e-3) / 1e9
     value_seq = wl.step_bytes / (results["sequential"] * 1e-3) / 1e9
@@ -471,6 +571,8 @@ def main():
         out["roofline"]["pct_of_measured_peak"] = round(100 * dom_gbps / peak["GBps"], 2)
     if per_kernel:
         out["per_kernel"] = per_kernel
+    if fused_layer is not None:
+        out["fused_layer"] = fused_layer
     print(json.dumps(out), flush=True)
 
 
