@@ -29,12 +29,14 @@ exact rational brute force, quantizer error bounds, torch's rms_norm and
 silu, closed-form normalizations and activations); there is no unpinned
 function.
 """
-from .formats import (BF16, INT8_G32, Q4_0_G32, INT4_G128, GROUP, bf16_to_f64, f16_to_f64,
+from .formats import (BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64, GROUP, K_ALIGN,
+                      scales_per_row, bf16_to_f64, f16_to_f64,
                       f64_to_f16_bits, dequantize)
 from .gemv import gemv_ref, check_parity, parity_report
 from .quantize import quantize_from_bf16
 from .argmax import argmax_ref
 
-__all__ = ["BF16", "INT8_G32", "Q4_0_G32", "INT4_G128", "GROUP", "bf16_to_f64", "f16_to_f64",
+__all__ = ["BF16", "INT8_G32", "Q4_0_G32", "INT4_G128", "INT8_ROW", "INT4_G64", "GROUP", "K_ALIGN",
+           "scales_per_row", "bf16_to_f64", "f16_to_f64",
            "f64_to_f16_bits", "dequantize", "gemv_ref", "check_parity", "parity_report",
            "quantize_from_bf16", "argmax_ref"]

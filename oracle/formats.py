@@ -25,13 +25,32 @@ Formats (all planar: codes in one array, scales in another, row-major):
   The pages do not give its nibble order; this oracle takes the same
   half-split as Q4_0: element j in the low nibble of byte j, element j + 64
   in the high nibble.
+* int4-g64: the same value rule with one scale per 64 weights, 32 code bytes
+  per block ("infer", the g64 row of the perplexity table), the same
+  half-split: element j in the low nibble of byte j, element j + 32 in the
+  high nibble.
+* int8-row: one signed 8-bit code per weight and one binary16 scale per row;
+  weight = code * scale ("infer": its int8 weights carry one scale per row,
+  perplexity table and its notes). The pages do not give the scale's type;
+  binary16, like every other scale here.
 """
 from __future__ import annotations
 
 import numpy as np
 
-BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
-GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
+BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64 = 0, 1, 2, 3, 4, 5
+# weights per scale; 0: one scale per row (int8-row)
+GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128, INT8_ROW: 0, INT4_G64: 64}
+# K must be a multiple of this
+K_ALIGN = {BF16: 32, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128, INT8_ROW: 32, INT4_G64: 64}
+NIBBLE_FORMATS = (Q4_0_G32, INT4_G128, INT4_G64)
+
+
+def scales_per_row(fmt: int, K: int) -> int:
+    """Number of scales of one row (0 for bf16)."""
+    if fmt == BF16:
+        return 0
+    return 1 if GROUP[fmt] == 0 else K // GROUP[fmt]
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -118,14 +137,18 @@ def dequantize(fmt: int, w: np.ndarray, s, K: int) -> np.ndarray:
 
     bf16: W_hat = value of the bf16 bits.
     int8-g32: W_hat[m, k] = q[m, k] * d[m, k // 32].
-    Q4_0-g32 / int4-g128: W_hat[m, k] = (q[m, k] - 8) * d[m, k // G].
+    int8-row: W_hat[m, k] = q[m, k] * d[m].
+    Q4_0-g32 / int4-g128 / int4-g64: W_hat[m, k] = (q[m, k] - 8) * d[m, k // G].
     Every product is exact in float64 (at most 8 + 11 significant bits).
     """
     if fmt == BF16:
         return bf16_to_f64(w).reshape(-1, K)
-    G = GROUP[fmt]
     d = f16_to_f64(s)
     M = d.shape[0]
+    if fmt == INT8_ROW:
+        q = np.asarray(w, dtype=np.int8).astype(np.int64).reshape(M, K)
+        return q.astype(np.float64) * d.reshape(M, 1)
+    G = GROUP[fmt]
     if fmt == INT8_G32:
         q = np.asarray(w, dtype=np.int8).astype(np.int64).reshape(M, K)
     else:

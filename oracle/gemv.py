@@ -19,7 +19,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-from .formats import GROUP, BF16, bf16_to_f64, dequantize
+from .formats import GROUP, BF16, INT8_G32, INT8_ROW, bf16_to_f64, dequantize, scales_per_row
 
 REL_TOL = 1e-3
 ABS_TOL = 1e-5
@@ -27,14 +27,14 @@ ABS_TOL = 1e-5
 
 def _row_slice(fmt: int, w: np.ndarray, s, M: int, K: int, rows: np.ndarray):
     """Select whole rows of the planar code and scale arrays."""
-    G = GROUP[fmt]
     if fmt == BF16:
         return np.asarray(w).reshape(M, K)[rows], None
-    if fmt == 1:  # int8-g32: one code per weight
+    if fmt in (INT8_G32, INT8_ROW):  # one code per weight
         wr = np.asarray(w).reshape(M, K)[rows]
     else:
+        G = GROUP[fmt]
         wr = np.asarray(w).reshape(M, K // G, G // 2)[rows]
-    sr = np.asarray(s).reshape(M, K // G)[rows]
+    sr = np.asarray(s).reshape(M, scales_per_row(fmt, K))[rows]
     return wr, sr
 
 

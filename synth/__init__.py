@@ -31,10 +31,21 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 # format ids, mirrored from the C header on purpose: these are names, not math
-BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
-FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128"}
+BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64 = 0, 1, 2, 3, 4, 5
+FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128",
+             INT8_ROW: "int8_row", INT4_G64: "int4_g64"}
 FMT_BY_NAME = {v: k for k, v in FMT_NAMES.items()}
-GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
+# weights per scale (0: one scale per row); K must be a multiple of K_ALIGN
+GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128, INT8_ROW: 0, INT4_G64: 64}
+K_ALIGN = {BF16: 32, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128, INT8_ROW: 32, INT4_G64: 64}
+ALL_FORMATS = (BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64)
+
+
+def scale_shape(fmt: int, M: int, K: int):
+    """Shape of the planar scale array (None for bf16)."""
+    if fmt == BF16:
+        return None
+    return (M,) if GROUP[fmt] == 0 else (M, K // GROUP[fmt])
 
 PROJ = {"qkv": 0, "o": 1, "gate_up": 2, "down": 3, "lm_head": 4}
 T_W, T_S, T_X = 0, 1, 2
@@ -89,7 +100,8 @@ class Gemv:
     seeds: Tuple[int, int, int]
 
 
-SCALE_RANGE = {INT8_G32: (1e-4, 4e-4), Q4_0_G32: (0.001, 0.005), INT4_G128: (0.001, 0.005)}
+SCALE_RANGE = {INT8_G32: (1e-4, 4e-4), Q4_0_G32: (0.001, 0.005), INT4_G128: (0.001, 0.005),
+               INT8_ROW: (1e-4, 4e-4), INT4_G64: (0.001, 0.005)}
 
 
 def make_gemv(name: str, fmt: int, M: int, K: int, B: int, cfg: int, layer: int, proj: str,
@@ -100,9 +112,9 @@ def make_gemv(name: str, fmt: int, M: int, K: int, B: int, cfg: int, layer: int,
     if fmt == BF16:
         w = bf16_normal(rw, (M, K), w_std)
         s = None
-    elif fmt == INT8_G32:
+    elif fmt in (INT8_G32, INT8_ROW):
         w = int8_uniform(rw, (M, K))
-        s = f16_uniform(rs, (M, K // G), *SCALE_RANGE[fmt])
+        s = f16_uniform(rs, scale_shape(fmt, M, K), *SCALE_RANGE[fmt])
     else:
         w = random_bytes(rw, (M, K // G, G // 2))
         s = f16_uniform(rs, (M, K // G), *SCALE_RANGE[fmt])
@@ -148,6 +160,9 @@ def workload_specs(cfg: int) -> List[Spec]:
         return [Spec("gate_up", INT4_G128, 16384, 2048, 5, 0, "gate_up"),
                 Spec("down", INT4_G128, 2048, 8192, 5, 0, "down"),
                 Spec("lm_head", INT8_G32, 128256, 2048, 5, 0, "lm_head")]
+    if cfg == 6:
+        return ([Spec(p, Q4_0_G32, m, k, 6, 0, p) for p, m, k in LLAMA32_1B] +
+                [Spec("lm_head", INT8_ROW, 128256, 2048, 6, 999, "lm_head")])
     raise ValueError(f"unknown workload {cfg}")
 
 
@@ -157,10 +172,11 @@ WORKLOAD_NAMES = {
     3: "int8-g32 GEMV set, Llama-3.2-1B decode shapes",
     4: "Q4_0-g32 TinyLlama-1.1B decode-step weight stream (89 GEMVs) + argmax",
     5: "int4-g128 FFN + int8-g32 LM head (Llama-3.2-1B shapes) + argmax",
+    6: "int4-g32 (Q4_0) Llama-3.2-1B layer GEMVs + int8 per-row LM head + argmax",
 }
-WORKLOAD_BATCHES = {1: [1], 2: [1], 3: [1], 4: [1, 2, 4, 8], 5: [1, 8]}
+WORKLOAD_BATCHES = {1: [1], 2: [1], 3: [1], 4: [1, 2, 4, 8], 5: [1, 8], 6: [1, 8]}
 # workloads whose last GEMV is an LM head followed by argmax over its logits
-WORKLOAD_ARGMAX = {1: False, 2: True, 3: False, 4: True, 5: True}
+WORKLOAD_ARGMAX = {1: False, 2: True, 3: False, 4: True, 5: True, 6: True}
 
 
 def make_workload(cfg: int, B: int) -> List[Gemv]:

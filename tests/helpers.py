@@ -35,7 +35,7 @@ def build_case(case):
         w = np.zeros((M, K), dtype=np.uint16)
         for r, row in enumerate(wspec["rows_bf16"]):
             w[r, :len(row)] = [_hex16(v) for v in row]
-    elif fmt == synth.INT8_G32:
+    elif fmt in (synth.INT8_G32, synth.INT8_ROW):
         w = np.zeros((M, K), dtype=np.int8)
         if "fill" in wspec:
             w[:] = wspec["fill"]
@@ -60,6 +60,8 @@ def build_case(case):
     s = None
     if case["s"] is not None:
         s = np.array([[_hex16(v) for v in row] for row in case["s"]], dtype=np.uint16)
+        if fmt == synth.INT8_ROW:
+            s = s.reshape(M)
     xspec = case["x"]
     if "fill_bf16" in xspec:
         x = np.array([[_hex16(xspec["fill_bf16"][0])] * K], dtype=np.uint16)

@@ -27,7 +27,7 @@ import oracle.quantize as oquant
 import synth
 from helpers import build_case, load_json
 
-FMTS_Q = [synth.INT8_G32, synth.Q4_0_G32, synth.INT4_G128]
+FMTS_Q = [synth.INT8_G32, synth.Q4_0_G32, synth.INT4_G128, synth.INT8_ROW, synth.INT4_G64]
 ALL_FMTS = [synth.BF16] + FMTS_Q
 
 
@@ -94,6 +94,8 @@ def _brute_weight(fmt, w, s, m, k, K):
     """One weight as an exact rational, indexed element by element."""
     if fmt == synth.BF16:
         return _frac_bf16(w[m, k])
+    if fmt == synth.INT8_ROW:
+        return int(w[m, k]) * _frac_f16(s[m])
     G = synth.GROUP[fmt]
     d = _frac_f16(s[m, k // G])
     if fmt == synth.INT8_G32:
@@ -140,13 +142,13 @@ def _quant_bounds_ok(fmt, w_bits, M, K) -> bool:
     (clamped from 8 to 7): <= |d| (1 + 2^-8); the group's largest-magnitude
     element m gets code 0 and reconstructs within |m| 2^-11. Valid for normal d.
     """
-    G = synth.GROUP[fmt]
+    G = synth.GROUP[fmt] or K                    # int8-row: the whole row
     codes, d_bits = oracle.quantize_from_bf16(fmt, w_bits, M, K)
     w = oracle.bf16_to_f64(w_bits).reshape(M, K)
     w_hat = oracle.dequantize(fmt, codes, d_bits, K)
     d = np.repeat(np.abs(oracle.f16_to_f64(d_bits)).reshape(M, K // G), G, axis=1)
     err = np.abs(w - w_hat)
-    if fmt == synth.INT8_G32:
+    if fmt in (synth.INT8_G32, synth.INT8_ROW):
         return bool((err <= d / 2).all())
     q = oformats.decode_nibble_blocks(codes.reshape(M, K // G, G // 2), G)
     ok_regular = (err <= d / 2) | ((q == 15) & (err <= d * (1 + 2 ** -8)))
@@ -190,8 +192,9 @@ def test_quantize_positive_max_maps_to_minus8():
 def test_quantize_special_groups():
     K = 32
     z = np.zeros((1, K), dtype=np.uint16)
-    for fmt, zero_code in ((synth.Q4_0_G32, 0x88), (synth.INT8_G32, 0)):
-        codes, d_bits = oracle.quantize_from_bf16(fmt, z, 1, K)
+    for fmt, zero_code in ((synth.Q4_0_G32, 0x88), (synth.INT8_G32, 0), (synth.INT4_G64, 0x88),
+                           (synth.INT8_ROW, 0)):
+        codes, d_bits = oracle.quantize_from_bf16(fmt, np.zeros((1, 64), dtype=np.uint16), 1, 64)
         assert (d_bits == 0).all()
         assert (codes.view(np.uint8) == np.uint8(zero_code)).all()
     # tie in |w| between +a and -a: the first in index order sets the sign of d
@@ -303,7 +306,7 @@ def _wrap_dequant(offset=0, roll_scales=False, neg=False):
         if roll_scales and s is not None:
             s = np.roll(np.asarray(s), 1, axis=-1)
         out = orig(fmt, w, s, K)
-        if fmt in (synth.Q4_0_G32, synth.INT4_G128) and offset:
+        if fmt in (synth.Q4_0_G32, synth.INT4_G128, synth.INT4_G64) and offset:
             G = synth.GROUP[fmt]
             d = np.repeat(oformats.f16_to_f64(s).reshape(out.shape[0], K // G), G, axis=1)
             out = out + offset * d
@@ -333,7 +336,7 @@ def _mut_f16_double(bits):
 def _mut_quant_amax8(fmt, w_bits, M, K):
     """The unsigned largest-|w|/8 scale, which clips positive maxima to +7."""
     G = synth.GROUP[fmt]
-    if fmt == synth.INT8_G32:
+    if fmt in (synth.INT8_G32, synth.INT8_ROW):
         return _orig_quant(fmt, w_bits, M, K)
     w = oformats.bf16_to_f64(np.asarray(w_bits).reshape(M, K)).reshape(M, K // G, G)
     d_bits = oformats.f64_to_f16_bits(np.abs(w).max(axis=2) / 8.0)
