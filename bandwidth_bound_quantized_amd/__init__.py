@@ -21,15 +21,16 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
-BF16, INT8_G32, Q4_0_G32, INT4_G128 = 0, 1, 2, 3
+BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64 = 0, 1, 2, 3, 4, 5
 SRC_CANONICAL, SRC_BF16 = 0, 1
 OK, EINVAL, ESHAPE, EALIGN, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
 MAX_BATCH = 8
 FLAG_BATCH_INVARIANT = 1
 ARGMAX_WS_WORDS_PER_ROW = 2
 FUSED_ARGMAX_WS_WORDS_PER_ROW = 4096
-GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128}
-FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128"}
+GROUP = {BF16: 1, INT8_G32: 32, Q4_0_G32: 32, INT4_G128: 128, INT8_ROW: 0, INT4_G64: 64}   # 0: per row
+FMT_NAMES = {BF16: "bf16", INT8_G32: "int8_g32", Q4_0_G32: "q4_0_g32", INT4_G128: "int4_g128",
+             INT8_ROW: "int8_row", INT4_G64: "int4_g64"}
 
 
 class QgemvError(RuntimeError):
@@ -262,7 +263,7 @@ def grouped_descs(entries) -> "ctypes.Array":
     return arr
 
 
-ELEMS_PER_UNIT = {BF16: 8, INT8_G32: 16, Q4_0_G32: 32, INT4_G128: 32}
+ELEMS_PER_UNIT = {BF16: 8, INT8_G32: 16, Q4_0_G32: 32, INT4_G128: 32, INT8_ROW: 16, INT4_G64: 32}
 
 
 def group_class(fmt: int, K: int, batch: int) -> int:

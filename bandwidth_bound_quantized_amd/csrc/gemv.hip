@@ -96,6 +96,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// f(std::integral_constant<int, FMT>{}) for the runtime format (validated by
+// the caller)
+template <typename F>
+auto with_fmt(int fmt, F&& f) {
+  switch (fmt) {
+    case QGEMV_BF16: return f(std::integral_constant<int, QGEMV_BF16>{});
+    case QGEMV_INT8_G32: return f(std::integral_constant<int, QGEMV_INT8_G32>{});
+    case QGEMV_Q4_0_G32: return f(std::integral_constant<int, QGEMV_Q4_0_G32>{});
+    case QGEMV_INT4_G128: return f(std::integral_constant<int, QGEMV_INT4_G128>{});
+    case QGEMV_INT8_ROW: return f(std::integral_constant<int, QGEMV_INT8_ROW>{});
+    default: return f(std::integral_constant<int, QGEMV_INT4_G64>{});
+  }
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -149,7 +163,7 @@ template <int FMT> struct Traits;
 template <> struct Traits<QGEMV_BF16> {
   static constexpr int kElems = 8;      // weights per 16-byte unit
   static constexpr int kPairs = 4;      // bf16 pairs per unit (= x dwords per unit)
-  static constexpr int kUnitsPerScale = 0;
+  static constexpr int kUnitsPerScale = 0;  // no scales (-1: one per row; else units per group)
   static constexpr int kUC = 4;         // units per lane per step
   static constexpr bool kBias = false;
 };
@@ -174,6 +188,35 @@ template <> struct Traits<QGEMV_INT4_G128> {
   static constexpr int kUC = 1;
   static constexpr bool kBias = true;
 };
+template <> struct Traits<QGEMV_INT8_ROW> {
+  static constexpr int kElems = 16;
+  static constexpr int kPairs = 8;
+  static constexpr int kUnitsPerScale = -1;  // one scale per row
+  static constexpr int kUC = 2;
+  static constexpr bool kBias = false;
+};
+template <> struct Traits<QGEMV_INT4_G64> {
+  static constexpr int kElems = 32;
+  static constexpr int kPairs = 16;
+  static constexpr int kUnitsPerScale = 2;
+  static constexpr int kUC = 1;
+  static constexpr bool kBias = true;
+};
+
+constexpr bool is_int8_fmt(int f) { return f == QGEMV_INT8_G32 || f == QGEMV_INT8_ROW; }
+
+// Scales of one row of U units, and the scale of unit t (kUnitsPerScale:
+// 0 none, -1 one per row, else units per scale group).
+template <int FMT>
+__device__ __forceinline__ int scales_per_row(int U) {
+  constexpr int k = Traits<FMT>::kUnitsPerScale;
+  return k > 0 ? U / k : (k < 0 ? 1 : 0);
+}
+template <int FMT>
+__device__ __forceinline__ int scale_index(int t) {
+  constexpr int k = Traits<FMT>::kUnitsPerScale;
+  return k > 0 ? t / k : 0;
+}
 
 // Dword offset (within one batch row of x, stored as bf16 pairs) of the x
 // values that pair with the first and the second half of unit t's pairs.
@@ -181,11 +224,15 @@ template <int FMT>
 __device__ __forceinline__ void x_offsets(int t, int& lo, int& hi) {
   if constexpr (FMT == QGEMV_BF16) {
     lo = 4 * t; hi = lo;
-  } else if constexpr (FMT == QGEMV_INT8_G32) {
+  } else if constexpr (is_int8_fmt(FMT)) {
     lo = 8 * t; hi = lo + 4;
   } else if constexpr (FMT == QGEMV_Q4_0_G32) {
     // block t: low nibbles are elements 32t..32t+15, high nibbles 32t+16..32t+31
     lo = 16 * t; hi = lo + 8;
+  } else if constexpr (FMT == QGEMV_INT4_G64) {
+    // block t>>1, half c = t&1: low nibbles are elements 64(t>>1)+16c..+15,
+    // high nibbles the same positions + 32
+    lo = 32 * (t >> 1) + 8 * (t & 1); hi = lo + 16;
   } else {
     // block t>>2, quarter c = t&3: low nibbles are elements 128(t>>2)+16c..+15,
     // high nibbles the same positions + 64
@@ -201,7 +248,7 @@ __device__ __forceinline__ void read_x(const uint32_t* xb, int t, uint32_t (&xv)
   if constexpr (FMT == QGEMV_BF16) {
     u32x4 a = *reinterpret_cast<const u32x4*>(xb + lo);
     xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-  } else if constexpr (FMT == QGEMV_INT8_G32) {
+  } else if constexpr (is_int8_fmt(FMT)) {
     u32x4 a = *reinterpret_cast<const u32x4*>(xb + lo);
     u32x4 b = *reinterpret_cast<const u32x4*>(xb + hi);
     xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
@@ -226,7 +273,7 @@ __device__ __forceinline__ void unpack(const u32x4& w, uint32_t (&p)[Traits<FMT>
   if constexpr (FMT == QGEMV_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = wd[i];
-  } else if constexpr (FMT == QGEMV_INT8_G32) {
+  } else if constexpr (is_int8_fmt(FMT)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // sign-extended bytes -> float32 (exact); a float32 holding an integer of
@@ -563,12 +610,12 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     next_start = (N > 1 && jj + 1 < tab.n) ? tab.e[jj + 1].start : tab.total;
     U = e.K / T::kElems;
     row_bytes = U * 16;
-    nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
+    nsc = scales_per_row<FMT>(U);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int t = min(c * 64 + lane, U - 1);
       woff[c] = t * 16;
-      soff[c] = T::kUnitsPerScale ? (t / T::kUnitsPerScale) * 2 : 0;
+      soff[c] = scale_index<FMT>(t) * 2;
     }
     // (fused prologue: x was normalized into LDS by the workgroup, xn)
     const uint32_t* xsrc = reinterpret_cast<const uint32_t*>(e.X);
@@ -599,7 +646,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         wv[r][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[c] + r * row_bytes, 0, kWeightAux));
-    if constexpr (T::kUnitsPerScale > 0) {
+    if constexpr (T::kUnitsPerScale != 0) {
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(S + static_cast<size_t>(row0) * nsc, static_cast<uint32_t>(rows * nsc * 2));
 #pragma unroll
@@ -922,6 +969,22 @@ template <> struct MfmaFmt<QGEMV_INT4_G128> {
   static constexpr int kChunksPerGroup = 4;
   static constexpr int kStepElems = 128 * kSlices;
 };
+// int8-row: no group scales inside a step; the row's scale multiplies the
+// finished dot product in the store
+template <> struct MfmaFmt<QGEMV_INT8_ROW> {
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT8;
+  static constexpr int kChunksPerSlice = 2;
+  static constexpr int kGroups = 0;
+  static constexpr int kChunksPerGroup = 0;
+  static constexpr int kStepElems = 64 * kSlices;
+};
+template <> struct MfmaFmt<QGEMV_INT4_G64> {
+  static constexpr int kSlices = QGEMV_MFMA_SLICES_Q4;
+  static constexpr int kChunksPerSlice = 4;
+  static constexpr int kGroups = 2 * kSlices;
+  static constexpr int kChunksPerGroup = 2;
+  static constexpr int kStepElems = 128 * kSlices;
+};
 
 // K element at position pos (0..31) of chunk c; position pos = 8q + 4h + j
 // is the j-th code of half h of lane row q after the exchange.
@@ -934,12 +997,16 @@ template <> struct MfmaFmt<QGEMV_INT4_G128> {
 //   int4-g128: slice = 1 group of 128; lane row q of chunk c holds byte
 //           dword q of the group's quarter c: elements 16c+4q.. (low) and
 //           64+16c+4q.. (high).
+//   int4-g64: slice = 2 groups of 64; chunk c is half c&1 of group c>>1:
+//           elements 16(c&1)+4q.. (low) and 32+16(c&1)+4q.. (high).
+//   int8-row: as int8-g32.
 template <int FMT>
 __device__ __forceinline__ int chunk_elem(int c, int pos) {
   const int q = pos >> 3, h = (pos >> 2) & 1, j = pos & 3;
   if constexpr (FMT == QGEMV_BF16) return 32 * c + pos;
-  else if constexpr (FMT == QGEMV_INT8_G32) return 32 * c + 16 * (q & 1) + 8 * (q >> 1) + 4 * h + j;
+  else if constexpr (is_int8_fmt(FMT)) return 32 * c + 16 * (q & 1) + 8 * (q >> 1) + 4 * h + j;
   else if constexpr (FMT == QGEMV_Q4_0_G32) return 32 * c + 16 * h + 4 * q + j;
+  else if constexpr (FMT == QGEMV_INT4_G64) return 64 * (c >> 1) + 32 * h + 16 * (c & 1) + 4 * q + j;
   else return 128 * (c >> 2) + 64 * h + 16 * (c & 3) + 4 * q + j;
 }
 
@@ -1133,8 +1200,8 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
   const int nsteps = K / F::kStepElems;
   const int Lw = nsteps / KS;                          // steps per wave per tile
   const uint32_t row_bytes = static_cast<uint32_t>(
-      FMT == QGEMV_BF16 ? 2 * K : FMT == QGEMV_INT8_G32 ? K : K / 2);
-  constexpr bool kBiasSums = F::kChunksPerGroup > 0 && FMT != QGEMV_INT8_G32;   // 4-bit formats
+      FMT == QGEMV_BF16 ? 2 * K : is_int8_fmt(FMT) ? K : K / 2);
+  constexpr bool kBiasSums = F::kChunksPerGroup > 0 && !is_int8_fmt(FMT);   // 4-bit formats
   // LDS: x [nchunk][NB][32] bf16 | group sums [ngroups][NB] (4-bit) | partial tiles
   float* sneg = reinterpret_cast<float*>(xs + static_cast<size_t>(nchunk) * NB * 32);
   f32x4* red = reinterpret_cast<f32x4*>(sneg + (kBiasSums ? ngroups * NB : 0));
@@ -1202,7 +1269,7 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // per step: one D tile per scale group (all of them issued before any is scaled)
-  constexpr int kDch = FMT == QGEMV_BF16 ? 1 : F::kGroups;
+  constexpr int kDch = F::kGroups > 0 ? F::kGroups : 1;
   auto compute = [&](const u32x4 (&w)[F::kSlices], const uint32_t (&sr)[kSR], int st_local,
                      f32x4& acc, f32x4& bacc) {
     const int st = ks * Lw + st_local;
@@ -1230,7 +1297,7 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
         for (int k = 0; k < 4; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(r[k]) : "v"(r[k]));
       }
 #endif
-      if constexpr (FMT == QGEMV_INT8_G32) {
+      if constexpr (is_int8_fmt(FMT)) {
         swap32(r[0], r[2]);
         swap32(r[1], r[3]);
       } else if constexpr (FMT != QGEMV_BF16) {
@@ -1247,6 +1314,12 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
             bf16x8_t, *reinterpret_cast<const u32x4*>(xs + (static_cast<size_t>(c) * NB + bcl) * 32 + 8 * q));
         if constexpr (FMT == QGEMV_BF16) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, w[l]), acc, 0, 0, 0);
+        } else if constexpr (FMT == QGEMV_INT8_ROW) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), acc, 0, 0, 0);
+        } else if constexpr (FMT == QGEMV_INT4_G64) {
+          // two chunks per group: the second accumulates onto the first
+          const int gi = (l * kCPS + ch) >> 1;
+          dch[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), (ch & 1) ? dch[gi] : zero, 0, 0, 0);
         } else if constexpr (FMT == QGEMV_INT8_G32) {
           dch[l * kCPS + ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), zero, 0, 0, 0);
         } else if constexpr (FMT == QGEMV_Q4_0_G32) {
@@ -1260,7 +1333,7 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
     // group scales, applied after all of the step's matrix instructions are
     // issued (each scale FMA waits for its MFMA's result; interleaving them
     // stalls on every chunk)
-    if constexpr (FMT != QGEMV_BF16) {
+    if constexpr (F::kGroups > 0) {
 #pragma unroll
       for (int g = 0; g < kDch; ++g) {
         const float sc = scale_of(s, g);
@@ -1283,9 +1356,16 @@ __device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1,
 
   // D tile -> y: lane (i, q) holds batch rows 4q..4q+3 of row i of the tile
   // (the paired row of a gate/up pair is in lane i ^ 1, same q)
-  auto store = [&](const f32x4& v, int n) {
+  auto store = [&](const f32x4& v_in, int n) {
     const int tile = (g0 + n) * TW + tg;
     const int row = tile * 16 + i;
+    f32x4 v = v_in;
+    if constexpr (FMT == QGEMV_INT8_ROW) {
+      // the row's scale, applied once to the finished dot products
+      const float d = half_to_float(S[min(row, M - 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] *= d;
+    }
     if constexpr (FUSED) {
       f32x4 pv = v;
       if (fu.epi == kEpiSwiglu) {
@@ -1522,7 +1602,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int KD = K >> 1;                              // x dwords per batch row
   const int U = K / T::kElems;                        // 16-byte units per row
   const size_t row_bytes = static_cast<size_t>(U) * 16;
-  const int nsc = T::kUnitsPerScale ? U / T::kUnitsPerScale : 0;
+  const int nsc = scales_per_row<FMT>(U);
   const int groups = (M + R - 1) / R;
   const int waves_total = gridDim.x * kWaves;
   const int nchunk = (U + 64 * UC - 1) / (64 * UC);
@@ -1546,8 +1626,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       for (int u = 0; u < UC; ++u) {
         const int t = min(ch * 64 * UC + u * 64 + lane, U - 1);
         wv[r][u] = load_weights(wrow + t);
-        if constexpr (T::kUnitsPerScale > 0)
-          sv[r][u] = S[static_cast<size_t>(row) * nsc + t / T::kUnitsPerScale];
+        if constexpr (T::kUnitsPerScale != 0)
+          sv[r][u] = S[static_cast<size_t>(row) * nsc + scale_index<FMT>(t)];
       }
     }
   };
@@ -1824,18 +1904,14 @@ hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n,
 
 // ---- matrix-core kernel: launch plan
 int mfma_step_elems(int fmt) {
-  switch (fmt) {
-    case QGEMV_BF16: return MfmaFmt<QGEMV_BF16>::kStepElems;
-    case QGEMV_INT8_G32: return MfmaFmt<QGEMV_INT8_G32>::kStepElems;
-    case QGEMV_Q4_0_G32: return MfmaFmt<QGEMV_Q4_0_G32>::kStepElems;
-    default: return MfmaFmt<QGEMV_INT4_G128>::kStepElems;
-  }
+  return with_fmt(fmt, [](auto F) { return MfmaFmt<decltype(F)::value>::kStepElems; });
 }
 
 size_t mfma_lds_bytes(int fmt, int K, int NB, int KS, int TW) {
   size_t b = static_cast<size_t>(NB) * K * 2;                       // x
   if (fmt == QGEMV_Q4_0_G32) b += static_cast<size_t>(K / 32) * NB * 4;   // group sums
   if (fmt == QGEMV_INT4_G128) b += static_cast<size_t>(K / 128) * NB * 4;
+  if (fmt == QGEMV_INT4_G64) b += static_cast<size_t>(K / 64) * NB * 4;
   if (KS > 1) b += static_cast<size_t>(2) * TW * KS * (4 * NB) * 16;  // partial tiles
   return b;
 }
@@ -1926,12 +2002,7 @@ hipError_t launch_mfma(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t 
 
 template <int N>
 hipError_t launch_mfma_fmt(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st, int nb) {
-  switch (a[0].fmt) {
-    case QGEMV_BF16: return launch_mfma<QGEMV_BF16, N>(a, n, p, st, nb);
-    case QGEMV_INT8_G32: return launch_mfma<QGEMV_INT8_G32, N>(a, n, p, st, nb);
-    case QGEMV_Q4_0_G32: return launch_mfma<QGEMV_Q4_0_G32, N>(a, n, p, st, nb);
-    default: return launch_mfma<QGEMV_INT4_G128, N>(a, n, p, st, nb);
-  }
+  return with_fmt(a[0].fmt, [&](auto F) { return launch_mfma<decltype(F)::value, N>(a, n, p, st, nb); });
 }
 }  // namespace
 
@@ -1940,14 +2011,17 @@ FmtInfo fmt_info(int fmt) {
     case QGEMV_BF16: return {1, 8};
     case QGEMV_INT8_G32: return {32, 16};
     case QGEMV_Q4_0_G32: return {32, 32};
-    default: return {128, 32};
+    case QGEMV_INT4_G128: return {128, 32};
+    case QGEMV_INT8_ROW: return {0, 16};
+    default: return {64, 32};
   }
 }
 
 size_t gemv_lds_bytes(int fmt, int K, int batch) {
   const int nb = round_batch(batch);             // (batch 8 for the invariant mode's size)
   size_t bytes = static_cast<size_t>(nb) * K * 2;
-  if (fmt == QGEMV_Q4_0_G32 || fmt == QGEMV_INT4_G128) bytes += static_cast<size_t>(nb) * (K / 32) * 4;
+  if (fmt == QGEMV_Q4_0_G32 || fmt == QGEMV_INT4_G128 || fmt == QGEMV_INT4_G64)
+    bytes += static_cast<size_t>(nb) * (K / 32) * 4;                  // -8 * sum(x) per 16-byte unit
   return bytes;
 }
 
@@ -1975,12 +2049,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
     const int groups = (a.M + R - 1) / R;
     const int wg_needed = (groups + kWaves - 1) / kWaves;
     const int grid = std::max(1, std::min(wg_needed, cus * QGEMV_MAX_WG_PER_CU));
-    switch (a.fmt) {
-      case QGEMV_BF16: return launch_xreg<QGEMV_BF16>(a, R, nch, grid, stream);
-      case QGEMV_INT8_G32: return launch_xreg<QGEMV_INT8_G32>(a, R, nch, grid, stream);
-      case QGEMV_Q4_0_G32: return launch_xreg<QGEMV_Q4_0_G32>(a, R, nch, grid, stream);
-      default: return launch_xreg<QGEMV_INT4_G128>(a, R, nch, grid, stream);
-    }
+    return with_fmt(a.fmt, [&](auto F) { return launch_xreg<decltype(F)::value>(a, R, nch, grid, stream); });
   }
   MfmaPlan plan;
   if (plan_mfma(a.fmt, a.M, a.K, inv ? 8 : a.batch, cus, &plan)) return launch_mfma_fmt<1>(&a, 1, plan, stream, nb);
@@ -2000,17 +2069,13 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
                     allow_big_lds<F, 2, 1>(); allow_big_lds<F, 2, 2>(); allow_big_lds<F, 2, 4>(); \
                     allow_big_lds<F, 1, 1>(); allow_big_lds<F, 1, 2>(); allow_big_lds<F, 1, 4>();
       QG_ALLOW(QGEMV_BF16) QG_ALLOW(QGEMV_INT8_G32) QG_ALLOW(QGEMV_Q4_0_G32) QG_ALLOW(QGEMV_INT4_G128)
+      QG_ALLOW(QGEMV_INT8_ROW) QG_ALLOW(QGEMV_INT4_G64)
 #undef QG_ALLOW
       return true;
     }();
     (void)once;
   }
-  switch (a.fmt) {
-    case QGEMV_BF16: return launch_f<QGEMV_BF16>(a, R, grid, lds, stream, nb);
-    case QGEMV_INT8_G32: return launch_f<QGEMV_INT8_G32>(a, R, grid, lds, stream, nb);
-    case QGEMV_Q4_0_G32: return launch_f<QGEMV_Q4_0_G32>(a, R, grid, lds, stream, nb);
-    default: return launch_f<QGEMV_INT4_G128>(a, R, grid, lds, stream, nb);
-  }
+  return with_fmt(a.fmt, [&](auto F) { return launch_f<decltype(F)::value>(a, R, grid, lds, stream, nb); });
 }
 
 int gemv_group_class(int fmt, int K, int batch) {
@@ -2056,12 +2121,9 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int a
   long cap = static_cast<long>(cus) * QGEMV_GROUP_MAX_WG_PER_CU;
   if (am >= 0 && cap > kFusedSlots) cap = kFusedSlots;       // one argmax slot per workgroup
   const int grid = static_cast<int>(std::max<long>(1, std::min<long>((total + kWaves - 1) / kWaves, cap)));
-  switch (a[0].fmt) {
-    case QGEMV_BF16: return launch_group1<QGEMV_BF16>(a, R, nch, n, grid, am, slots, idx, stream);
-    case QGEMV_INT8_G32: return launch_group1<QGEMV_INT8_G32>(a, R, nch, n, grid, am, slots, idx, stream);
-    case QGEMV_Q4_0_G32: return launch_group1<QGEMV_Q4_0_G32>(a, R, nch, n, grid, am, slots, idx, stream);
-    default: return launch_group1<QGEMV_INT4_G128>(a, R, nch, n, grid, am, slots, idx, stream);
-  }
+  return with_fmt(a[0].fmt, [&](auto F) {
+    return launch_group1<decltype(F)::value>(a, R, nch, n, grid, am, slots, idx, stream);
+  });
 }
 
 // ---- qgemv_run_fused: one GEMV with the RMSNorm prologue and an epilogue.
@@ -2165,12 +2227,7 @@ hipError_t launch_fused_fmt(const GemvArgs& a, const Fusion& f, uint64_t* slots,
 
 hipError_t launch_gemv_fused(const GemvArgs& a, const Fusion& f, uint64_t* slots, int32_t* idx,
                              hipStream_t stream) {
-  switch (a.fmt) {
-    case QGEMV_BF16: return launch_fused_fmt<QGEMV_BF16>(a, f, slots, idx, stream);
-    case QGEMV_INT8_G32: return launch_fused_fmt<QGEMV_INT8_G32>(a, f, slots, idx, stream);
-    case QGEMV_Q4_0_G32: return launch_fused_fmt<QGEMV_Q4_0_G32>(a, f, slots, idx, stream);
-    default: return launch_fused_fmt<QGEMV_INT4_G128>(a, f, slots, idx, stream);
-  }
+  return with_fmt(a.fmt, [&](auto F) { return launch_fused_fmt<decltype(F)::value>(a, f, slots, idx, stream); });
 }
 
 }  // namespace qgemv

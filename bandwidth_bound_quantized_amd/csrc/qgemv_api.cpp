@@ -18,22 +18,35 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
-bool valid_fmt(int fmt) { return fmt >= QGEMV_BF16 && fmt <= QGEMV_INT4_G128; }
+bool valid_fmt(int fmt) { return fmt >= QGEMV_BF16 && fmt <= QGEMV_INT4_G64; }
 
-int group_of(int fmt) {
+// K must be a multiple of this (the scale group; 32 for bf16 and int8-row)
+int k_align(int fmt) {
   switch (fmt) {
-    case QGEMV_INT8_G32: return 32;
-    case QGEMV_Q4_0_G32: return 32;
     case QGEMV_INT4_G128: return 128;
-    default: return 32;   // bf16: K must still be a multiple of 32
+    case QGEMV_INT4_G64: return 64;
+    default: return 32;
   }
 }
+
+// weights per scale for a row of K (int8-row: the whole row; bf16: none)
+int64_t group_of(int fmt, int64_t K) {
+  switch (fmt) {
+    case QGEMV_INT8_G32: case QGEMV_Q4_0_G32: return 32;
+    case QGEMV_INT4_G128: return 128;
+    case QGEMV_INT4_G64: return 64;
+    case QGEMV_INT8_ROW: return K;
+    default: return 0;
+  }
+}
+
+bool is_int8(int fmt) { return fmt == QGEMV_INT8_G32 || fmt == QGEMV_INT8_ROW; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int check_shape(int fmt, int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M >= kMaxDim || K >= kMaxDim) return QGEMV_ESHAPE;
-  if (K % group_of(fmt) != 0) return QGEMV_ESHAPE;
+  if (K % k_align(fmt) != 0) return QGEMV_ESHAPE;
   return QGEMV_OK;
 }
 
@@ -42,7 +55,9 @@ void sizes(int fmt, int64_t M, int64_t K, size_t* w, size_t* s) {
   switch (fmt) {
     case QGEMV_BF16: *w = 2 * mk; *s = 0; break;
     case QGEMV_INT8_G32: *w = mk; *s = 2 * (mk / 32); break;
+    case QGEMV_INT8_ROW: *w = mk; *s = 2 * static_cast<size_t>(M); break;
     case QGEMV_Q4_0_G32: *w = mk / 2; *s = 2 * (mk / 32); break;
+    case QGEMV_INT4_G64: *w = mk / 2; *s = 2 * (mk / 64); break;
     default: *w = mk / 2; *s = 2 * (mk / 128); break;
   }
 }
@@ -101,20 +116,20 @@ double bf16_to_double(uint16_t h) {
 }
 
 // Quantize one group of G bf16 weights. Returns false on a range error.
-bool quantize_group(int fmt, const uint16_t* w, int G, uint16_t* d_out, int* q_out) {
-  double v[128];
-  for (int j = 0; j < G; ++j) {
+// (G up to K for int8-row; v and q_out hold G values)
+bool quantize_group(int fmt, const uint16_t* w, int64_t G, double* v, uint16_t* d_out, int* q_out) {
+  for (int64_t j = 0; j < G; ++j) {
     v[j] = bf16_to_double(w[j]);
     if (!std::isfinite(v[j])) return false;
   }
   double d_exact;
-  if (fmt == QGEMV_INT8_G32) {
+  if (is_int8(fmt)) {
     double amax = 0.0;
-    for (int j = 0; j < G; ++j) amax = std::fmax(amax, std::fabs(v[j]));
+    for (int64_t j = 0; j < G; ++j) amax = std::fmax(amax, std::fabs(v[j]));
     d_exact = amax / 127.0;
   } else {
-    int first = 0;
-    for (int j = 1; j < G; ++j)
+    int64_t first = 0;
+    for (int64_t j = 1; j < G; ++j)
       if (std::fabs(v[j]) > std::fabs(v[first])) first = j;   // strict: first of ties
     d_exact = v[first] / -8.0;
   }
@@ -123,8 +138,8 @@ bool quantize_group(int fmt, const uint16_t* w, int G, uint16_t* d_out, int* q_o
   if ((dh & 0x7C00) == 0x7C00) return false;                   // overflow
   const double d = half_to_double(dh);
   *d_out = dh;
-  for (int j = 0; j < G; ++j) {
-    if (fmt == QGEMV_INT8_G32) {
+  for (int64_t j = 0; j < G; ++j) {
+    if (is_int8(fmt)) {
       double q = (d == 0.0) ? 0.0 : std::nearbyint(v[j] / d);
       q = std::fmin(127.0, std::fmax(-127.0, q));
       q_out[j] = static_cast<int>(q);
@@ -143,29 +158,30 @@ int pack_from_bf16(int fmt, const uint16_t* src, int64_t M, int64_t K, void* dst
     std::memcpy(dst_w, src, static_cast<size_t>(M) * K * 2);
     return QGEMV_OK;
   }
-  const int G = group_of(fmt);
+  const int64_t G = group_of(fmt, K);
   const int64_t ng = K / G;
-  int q[128];
+  std::vector<int> q(static_cast<size_t>(G));
+  std::vector<double> v(static_cast<size_t>(G));
   // validate everything first so that nothing is written on error
   for (int64_t i = 0; i < M * K; ++i)
     if (!std::isfinite(bf16_to_double(src[i]))) return QGEMV_ERANGE;
   for (int64_t m = 0; m < M; ++m) {
     for (int64_t g = 0; g < ng; ++g) {
       uint16_t dh;
-      if (!quantize_group(fmt, src + m * K + g * G, G, &dh, q)) return QGEMV_ERANGE;
+      if (!quantize_group(fmt, src + m * K + g * G, G, v.data(), &dh, q.data())) return QGEMV_ERANGE;
     }
   }
   for (int64_t m = 0; m < M; ++m) {
     for (int64_t g = 0; g < ng; ++g) {
       uint16_t dh;
-      quantize_group(fmt, src + m * K + g * G, G, &dh, q);
+      quantize_group(fmt, src + m * K + g * G, G, v.data(), &dh, q.data());
       dst_s[m * ng + g] = dh;
-      if (fmt == QGEMV_INT8_G32) {
+      if (is_int8(fmt)) {
         int8_t* out = static_cast<int8_t*>(dst_w) + m * K + g * G;
-        for (int j = 0; j < G; ++j) out[j] = static_cast<int8_t>(q[j]);
+        for (int64_t j = 0; j < G; ++j) out[j] = static_cast<int8_t>(q[j]);
       } else {
         uint8_t* out = static_cast<uint8_t*>(dst_w) + (m * ng + g) * (G / 2);
-        for (int j = 0; j < G / 2; ++j)
+        for (int64_t j = 0; j < G / 2; ++j)
           out[j] = static_cast<uint8_t>(q[j] | (q[j + G / 2] << 4));
       }
     }
@@ -247,7 +263,7 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
 
 int qgemv_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
                    int32_t* err, void* stream) {
-  if (fmt != QGEMV_INT8_G32 && fmt != QGEMV_Q4_0_G32 && fmt != QGEMV_INT4_G128) return QGEMV_EINVAL;
+  if (!valid_fmt(fmt) || fmt == QGEMV_BF16) return QGEMV_EINVAL;
   if (!w || !codes || !scales) return QGEMV_EINVAL;
   const int st = check_shape(fmt, M, K);
   if (st) return st;

@@ -1,6 +1,6 @@
 // Weight quantizer on the device (gfx950): bf16 weights -> Q4_0-g32,
-// int4-g128 or int8-g32 codes and binary16 scales, bit-identical to the
-// host quantizer of qgemv_pack (SRC_BF16).
+// int4-g128, int4-g64, int8-g32 or int8-row codes and binary16 scales,
+// bit-identical to the host quantizer of qgemv_pack (SRC_BF16).
 //
 // Rule (the Rust page, "Is the 4-bit model still good?", and "infer", design
 // notes: the group's element of largest magnitude, with its sign, maps to
@@ -13,7 +13,7 @@
 // non-finite weight or a scale past binary16's range is an error.
 //
 // One thread per group (offline work; every thread reads its group's
-// contiguous bf16 weights with 16-byte loads). float64 arithmetic: every
+// contiguous bf16 weights with 16-byte loads); int8-row: one wave per row. float64 arithmetic: every
 // bf16 and binary16 value is exact in it, and the divisions are IEEE
 // (correctly rounded) divisions.
 #include "qgemv_internal.h"
@@ -64,7 +64,7 @@ template <int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ w, int64_t M, int64_t K,
                                                        uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                                                        int32_t* __restrict__ err) {
-  constexpr int G = FMT == QGEMV_INT4_G128 ? 128 : 32;
+  constexpr int G = FMT == QGEMV_INT4_G128 ? 128 : FMT == QGEMV_INT4_G64 ? 64 : 32;
   const int64_t ng = K / G;
   const int64_t grp = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (grp >= M * ng) return;
@@ -143,18 +143,76 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   if (bad && err) atomicExch(err, QGEMV_ERANGE);
 }
 
+// int8 with one scale per row: one wave per row (4 per workgroup). The
+// row's largest |w| (on the magnitude bits, an exact max in any order), the
+// scale, then the codes, 8 weights per lane and step.
+__global__ __launch_bounds__(256) void quantize_int8_row_kernel(const uint16_t* __restrict__ w, int64_t M,
+                                                                int64_t K, int8_t* __restrict__ codes,
+                                                                uint16_t* __restrict__ scales,
+                                                                int32_t* __restrict__ err) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;                                // the whole wave
+  const uint16_t* wr = w + row * K;
+  uint32_t best = 0;
+  bool bad = false;
+  for (int64_t k = 8 * lane; k < K; k += 512) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(wr + k);
+    const uint32_t d4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a0 = d4[i] & 0x7FFFu, a1 = (d4[i] >> 16) & 0x7FFFu;
+      bad |= a0 >= 0x7F80u || a1 >= 0x7F80u;
+      best = a0 > best ? a0 : best;
+      best = a1 > best ? a1 : best;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t t = static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), o));
+    best = t > best ? t : best;
+  }
+  bad = __any(bad);
+  uint16_t dh = double_to_half_rne(bf16_to_double(static_cast<uint16_t>(best)) / 127.0);
+  if ((dh & 0x7FFF) == 0) dh = 0;                      // a zero scale is +0
+  bad |= (dh & 0x7C00) == 0x7C00;
+  const double d = half_bits_to_double(dh);
+  if (lane == 0) scales[row] = dh;
+  for (int64_t k = 8 * lane; k < K; k += 512) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(wr + k);
+    const uint32_t d4[4] = {u.x, u.y, u.z, u.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t b = static_cast<uint16_t>((i & 1) ? (d4[i >> 1] >> 16) : (d4[i >> 1] & 0xFFFFu));
+      double q = d == 0.0 ? 0.0 : __builtin_rint(bf16_to_double(b) / d);
+      q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
+      out[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xFFu) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(codes + row * K + k) = make_uint2(out[0], out[1]);
+  }
+  if (bad && err && lane == 0) atomicExch(err, QGEMV_ERANGE);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
                            int32_t* err, hipStream_t stream) {
-  const int G = fmt == QGEMV_INT4_G128 ? 128 : 32;
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  if (fmt == QGEMV_INT8_ROW) {
+    const unsigned grid = static_cast<unsigned>((M + 3) / 4);
+    quantize_int8_row_kernel<<<grid, 256, 0, stream>>>(w, M, K, reinterpret_cast<int8_t*>(c), scales, err);
+    return hipGetLastError();
+  }
+  const int G = fmt == QGEMV_INT4_G128 ? 128 : fmt == QGEMV_INT4_G64 ? 64 : 32;
   const int64_t groups = M * (K / G);
   const unsigned grid = static_cast<unsigned>((groups + 255) / 256);
-  uint8_t* c = static_cast<uint8_t*>(codes);
   switch (fmt) {
     case QGEMV_INT8_G32: quantize_kernel<QGEMV_INT8_G32><<<grid, 256, 0, stream>>>(w, M, K, c, scales, err); break;
     case QGEMV_Q4_0_G32: quantize_kernel<QGEMV_Q4_0_G32><<<grid, 256, 0, stream>>>(w, M, K, c, scales, err); break;
-    default: quantize_kernel<QGEMV_INT4_G128><<<grid, 256, 0, stream>>>(w, M, K, c, scales, err); break;
+    case QGEMV_INT4_G128: quantize_kernel<QGEMV_INT4_G128><<<grid, 256, 0, stream>>>(w, M, K, c, scales, err); break;
+    case QGEMV_INT4_G64: quantize_kernel<QGEMV_INT4_G64><<<grid, 256, 0, stream>>>(w, M, K, c, scales, err); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -518,8 +518,9 @@ def main():
 
     names = {1: "bf16_gemv_2048x2048", 2: "q4_0_g32_tinyllama_gemv_set+argmax",
              3: "int8_g32_llama32_1b_gemv_set", 4: "q4_0_g32_tinyllama_decode_step_89_gemvs+argmax",
-             5: "int4_g128_ffn+int8_g32_lm_head+argmax"}
-    dtypes = {1: "bf16", 2: "q4_0", 3: "int8", 4: "q4_0", 5: "int4/int8"}
+             5: "int4_g128_ffn+int8_g32_lm_head+argmax",
+             6: "q4_0_g32_llama32_1b_layer_gemvs+int8_row_lm_head+argmax"}
+    dtypes = {1: "bf16", 2: "q4_0", 3: "int8", 4: "q4_0", 5: "int4/int8", 6: "q4_0/int8"}
     if dom_key[0] == "alone":
         dom_label = f"qgemv_run {wl.gemvs[dom_key[1]].name}"
     elif wl.has_argmax and len(wl.gemvs) - 1 in wl.classes[dom_key]:

@@ -26,6 +26,15 @@
  *                    ("infer", g128 rows of the decode and perplexity tables;
  *                    the nibble order is this library's reading, the same
  *                    half-split as Q4_0).
+ *   QGEMV_INT8_ROW   W: int8 [M][K]; scales: binary16 [M] (one per row);
+ *                    weight = code * scale ("infer", perplexity table and
+ *                    notes: its int8 weights have one scale per row; the
+ *                    scale type is this library's reading).
+ *   QGEMV_INT4_G64   W: uint8 [M][K/64][32]; scales: binary16 [M][K/64];
+ *                    element j of a block is the low nibble of byte j,
+ *                    element j+32 the high nibble; weight = (code-8)*scale
+ *                    ("infer", the g64 row of the perplexity table; nibble
+ *                    order as for g128).
  * Activations x: bf16 bits [batch][K]. Output y: float32 [batch][M].
  *
  * Conventions for every entry point:
@@ -55,7 +64,9 @@ enum {
   QGEMV_BF16 = 0,
   QGEMV_INT8_G32 = 1,
   QGEMV_Q4_0_G32 = 2,
-  QGEMV_INT4_G128 = 3
+  QGEMV_INT4_G128 = 3,
+  QGEMV_INT8_ROW = 4,
+  QGEMV_INT4_G64 = 5
 };
 
 /* source kinds for qgemv_pack */
@@ -67,8 +78,8 @@ enum {
 enum {
   QGEMV_OK = 0,
   QGEMV_EINVAL = -1, /* null pointer, unknown format or source kind */
-  QGEMV_ESHAPE = -2, /* M < 1, K not a positive multiple of the group (32, or
-                        128 for int4-g128), batch outside 1..8, V < 1, or K
+  QGEMV_ESHAPE = -2, /* M < 1, K not a positive multiple of the group (32;
+                        128 for int4-g128, 64 for int4-g64), batch outside 1..8, V < 1, or K
                         beyond what one workgroup's LDS can stage */
   QGEMV_EALIGN = -3, /* W, x or y not 16-byte aligned; scales or logits not
                         4-byte aligned; ws not 8-byte aligned */
@@ -83,9 +94,9 @@ enum {
 
 /*
  * qgemv_packed_size - bytes of the device layout of an M x K matrix.
- * Host only, no HIP calls. *w_bytes gets the code bytes (2MK, MK, MK/2, MK/2
- * for bf16, int8-g32, Q4_0-g32, int4-g128), *s_bytes the scale bytes
- * (0 for bf16, else 2*M*K/G). These are the byte counts the pages use for
+ * Host only, no HIP calls. *w_bytes gets the code bytes (2MK for bf16, MK
+ * for the int8 formats, MK/2 for the 4-bit ones), *s_bytes the scale bytes
+ * (0 for bf16, 2M for int8-row, else 2*M*K/G). These are the byte counts the pages use for
  * their bandwidth figures (4.5 bits per weight for Q4_0; "infer"'s per-token
  * weight totals). Errors: EINVAL (null out-pointer, bad fmt), ESHAPE.
  */
@@ -101,8 +112,8 @@ int qgemv_packed_size(int fmt, int64_t M, int64_t K, size_t* w_bytes, size_t* s_
  *     group is quantized (src_scales ignored): 4-bit formats take the
  *     group's element of largest magnitude with its sign, m, and set
  *     scale = binary16(m / -8) so that m maps to code 0 (Rust page, "Is the
- *     4-bit model still good?"; "infer", design notes); int8-g32 sets
- *     scale = binary16(max|w| / 127). Then code = round-half-even(w / scale)
+ *     4-bit model still good?"; "infer", design notes); the int8 formats
+ *     set scale = binary16(max|w| / 127) over the group (int8-row: the row). Then code = round-half-even(w / scale)
  *     (+8 for 4-bit), clamped to [0,15] or [-127,127]; ties in |w| go to the
  *     first element; a scale that rounds to zero is stored as +0 with every
  *     code 8 (4-bit) or 0 (int8). The division is done in double precision
@@ -119,7 +130,7 @@ int qgemv_pack(int fmt, int src_kind, const void* src_w, const uint16_t* src_sca
  * above, bit-identical to what qgemv_pack writes for the same weights (the
  * rule and its readings as documented there: the Rust page, "Is the 4-bit
  * model still good?"; "infer", design notes and its quantizer tests).
- * fmt: INT8_G32, Q4_0_G32 or INT4_G128 (EINVAL for BF16). Device pointers:
+ * fmt: any quantized format (EINVAL for BF16). Device pointers:
  * w 16-byte aligned; codes (qgemv_packed_size's w_bytes) 16-byte aligned;
  * scales (s_bytes) 4-byte aligned; err: a device int32 or NULL. A group
  * with a non-finite weight or a scale past binary16's range stores
@@ -137,7 +148,7 @@ int qgemv_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes
  * bf16); x: bf16 [batch][K]; y: float32 [batch][M], overwritten (not
  * accumulated). Accumulation is float32; each 32-weight group's scale is
  * applied once to the group's partial sum. 1 <= batch <= 8, M >= 1 (any
- * value), K a multiple of 32 (of 128 for int4-g128) such that x fits in
+ * value), K a multiple of 32 (128 for int4-g128, 64 for int4-g64) such that x fits in
  * one workgroup's LDS: nb * K * 2 bytes (plus nb * K / 8 for the 4-bit
  * formats) <= 163840, nb = batch rounded up to 1, 2, 4 or 8 (e.g. 4-bit:
  * K <= 9632 at batch 5..8, K <= 77088 at batch 1; bf16/int8: K <= 10240 at
@@ -194,7 +205,7 @@ typedef struct {
  * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit)
  * share launches (one per format, up to 64 entries each), and so do entries
  * of one format and K that the matrix-core kernel handles (batch 3..8, K a
- * multiple of 256 for Q4_0, 128 for int8 and bf16, 512 for int4-g128, x in
+ * multiple of 256 for Q4_0 and int4-g64, 128 for int8 and bf16, 512 for int4-g128, x in
  * LDS), so the per-launch start-up cost is paid once per group instead of
  * once per GEMV; other entries are launched one by one. All validation
  * happens before anything is launched. Errors as qgemv_run; ESHAPE also

@@ -59,6 +59,8 @@ def test_packed_sizes_basic():
     assert qg.packed_size(qg.Q4_0_G32, 2048, 2048) == (2097152, 262144)   # 4.5 bits/weight
     assert qg.packed_size(qg.INT8_G32, 3072, 2048) == (6291456, 393216)
     assert qg.packed_size(qg.INT4_G128, 16384, 2048) == (16777216, 524288)
+    assert qg.packed_size(qg.INT8_ROW, 128256, 2048) == (262668288, 256512)   # one scale per row
+    assert qg.packed_size(qg.INT4_G64, 2048, 2048) == (2097152, 131072)      # 4.25 bits/weight
 
 
 def test_per_token_totals_match_infer_decode_table():
@@ -74,9 +76,10 @@ def test_per_token_totals_match_infer_decode_table():
     want = ACC["weights_per_token_GB"]
     assert round(total(qg.BF16) / 1e9, 2) == want["bf16"]
     assert round(total(qg.INT8_G32, scales=False) / 1e9, 2) == want["int8_codes_only"]
+    assert round(total(qg.INT8_ROW) / 1e9, 2) == want["int8_codes_only"]      # infer's int8: per-row scales
     assert round(total(qg.Q4_0_G32) / 1e9, 2) == want["int4_g32"]
     assert round(total(qg.INT4_G128) / 1e9, 2) == want["int4_g128"]
-    mixed = n * sum(_bytes(qg.Q4_0_G32, M, K) for _, M, K in layer) + _bytes(qg.INT8_G32, *head, scales=False)
+    mixed = n * sum(_bytes(qg.Q4_0_G32, M, K) for _, M, K in layer) + _bytes(qg.INT8_ROW, *head)
     assert round(mixed / 1e9, 2) == want["int4_g32_int8_head"]
 
 
@@ -84,7 +87,7 @@ def test_quantized_gemv_table_percentages_reproduce():
     peak = ACC["measured_peak_GBps"]
     for name, M, K, us4, pct4, us8, pct8 in ACC["quantized_gemv_table"]["rows"]:
         b4 = _bytes(qg.Q4_0_G32, M, K)                 # 18 bytes per 32 weights
-        b8 = _bytes(qg.INT8_G32, M, K, scales=False)   # per-row int8: 1 byte per weight
+        b8 = _bytes(qg.INT8_ROW, M, K)                 # per-row int8: 1 byte per weight + 2 per row
         assert abs(b4 / us4 / 1e3 / peak * 100 - pct4) <= 1.0, name
         assert abs(b8 / us8 / 1e3 / peak * 100 - pct8) <= 1.0, name
     for name, M, K, us, gbps, pct in ACC["bf16_gemv_table"]["rows"]:
@@ -94,7 +97,7 @@ def test_quantized_gemv_table_percentages_reproduce():
 
 
 # ------------------------------------------------------------------ pack
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64])
 def test_pack_canonical_roundtrip(fmt):
     g = synth.make_gemv("t", fmt, 37, 256, 1, 9, 1, "o")
     w, s = qg.pack(fmt, qg.SRC_CANONICAL, g.w, g.s, 37, 256)
@@ -121,7 +124,7 @@ def _quant_inputs():
     return w
 
 
-@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64])
 def test_pack_bf16_quantizer_bit_exact_vs_oracle(fmt):
     w = _quant_inputs()
     M, K = w.shape
@@ -131,7 +134,7 @@ def test_pack_bf16_quantizer_bit_exact_vs_oracle(fmt):
     assert (codes == o_codes.reshape(-1).view(np.uint8)).all()
 
 
-@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64])
 def test_pack_bf16_quantizer_bit_exact_config1_shape(fmt):
     rng = np.random.default_rng(fmt + 1000)
     w = synth.bf16_normal(rng, (2048, 2048), 0.02)
@@ -214,6 +217,8 @@ def test_run_validation_errors_before_any_launch():
     assert _run(S=None) == qg.EINVAL
     assert _run(M=0) == qg.ESHAPE
     assert _run(K=48) == qg.ESHAPE
+    assert _run(fmt=6) == qg.EINVAL
+    assert _run(fmt=qg.INT4_G64, K=2048 + 32) == qg.ESHAPE             # K a multiple of 64
     assert _run(fmt=qg.INT4_G128, K=2048 + 32) == qg.ESHAPE
     assert _run(batch=0) == qg.ESHAPE
     assert _run(batch=9) == qg.ESHAPE

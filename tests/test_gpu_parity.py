@@ -19,6 +19,9 @@ from helpers import build_case, load_json  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+ALL_FMTS = [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64]
+FMT_IDS = ["bf16", "int8", "q4_0", "int4", "int8_row", "int4_g64"]
+NIBBLE_FMTS = (qg.Q4_0_G32, qg.INT4_G128, qg.INT4_G64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -105,7 +108,7 @@ def test_decode_step_stream_layers_parity(B):
 
 
 # ------------------------------------------------------------ exactness
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FMT_IDS)
 def test_onehot_probes_bit_exact(fmt):
     """x = e_k: y[b, m] = W_hat[m, k_b] exactly (one product, every other term 0)."""
     M, K, B = 300, 1024, 8
@@ -121,14 +124,14 @@ def test_onehot_probes_bit_exact(fmt):
     assert (y == want).all()
 
 
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("M,K", [(1, 128), (63, 256), (65, 384), (1000, 5632), (7, 9216)])
 def test_ragged_shapes_all_batches(fmt, M, K):
-    if K % synth.GROUP[fmt]:
+    if K % synth.K_ALIGN[fmt]:
         K = (K // 128 + 1) * 128
     for B in range(1, 9):
         nb = 1 if B == 1 else 2 if B == 2 else 4 if B <= 4 else 8
-        lds = nb * K * 2 + (nb * K // 8 if fmt in (qg.Q4_0_G32, qg.INT4_G128) else 0)
+        lds = nb * K * 2 + (nb * K // 8 if fmt in NIBBLE_FMTS else 0)
         if lds > 160 * 1024:
             continue
         g = synth.make_gemv("t", fmt, M, K, B, 7, M % 997, "down")
@@ -136,13 +139,13 @@ def test_ragged_shapes_all_batches(fmt, M, K):
         assert_parity(fmt, g.w, g.s, g.x, M, K, B, y, what=f"M={M} K={K} B={B}")
 
 
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128])
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FMT_IDS)
 def test_zero_weights_random_x(fmt):
     """All weights zero (codes 8 for 4-bit): every output within 1e-5 of 0."""
     M, K, B = 256, 5632 if fmt != qg.INT4_G128 else 5632 - 5632 % 128, 2
     g = synth.make_gemv("t", fmt, M, K, B, 7, 5, "o")
     w = np.zeros_like(g.w)
-    if fmt in (qg.Q4_0_G32, qg.INT4_G128):
+    if fmt in NIBBLE_FMTS:
         w[:] = 0x88
     s = None if g.s is None else np.full_like(g.s, 0x1D1F)    # ~0.005, the largest generated scale
     y = gpu_gemv(fmt, w, s, g.x, M, K, B)
@@ -185,7 +188,7 @@ def test_pack_bf16_then_run():
     M, K, B = 512, 2048, 2
     wbf = synth.bf16_normal(rng, (M, K), 0.02)
     x = synth.bf16_normal(rng, (B, K), 1.0)
-    for fmt in (qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128):
+    for fmt in ALL_FMTS[1:]:
         codes, scales = qg.pack(fmt, qg.SRC_BF16, wbf, None, M, K)
         y = gpu_gemv(fmt, codes, scales, x, M, K, B)
         o_codes, o_scales = oracle.quantize_from_bf16(fmt, wbf, M, K)
@@ -340,7 +343,8 @@ def test_grouped_mixed_formats_ragged_and_fallback(B):
     shapes = [(synth.Q4_0_G32, 1, 2048), (synth.BF16, 65, 256), (synth.INT8_G32, 1000, 2048),
               (synth.Q4_0_G32, 63, 5632), (synth.INT4_G128, 300, 8192), (synth.INT8_G32, 70, 8192),
               (synth.Q4_0_G32, 4097, 2048), (synth.BF16, 7, 2048), (synth.INT4_G128, 129, 384),
-              (synth.Q4_0_G32, 2, 96)]
+              (synth.Q4_0_G32, 2, 96), (synth.INT8_ROW, 513, 2048), (synth.INT4_G64, 1029, 2048),
+              (synth.INT8_ROW, 40, 8192), (synth.INT4_G64, 3, 192)]
     gemvs = [synth.make_gemv(f"g{i}", f, M, K, B, 6, i, "o") for i, (f, M, K) in enumerate(shapes)]
     ys = _grouped(gemvs, B)
     for g, y in zip(gemvs, ys):
@@ -367,8 +371,7 @@ MFMA_SHAPES = [(2048, 2048), (17, 4096), (4100, 1024), (16, 512), (40000, 1024),
 
 @pytest.mark.parametrize("B", [3, 5, 8])
 @pytest.mark.parametrize("M,K", MFMA_SHAPES, ids=[f"{m}x{k}" for m, k in MFMA_SHAPES])
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128],
-                         ids=["bf16", "int8", "q4_0", "int4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FMT_IDS)
 def test_mfma_path_shapes(fmt, M, K, B):
     g = synth.make_gemv("t", fmt, M, K, B, 9, (M + K) % 991, "gate_up")
     y = gpu_gemv(fmt, g.w, g.s, g.x, M, K, B)
@@ -376,7 +379,7 @@ def test_mfma_path_shapes(fmt, M, K, B):
     assert_parity(fmt, g.w, g.s, g.x, M, K, B, y, rows=sample_rows(M), what=f"M={M} K={K} B={B}")
 
 
-@pytest.mark.parametrize("fmt", [qg.Q4_0_G32, qg.INT4_G128], ids=["q4_0", "int4"])
+@pytest.mark.parametrize("fmt", [qg.Q4_0_G32, qg.INT4_G128, qg.INT4_G64], ids=["q4_0", "int4", "int4_g64"])
 def test_mfma_path_all_codes_extreme(fmt):
     """Every 4-bit code 0 or 15 with the largest generated scale and x of one sign:
     the largest partial sums and the largest offset-term cancellation the
@@ -502,7 +505,7 @@ def _quant_edge_inputs():
     return w
 
 
-@pytest.mark.parametrize("fmt", [qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128], ids=["int8", "q4_0", "int4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS[1:], ids=FMT_IDS[1:])
 def test_device_quantizer_bit_exact(fmt):
     """qgemv_quantize against the oracle quantizer (and so against qgemv_pack, which the CPU
     tests hold bit-exact to it) on edge groups and on the 2048x2048 workload shape."""
@@ -536,7 +539,7 @@ def test_device_quantizer_then_run():
     rng = np.random.default_rng(17)
     M, K = 1024, 2048
     wbf = synth.bf16_normal(rng, (M, K), 0.02)
-    for fmt in (qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128):
+    for fmt in ALL_FMTS[1:]:
         codes, scales, err = gpu_quantize(fmt, wbf, M, K)
         assert err == 0
         for B in (1, 8):
@@ -562,15 +565,14 @@ INV_SHAPES = [(2048, 2048), (4100, 1024), (32000, 2048), (65, 384), (1000, 5632)
 
 
 @pytest.mark.parametrize("M,K", INV_SHAPES, ids=[f"{m}x{k}" for m, k in INV_SHAPES])
-@pytest.mark.parametrize("fmt", [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128],
-                         ids=["bf16", "int8", "q4_0", "int4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FMT_IDS)
 def test_batch_invariant_rows_bitwise_equal(fmt, M, K):
     """With the batch-invariant flag, row b of a batch-B call equals the
     batch-1 call on x[b] bit for bit, for B = 8, 5, 3, 2 (and matches the
     oracle within the usual bound)."""
-    if K % synth.GROUP[fmt]:
+    if K % synth.K_ALIGN[fmt]:
         K = (K // 128 + 1) * 128
-    if 8 * K * 2 + (K if fmt in (qg.Q4_0_G32, qg.INT4_G128) else 0) > 160 * 1024:
+    if 8 * K * 2 + (K if fmt in NIBBLE_FMTS else 0) > 160 * 1024:
         pytest.skip("x of 8 rows does not fit in LDS")
     g = synth.make_gemv("t", fmt, M, K, 8, 13, (3 * M + K) % 983, "gate_up")
     Wd = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
