@@ -19,6 +19,7 @@ Modules
   quantize  the bf16 -> int8-g32 / 4-bit quantizers (largest-magnitude
             value maps to code -8)
   argmax    the first index of the maximum, with NaN handling
+  attention grouped-query decode attention over a bf16 KV cache
   fused     the operations fused on either side of a GEMV: RMSNorm of the
             float32 residual stream into the bf16 GEMV input, the residual
             add, SwiGLU of paired gate/up rows, and their tolerances
@@ -26,7 +27,9 @@ Modules
 Parity status: every function here is pinned by tests that do not re-use it
 (library conversions, hand-built blocks with closed-form dot products,
 exact rational brute force, quantizer error bounds, torch's rms_norm and
-silu, closed-form normalizations and activations); there is no unpinned
+silu, closed-form normalizations and activations, torch's
+scaled_dot_product_attention and closed-form attention cases); there is no
+unpinned
 function.
 """
 from .formats import (BF16, INT8_G32, Q4_0_G32, INT4_G128, INT8_ROW, INT4_G64, GROUP, K_ALIGN,

@@ -192,3 +192,31 @@ def f32_logits_with_ties(rng: np.random.Generator, B: int, V: int) -> np.ndarray
         pos = np.sort(rng.choice(V, size=min(3, V), replace=False))
         a[b, pos] = hi
     return a
+
+
+# ------------------------------------------------------- decode attention
+@dataclasses.dataclass
+class Attention:
+    """Inputs of one grouped-query decode-attention call: q float32 [B][n_q][d];
+    k, v bf16 bits [B][n_kv][max_ctx][d] (positions past a sequence's length
+    hold random values that must not be read); lens int32 [B]."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    lens: np.ndarray
+    scale: float
+
+
+def make_attention(B: int, n_q: int, n_kv: int, d: int, max_ctx: int, seed: int,
+                   lens=None) -> Attention:
+    """q, k, v ~ N(0, 1) (k, v rounded to bf16); a length mix per sequence:
+    uniform in [max_ctx / 4, max_ctx] with the first sequence at max_ctx,
+    unless lens is given."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, n_q, d), dtype=np.float32)
+    k = bf16_normal(rng, (B, n_kv, max_ctx, d), 1.0)
+    v = bf16_normal(rng, (B, n_kv, max_ctx, d), 1.0)
+    if lens is None:
+        lens = rng.integers(max(1, max_ctx // 4), max_ctx + 1, size=B)
+        lens[0] = max_ctx
+    return Attention(q, k, v, np.asarray(lens, dtype=np.int32), 1.0 / float(np.sqrt(d)))
