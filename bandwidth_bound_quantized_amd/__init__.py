@@ -61,6 +61,9 @@ def _load() -> ctypes.CDLL:
         "qgemv_run_flags": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_vp]),
         "qgemv_run_fused": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_vp]),
         "qgemv_run_grouped": (c_int, [c_vp, c_int, c_int, c_vp]),
+        "qgemv_attention_workspace_size": (c_int, [c_int, c_int, c_int, c_int, c_i64, ctypes.POINTER(c_sz)]),
+        "qgemv_attention_decode": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_i64,
+                                           ctypes.c_float, c_vp, c_vp]),
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
         "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
@@ -77,7 +80,7 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_flags",
-           "qgemv_run_fused", "qgemv_run_grouped",
+           "qgemv_run_fused", "qgemv_run_grouped", "qgemv_attention_workspace_size", "qgemv_attention_decode",
            "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
@@ -190,6 +193,39 @@ def run_ptr(fmt: int, wp: int, sp: Optional[int], xp: int, yp: int, M: int, K: i
     st = _lib.qgemv_run(fmt, wp, sp, xp, yp, M, K, batch, stream_handle)
     if st != OK:
         raise QgemvError(st, "qgemv_run")
+
+
+def attention_workspace_size(batch: int, n_q: int, n_kv: int, head_dim: int, max_ctx: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.qgemv_attention_workspace_size(batch, n_q, n_kv, head_dim, max_ctx, ctypes.byref(n)),
+           "qgemv_attention_workspace_size")
+    return n.value
+
+
+def attention_workspace(batch: int, n_q: int, n_kv: int, head_dim: int, max_ctx: int, device="cuda"):
+    """A zero-filled workspace for attention_decode (its counters are left zero by every call)."""
+    import torch
+    n = attention_workspace_size(batch, n_q, n_kv, head_dim, max_ctx)
+    return torch.zeros((n + 15) // 16 * 4, dtype=torch.int32, device=device)
+
+
+def attention_decode(q, k_cache, v_cache, ctx_lens, out, batch: int, n_q: int, n_kv: int, head_dim: int,
+                     max_ctx: int, scale: float, ws, stream=None) -> None:
+    """qgemv_attention_decode: grouped-query decode attention over a bf16 KV cache."""
+    import torch
+    qp = _dev_ptr(q, "q", torch.float32)
+    kp = _dev_ptr(k_cache, "k_cache", (torch.int16, torch.uint16, torch.bfloat16))
+    vp = _dev_ptr(v_cache, "v_cache", (torch.int16, torch.uint16, torch.bfloat16))
+    lp = _dev_ptr(ctx_lens, "ctx_lens", torch.int32)
+    op = _dev_ptr(out, "out", torch.float32)
+    wp = _dev_ptr(ws, "ws")
+    if (q.numel() < batch * n_q * head_dim or out.numel() < batch * n_q * head_dim
+            or k_cache.numel() < batch * n_kv * max_ctx * head_dim or v_cache.numel() < batch * n_kv * max_ctx * head_dim
+            or ctx_lens.numel() < batch
+            or ws.numel() * ws.element_size() < attention_workspace_size(batch, n_q, n_kv, head_dim, max_ctx)):
+        raise ValueError("a buffer is too small for the shape")
+    _check(_lib.qgemv_attention_decode(qp, kp, vp, lp, op, batch, n_q, n_kv, head_dim, max_ctx, scale, wp,
+                                       _stream_handle(stream)), "qgemv_attention_decode")
 
 
 class Fusion(ctypes.Structure):

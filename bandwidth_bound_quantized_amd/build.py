@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemv.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "qgemv")
 
-SOURCES = ["gemv.hip", "argmax.hip", "quantize.hip", "stream_read.hip", "qgemv_api.cpp"]
+SOURCES = ["gemv.hip", "argmax.hip", "quantize.hip", "attention.hip", "stream_read.hip", "qgemv_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

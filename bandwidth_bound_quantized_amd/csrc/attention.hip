@@ -1,0 +1,338 @@
+// Grouped-query decode attention over a bf16 KV cache (gfx950), split over
+// the context ("infer": split-KV decode attention, one block per key/value
+// head serving its query heads, splits to fill the GPU at long context, then
+// a merge; the Rust page: online softmax over 64-position blocks, query
+// heads that share a key/value head processed together so the cache is read
+// once per key/value head).
+//
+// out[b][h][:] = sum_t p_t v[b][h/G][t][:] / sum_t p_t,
+// p_t = exp(scale * q[b][h] . k[b][h/G][t] - max), t < L_b.
+//
+// Work: one workgroup (4 waves) per (sequence b, key/value head, split s);
+// split s covers P consecutive positions, taken by the waves in blocks of BP
+// positions round-robin. Inside a wave, SUB adjacent lanes share a position
+// and each owns DL = 64 / G consecutive head dims, so every lane keeps the G
+// query heads' slices of q (G * DL = 64 floats) and of the output
+// accumulator (64 floats) in registers; a round covers PP = 64 / SUB
+// positions, whose K (then V) rows are one contiguous stretch of the cache.
+// Scores: DL-long dot products per lane, summed over the SUB lanes of the
+// position; softmax online per block (the block's maximum across the wave,
+// one rescale of the accumulator per block). K/V are read through buffer
+// resources sized to the sequence's L_b positions: positions past it read
+// as zero and are masked, so nothing past the valid cache is touched.
+// Float32 arithmetic throughout; exponentials in base 2 with log2(e) folded
+// into q.
+//
+// The waves of a workgroup meet in LDS; with more than one split, each
+// workgroup writes its (max, sum, accumulator) for its G heads to the
+// caller's workspace, and the last split of a (b, head) to arrive (a counter
+// in the workspace, reset by it) merges them and writes out.
+#include <math.h>
+#include <algorithm>
+#include <type_traits>
+
+#include "qgemv_internal.h"
+#include "qgemv.h"
+
+namespace qgemv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, int G>
+struct AttnShape {
+  static constexpr int DL = 64 / G;                     // head dims per lane
+  static constexpr int SUB = D / DL;                    // lanes per position
+  static constexpr int PP = 64 / SUB;                   // positions per round
+  static constexpr int BP0 = 131072 / (G * G * D);      // at most 32 score registers
+  static constexpr int BP = BP0 < 64 ? BP0 : 64;        // positions per softmax block
+  static constexpr int R = BP / PP;                     // rounds per block
+  static_assert(DL >= 8 && DL % 8 == 0 && SUB >= 1 && SUB <= 16 && R >= 1, "shape");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// DL bf16 values (DL / 8 16-byte loads) at byte offset voff of the resource
+template <int DL>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u32x4 (&w)[DL / 8]) {
+#pragma unroll
+  for (int i = 0; i < DL / 8; ++i)
+    w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, 0, 0));
+}
+
+__device__ __forceinline__ float lo_f(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_f(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+template <int W>
+__device__ __forceinline__ float sum_lanes(float x) {        // over lane bits below log2(W)
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <int FROM>
+__device__ __forceinline__ float max_lanes_from(float x) {   // over lane bits >= log2(FROM)
+#pragma unroll
+  for (int o = FROM; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+template <int FROM>
+__device__ __forceinline__ float sum_lanes_from(float x) {
+#pragma unroll
+  for (int o = FROM; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Per-split partial record in the workspace: m[G], l[G], acc[G][D] (floats).
+template <int D, int G>
+constexpr int part_floats() { return 2 * G + G * D; }
+
+template <int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ lens, float* __restrict__ out, int n_kv, int max_ctx, int S, int P,
+    float scale, uint32_t* __restrict__ counters, float* __restrict__ parts) {
+  using A = AttnShape<D, G>;
+  constexpr int DL = A::DL, SUB = A::SUB, PP = A::PP, BP = A::BP, R = A::R;
+  __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
+  __shared__ float sh_acc[kAttnWaves][G][D];
+  __shared__ int sh_last;
+
+  const int s = blockIdx.x % S;
+  const int bh = blockIdx.x / S;                        // b * n_kv + kv head
+  const int b = bh / n_kv, kvh = bh - b * n_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int sub = lane % SUB, pr = lane / SUB;          // dims slice, position in the round
+  const int L = min(max(lens[b], 1), max_ctx);
+
+  // q slices of the G heads, pre-multiplied by scale * log2(e)
+  float qr[G][DL];
+  const float qs = scale * kLog2e;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* qh = q + (static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + sub * DL;
+#pragma unroll
+    for (int j = 0; j < DL; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(qh + j);
+      qr[g][j] = v.x * qs; qr[g][j + 1] = v.y * qs; qr[g][j + 2] = v.z * qs; qr[g][j + 3] = v.w * qs;
+    }
+  }
+  float acc[G][DL];
+  float m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DL; ++j) acc[g][j] = 0.f;
+  }
+
+  // this (b, kv head)'s cache rows, sized to L positions
+  const size_t head_off = static_cast<size_t>(bh) * max_ctx * D;
+  const uint32_t nbytes = static_cast<uint32_t>(L) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = attn_rsrc(kc + head_off, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = attn_rsrc(vc + head_off, nbytes);
+
+  const int p0 = s * P, p1 = min(p0 + P, L);
+  for (int t0 = p0 + wave * BP; t0 < p1; t0 += kAttnWaves * BP) {
+    // scores of the block's positions (log2 units), -inf past L
+    float sc[R][G];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = t0 + r * PP + pr;
+      u32x4 w[DL / 8];
+      load_row<DL>(rk, static_cast<uint32_t>(t) * D * 2 + sub * DL * 2, w);
+      float dot[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) dot[g] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DL / 8; ++i) {
+        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float k0 = lo_f(wd[c]), k1 = hi_f(wd[c]);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            dot[g] = __builtin_fmaf(qr[g][8 * i + 2 * c], k0, dot[g]);
+            dot[g] = __builtin_fmaf(qr[g][8 * i + 2 * c + 1], k1, dot[g]);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float tot = sum_lanes<SUB>(dot[g]);
+        sc[r][g] = t < p1 ? tot : -INFINITY;
+      }
+    }
+    // online softmax: the block's maximum over the wave, one rescale
+    float pw[R][G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float bm = sc[0][g];
+#pragma unroll
+      for (int r = 1; r < R; ++r) bm = fmaxf(bm, sc[r][g]);
+      bm = max_lanes_from<SUB>(bm);
+      const float mn = fmaxf(m[g], bm);                  // finite: the block has a valid position
+      const float alpha = exp2f(m[g] - mn);              // 0 on the first block (m = -inf)
+      m[g] = mn;
+      l[g] *= alpha;
+#pragma unroll
+      for (int j = 0; j < DL; ++j) acc[g][j] *= alpha;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        pw[r][g] = exp2f(sc[r][g] - mn);                 // 0 past L
+        l[g] += pw[r][g];
+      }
+    }
+    // values
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = t0 + r * PP + pr;
+      u32x4 w[DL / 8];
+      load_row<DL>(rv, static_cast<uint32_t>(t) * D * 2 + sub * DL * 2, w);
+#pragma unroll
+      for (int i = 0; i < DL / 8; ++i) {
+        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float v0 = lo_f(wd[c]), v1 = hi_f(wd[c]);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            acc[g][8 * i + 2 * c] = __builtin_fmaf(pw[r][g], v0, acc[g][8 * i + 2 * c]);
+            acc[g][8 * i + 2 * c + 1] = __builtin_fmaf(pw[r][g], v1, acc[g][8 * i + 2 * c + 1]);
+          }
+        }
+      }
+    }
+  }
+
+  // the wave's totals: accumulators over its position lanes, sums over all
+  // lanes (each position counted by its SUB lanes)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l[g] = sum_lanes_from<1>(l[g]) * (1.f / SUB);
+#pragma unroll
+    for (int j = 0; j < DL; ++j) acc[g][j] = sum_lanes_from<SUB>(acc[g][j]);
+  }
+  if (lane < SUB) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < DL; ++j) sh_acc[wave][g][sub * DL + j] = acc[g][j];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) { sh_m[wave][g] = m[g]; sh_l[wave][g] = l[g]; }
+  }
+  __syncthreads();
+
+  // the workgroup's (max, sum, accumulator) per head: waves in order
+  const int tid = threadIdx.x;
+  for (int e = tid; e < G * D; e += kAttnThreads) {
+    const int g = e / D, j = e - g * D;
+    float M = sh_m[0][g];
+#pragma unroll
+    for (int w2 = 1; w2 < kAttnWaves; ++w2) M = fmaxf(M, sh_m[w2][g]);
+    float a = 0.f, den = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
+      const float f = sh_m[w2][g] == -INFINITY ? 0.f : exp2f(sh_m[w2][g] - M);
+      a += f * sh_acc[w2][g][j];
+      den += f * sh_l[w2][g];
+    }
+    if (S == 1) {
+      out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / den;
+    } else {
+      float* rec = parts + (static_cast<size_t>(bh) * S + s) * part_floats<D, G>();
+      rec[2 * G + e] = a;
+      if (j == 0) { rec[g] = M; rec[G + g] = den; }
+    }
+  }
+  if (S == 1) return;
+
+  // the last split of (b, head) to arrive merges all S records
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t prev = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == static_cast<uint32_t>(S - 1);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();
+  const float* rec0 = parts + static_cast<size_t>(bh) * S * part_floats<D, G>();
+  for (int e = tid; e < G * D; e += kAttnThreads) {
+    const int g = e / D, j = e - g * D;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, __builtin_nontemporal_load(rec0 + s2 * part_floats<D, G>() + g));
+    float a = 0.f, den = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float* rec = rec0 + s2 * part_floats<D, G>();
+      const float ms = __builtin_nontemporal_load(rec + g);
+      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      a += f * __builtin_nontemporal_load(rec + 2 * G + e);
+      den += f * __builtin_nontemporal_load(rec + G + g);
+    }
+    out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / den;
+  }
+  if (tid == 0) __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int G>
+hipError_t launch_attn_dg(const AttnArgs& a, hipStream_t st) {
+  const AttnPlan p = attention_plan(a.batch, a.n_q, a.n_kv, a.head_dim, a.max_ctx);
+  const int grid = a.batch * a.n_kv * p.splits;
+  uint32_t* counters = static_cast<uint32_t*>(a.ws);
+  float* parts = reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) + p.counter_bytes);
+  attn_decode_kernel<D, G><<<grid, kAttnThreads, 0, st>>>(a.q, a.k, a.v, a.lens, a.out, a.n_kv,
+                                                          static_cast<int>(a.max_ctx), p.splits, p.positions,
+                                                          a.scale, counters, parts);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
+  switch (a.n_q / a.n_kv) {
+    case 1: return launch_attn_dg<D, 1>(a, st);
+    case 2: return launch_attn_dg<D, 2>(a, st);
+    case 4: return launch_attn_dg<D, 4>(a, st);
+    default: return launch_attn_dg<D, 8>(a, st);
+  }
+}
+
+}  // namespace
+
+// Splits: enough workgroups for about two per CU of a 256-CU device (the
+// same for every device, so the workspace size is a function of the shape
+// alone), each at least one block per wave; positions per split a multiple
+// of the waves' blocks.
+AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx) {
+  const int G = n_q / n_kv;
+  const int bp = std::min(64, 131072 / (G * G * head_dim));
+  const int64_t unit = static_cast<int64_t>(kAttnWaves) * bp;       // positions of one round of blocks
+  const int64_t units = (max_ctx + unit - 1) / unit;
+  const int64_t want = std::max<int64_t>(1, 512 / std::max(1, batch * n_kv));
+  AttnPlan p;
+  p.splits = static_cast<int>(std::min<int64_t>(units, want));
+  const int64_t per = (units + p.splits - 1) / p.splits;
+  p.positions = static_cast<int>(per * unit);
+  p.splits = static_cast<int>((max_ctx + p.positions - 1) / p.positions);
+  p.counter_bytes = ((static_cast<size_t>(batch) * n_kv * 4 + 255) / 256) * 256;
+  p.part_bytes = p.splits > 1 ? static_cast<size_t>(batch) * n_kv * p.splits * (2 * G + G * head_dim) * 4 : 0;
+  return p;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) return launch_attn_d<64>(a, stream);
+  return launch_attn_d<128>(a, stream);
+}
+
+}  // namespace qgemv

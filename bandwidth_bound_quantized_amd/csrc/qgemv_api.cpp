@@ -316,6 +316,43 @@ int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16
   return record_hip(qgemv::launch_gemv_fused(a, fu, f->argmax_ws, f->argmax_idx, static_cast<hipStream_t>(stream)));
 }
 
+static int check_attention_shape(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx) {
+  if (batch < 1 || n_kv < 1 || n_q < 1 || n_q % n_kv != 0) return QGEMV_ESHAPE;
+  const int G = n_q / n_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return QGEMV_ESHAPE;
+  if (head_dim != 64 && head_dim != 128) return QGEMV_ESHAPE;
+  // (a block may address up to 64 positions past the context: keep the byte
+  // offsets of those in 32 bits too)
+  if (max_ctx < 1 || (max_ctx + 64) * head_dim * 2 >= (int64_t(1) << 32)) return QGEMV_ESHAPE;
+  const qgemv::AttnPlan p = qgemv::attention_plan(batch, n_q, n_kv, head_dim, max_ctx);
+  if (static_cast<int64_t>(batch) * n_kv * p.splits >= (int64_t(1) << 31)) return QGEMV_ESHAPE;
+  return QGEMV_OK;
+}
+
+int qgemv_attention_workspace_size(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx,
+                                   size_t* bytes) {
+  if (!bytes) return QGEMV_EINVAL;
+  const int st = check_attention_shape(batch, n_q, n_kv, head_dim, max_ctx);
+  if (st) return st;
+  const qgemv::AttnPlan p = qgemv::attention_plan(batch, n_q, n_kv, head_dim, max_ctx);
+  *bytes = p.counter_bytes + p.part_bytes;
+  return QGEMV_OK;
+}
+
+int qgemv_attention_decode(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* ctx_lens, float* out, int batch, int n_q, int n_kv,
+                           int head_dim, int64_t max_ctx, float scale, void* ws, void* stream) {
+  if (!q || !k_cache || !v_cache || !ctx_lens || !out || !ws) return QGEMV_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return QGEMV_EINVAL;
+  const int st = check_attention_shape(batch, n_q, n_kv, head_dim, max_ctx);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(ctx_lens, 4) || !aligned(ws, 16))
+    return QGEMV_EALIGN;
+  qgemv::AttnArgs a{q, k_cache, v_cache, ctx_lens, out, batch, n_q, n_kv, head_dim, max_ctx, scale, ws};
+  return record_hip(qgemv::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
 int qgemv_run_flags(int fmt, const void* W, const uint16_t* scales, const uint16_t* x, float* y,
                     int64_t M, int64_t K, int batch, int flags, void* stream) {
   if (flags & ~QGEMV_FLAG_BATCH_INVARIANT) return QGEMV_EINVAL;

@@ -96,6 +96,30 @@ hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws
 hipError_t launch_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
                            int32_t* err, hipStream_t stream);
 
+// Grouped-query decode attention (qgemv_attention_decode); shapes validated.
+struct AttnArgs {
+  const float* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* lens;
+  float* out;
+  int batch, n_q, n_kv, head_dim;
+  int64_t max_ctx;
+  float scale;
+  void* ws;
+};
+// How the context is split: `splits` workgroups per (sequence, key/value
+// head), `positions` each; the workspace holds counter_bytes of arrival
+// counters (zero between calls) and part_bytes of per-split records.
+struct AttnPlan {
+  int splits = 1;
+  int positions = 0;
+  size_t counter_bytes = 0;
+  size_t part_bytes = 0;
+};
+AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
 // Streaming-read measurement kernel.
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
                               hipStream_t stream);

@@ -319,6 +319,51 @@ int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16
                     int64_t M, int64_t K, int batch, const qgemv_fusion* fusion, void* stream);
 
 /*
+ * Grouped-query decode attention - the other bandwidth-bound kernel of a
+ * decode step: every query head compares its query with the keys of all
+ * earlier positions of its sequence in the KV cache and takes the
+ * softmax-weighted average of their values; groups of G = n_q / n_kv query
+ * heads share one key/value head, query head h reading key/value head h / G
+ * (the Rust page: layer walk-through and its attention rounds - online
+ * softmax over 64-position blocks, query heads of one key/value head
+ * processed together; "infer": split-KV decode attention with one block per
+ * key/value head and a merge of the splits, bf16 KV cache).
+ *   out[b][h][j] = sum_t p_t v[b][h/G][t][j] / sum_t p_t,
+ *   p_t = exp(scale * sum_j q[b][h][j] k[b][h/G][t][j] - max_t(...)),
+ *   0 <= t < ctx_lens[b].
+ *
+ * qgemv_attention_workspace_size - bytes of device workspace a call with
+ * this shape needs (*bytes; host only, no HIP calls). The workspace must be
+ * all zero before its first use; every call leaves its counters zero again.
+ * Calls that may run concurrently need distinct workspaces.
+ * Errors: EINVAL (null bytes), ESHAPE (as below).
+ */
+int qgemv_attention_workspace_size(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx,
+                                   size_t* bytes);
+
+/*
+ * qgemv_attention_decode - one decode step's attention for `batch`
+ * sequences. Device pointers:
+ *   q        float32 [batch][n_q][head_dim], 16-byte aligned;
+ *   k_cache, v_cache  bf16 bits [batch][n_kv][max_ctx][head_dim], 16-byte
+ *            aligned; only positions < ctx_lens[b] of sequence b are read;
+ *   ctx_lens int32 [batch], 4-byte aligned, each in 1..max_ctx (values
+ *            outside are clamped into that range; on the device so that a
+ *            captured graph stays valid as positions advance);
+ *   out      float32 [batch][n_q][head_dim], 16-byte aligned, overwritten;
+ *   ws       qgemv_attention_workspace_size bytes, 16-byte aligned.
+ * Shapes: batch >= 1, n_kv >= 1, n_q = G * n_kv with G in {1, 2, 4, 8},
+ * head_dim 64 or 128, 1 <= max_ctx with (max_ctx + 64) * head_dim * 2 < 2^32;
+ * scale > 0 and finite (1/sqrt(head_dim) for Llama models).
+ * Float32 arithmetic on the bf16 cache values. One launch; asynchronous on
+ * `stream`. Errors: EINVAL (null pointer, non-finite or non-positive
+ * scale), ESHAPE, EALIGN, EHIP.
+ */
+int qgemv_attention_decode(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* ctx_lens, float* out, int batch, int n_q, int n_kv,
+                           int head_dim, int64_t max_ctx, float scale, void* ws, void* stream);
+
+/*
  * qgemv_stream_read - measurement helper: read `bytes` bytes of device
  * memory at `buf` once with 16-byte loads and write one checksum word per
  * workgroup to sink[0 .. grid-1] (so the reads cannot be elided). This is the

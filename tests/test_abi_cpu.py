@@ -209,6 +209,29 @@ def test_run_fused_validation_errors_before_any_launch():
     assert _fused(argmax_idx=FAKE, argmax_ws=FAKE + 4) == qg.EALIGN
 
 
+def test_attention_workspace_and_validation():
+    L = qg.lib()
+    n = ctypes.c_size_t()
+    # Llama-3.2-1B heads at context 2048: 8 splits of 256 positions per key/value head
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, ctypes.byref(n)) == qg.OK
+    assert n.value == 256 + 8 * 8 * (2 * 4 + 4 * 64) * 4
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, None) == qg.EINVAL
+    for args in ((1, 24, 8, 64, 2048), (1, 32, 8, 96, 2048), (1, 32, 8, 64, 0), (0, 32, 8, 64, 16),
+                 (1, 32, 0, 64, 16), (1, 32, 8, 128, 1 << 24)):
+        assert L.qgemv_attention_workspace_size(*args, ctypes.byref(n)) == qg.ESHAPE, args
+
+    def call(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, scale=0.125, ws=FAKE, n_q=32, d=64):
+        return L.qgemv_attention_decode(q, k, v, lens, out, 1, n_q, 8, d, 2048, scale, ws, None)
+    assert call(q=None) == qg.EINVAL
+    assert call(ws=None) == qg.EINVAL
+    assert call(scale=0.0) == qg.EINVAL
+    assert call(scale=float("inf")) == qg.EINVAL
+    assert call(n_q=12) == qg.ESHAPE
+    assert call(d=80) == qg.ESHAPE
+    assert call(q=FAKE + 4) == qg.EALIGN
+    assert call(lens=FAKE + 2) == qg.EALIGN
+
+
 def test_run_validation_errors_before_any_launch():
     assert _run(fmt=7) == qg.EINVAL
     assert _run(W=None) == qg.EINVAL
