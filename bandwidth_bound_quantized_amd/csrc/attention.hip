@@ -39,9 +39,22 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnWaves = 4;
+#ifndef QGEMV_ATTN_WAVES
+#define QGEMV_ATTN_WAVES 4        // waves per workgroup
+#endif
+#ifndef QGEMV_ATTN_MIN_BLOCKS
+#define QGEMV_ATTN_MIN_BLOCKS 2   // blocks per wave before the context is split further
+#endif
+#ifndef QGEMV_ATTN_TARGET_WGS
+#define QGEMV_ATTN_TARGET_WGS 256 // workgroups worth splitting for
+#endif
+#ifndef QGEMV_ATTN_MAX_SPLITS
+#define QGEMV_ATTN_MAX_SPLITS 32  // splits per (sequence, key/value head)
+#endif
+constexpr int kAttnWaves = QGEMV_ATTN_WAVES;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplits = QGEMV_ATTN_MAX_SPLITS;
 
 template <int D, int G>
 struct AttnShape {
@@ -49,7 +62,9 @@ struct AttnShape {
   static constexpr int SUB = D / DL;                    // lanes per position
   static constexpr int PP = 64 / SUB;                   // positions per round
   static constexpr int BP0 = 131072 / (G * G * D);      // at most 32 score registers
-  static constexpr int BP = BP0 < 64 ? BP0 : 64;        // positions per softmax block
+  static constexpr int BPC = G * D >= 1024 ? 8 : G >= 8 ? 16 : 32;   // (two blocks' loads in flight)
+  static constexpr int BP1 = BP0 < BPC ? BP0 : BPC;
+  static constexpr int BP = BP1 > PP ? BP1 : PP;        // positions per softmax block
   static constexpr int R = BP / PP;                     // rounds per block
   static_assert(DL >= 8 && DL % 8 == 0 && SUB >= 1 && SUB <= 16 && R >= 1, "shape");
 };
@@ -69,26 +84,53 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t vof
 __device__ __forceinline__ float lo_f(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float hi_f(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+// Cross-lane reductions without LDS: DPP inside a 16-lane row, permlane
+// swaps across rows. With both operands the same register, a 32-lane swap
+// returns rows (0,1,0,1) and (2,3,2,3): combining them is a butterfly over
+// lane bit 5; a 16-lane swap does the same over bit 4.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float across32(float x, bool mx) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return mx ? fmaxf(__uint_as_float(a), __uint_as_float(b)) : __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float across16(float x, bool mx) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return mx ? fmaxf(__uint_as_float(a), __uint_as_float(b)) : __uint_as_float(a) + __uint_as_float(b);
+}
+
+// sum over the W lanes of each aligned group of W (every lane gets it)
 template <int W>
-__device__ __forceinline__ float sum_lanes(float x) {        // over lane bits below log2(W)
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) x += __shfl_xor(x, o);
+__device__ __forceinline__ float sum_lanes(float x) {
+  if constexpr (W >= 2) x += dppf<0xB1>(x);             // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) x += dppf<0x4E>(x);             // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) x += dppf<0x141>(x);            // row_half_mirror
+  if constexpr (W >= 16) x += dppf<0x140>(x);           // row_mirror
+  static_assert(W <= 16, "W");
   return x;
 }
 
-template <int FROM>
-__device__ __forceinline__ float max_lanes_from(float x) {   // over lane bits >= log2(FROM)
-#pragma unroll
-  for (int o = FROM; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+// reduce over the lanes that agree in the lane bits below log2(FROM): row
+// rotations by FROM, 2 FROM, .. 8 cover a row's lanes of one residue, then
+// the two row butterflies
+template <int FROM, bool MAX>
+__device__ __forceinline__ float reduce_from(float x) {
+  if constexpr (FROM <= 1) x = MAX ? fmaxf(x, dppf<0x121>(x)) : x + dppf<0x121>(x);
+  if constexpr (FROM <= 2) x = MAX ? fmaxf(x, dppf<0x122>(x)) : x + dppf<0x122>(x);
+  if constexpr (FROM <= 4) x = MAX ? fmaxf(x, dppf<0x124>(x)) : x + dppf<0x124>(x);
+  if constexpr (FROM <= 8) x = MAX ? fmaxf(x, dppf<0x128>(x)) : x + dppf<0x128>(x);
+  x = across16(x, MAX);
+  x = across32(x, MAX);
   return x;
 }
-
 template <int FROM>
-__device__ __forceinline__ float sum_lanes_from(float x) {
-#pragma unroll
-  for (int o = FROM; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float max_lanes_from(float x) { return reduce_from<FROM, true>(x); }
+template <int FROM>
+__device__ __forceinline__ float sum_lanes_from(float x) { return reduce_from<FROM, false>(x); }
 
 // Per-split partial record in the workspace: m[G], l[G], acc[G][D] (floats).
 template <int D, int G>
@@ -101,8 +143,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
     float scale, uint32_t* __restrict__ counters, float* __restrict__ parts) {
   using A = AttnShape<D, G>;
   constexpr int DL = A::DL, SUB = A::SUB, PP = A::PP, BP = A::BP, R = A::R;
+  // values: a lane owns 8 head dims of one position; VPI positions per load
+  // instruction, VI instructions per block
+  constexpr int VLN = D / 8, VPI = 64 / VLN, VI = BP / VPI;
+  static_assert(BP % VPI == 0, "block");
+  __shared__ float sh_p[kAttnWaves][BP][G];
   __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
   __shared__ float sh_acc[kAttnWaves][G][D];
+  __shared__ float sh_f[kMaxSplits][G], sh_sl[kMaxSplits][G];
+  __shared__ float sh_den[G];
   __shared__ int sh_last;
 
   const int s = blockIdx.x % S;
@@ -110,7 +159,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
   const int b = bh / n_kv, kvh = bh - b * n_kv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int sub = lane % SUB, pr = lane / SUB;          // dims slice, position in the round
+  const int sub = lane % SUB, pr = lane / SUB;          // keys: dims slice, position in the round
+  const int vl = lane % VLN, vp = lane / VLN;           // values: 8-dim slice, position in the load
   const int L = min(max(lens[b], 1), max_ctx);
 
   // q slices of the G heads, pre-multiplied by scale * log2(e)
@@ -125,37 +175,50 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
       qr[g][j] = v.x * qs; qr[g][j + 1] = v.y * qs; qr[g][j + 2] = v.z * qs; qr[g][j + 3] = v.w * qs;
     }
   }
-  float acc[G][DL];
+  float acc[G][8];
   float m[G], l[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
 #pragma unroll
-    for (int j = 0; j < DL; ++j) acc[g][j] = 0.f;
+    for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
   }
 
-  // this (b, kv head)'s cache rows, sized to L positions
-  const size_t head_off = static_cast<size_t>(bh) * max_ctx * D;
-  const uint32_t nbytes = static_cast<uint32_t>(L) * D * 2;
+  // this (b, kv head)'s cache rows of this split, [p0, p0 + P) cut at
+  // max_ctx (not at the sequence's length, so that the first loads need not
+  // wait for it): positions past it (a prefetch of the next block) read as
+  // zero and move no data; positions past the length are masked (scores) and
+  // zeroed (values) in registers
+  const int p0 = s * P, p1 = min(p0 + P, L);
+  const int pe = min(p0 + P, max_ctx);
+  const size_t head_off = static_cast<size_t>(bh) * max_ctx * D + static_cast<size_t>(p0) * D;
+  const uint32_t nbytes = static_cast<uint32_t>(pe - p0) * D * 2;
   const __amdgpu_buffer_rsrc_t rk = attn_rsrc(kc + head_off, nbytes);
   const __amdgpu_buffer_rsrc_t rv = attn_rsrc(vc + head_off, nbytes);
 
-  const int p0 = s * P, p1 = min(p0 + P, L);
-  for (int t0 = p0 + wave * BP; t0 < p1; t0 += kAttnWaves * BP) {
-    // scores of the block's positions (log2 units), -inf past L
+  // a block's keys (key-lane layout) and values (value-lane layout); u0 is
+  // the block's first position relative to p0
+  auto load_blk = [&](int u0, u32x4 (&kw)[R][DL / 8], u32x4 (&vw)[VI]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      load_row<DL>(rk, static_cast<uint32_t>(u0 + r * PP + pr) * D * 2 + sub * DL * 2, kw[r]);
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      vw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rv, static_cast<uint32_t>(u0 + i * VPI + vp) * D * 2 + vl * 16, 0, 0));
+  };
+  auto do_blk = [&](int u0, const u32x4 (&kw)[R][DL / 8], const u32x4 (&vw)[VI]) {
+    // scores (log2 units), -inf past the split
     float sc[R][G];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int t = t0 + r * PP + pr;
-      u32x4 w[DL / 8];
-      load_row<DL>(rk, static_cast<uint32_t>(t) * D * 2 + sub * DL * 2, w);
       float dot[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) dot[g] = 0.f;
 #pragma unroll
       for (int i = 0; i < DL / 8; ++i) {
-        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        const uint32_t wd[4] = {kw[r][i].x, kw[r][i].y, kw[r][i].z, kw[r][i].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float k0 = lo_f(wd[c]), k1 = hi_f(wd[c]);
@@ -166,14 +229,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
           }
         }
       }
+      const int t = p0 + u0 + r * PP + pr;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float tot = sum_lanes<SUB>(dot[g]);
         sc[r][g] = t < p1 ? tot : -INFINITY;
       }
     }
-    // online softmax: the block's maximum over the wave, one rescale
-    float pw[R][G];
+    // online softmax: the block's maximum over the wave, one rescale per
+    // block; the weights go to LDS for the value lanes
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float bm = sc[0][g];
@@ -185,48 +249,74 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
       m[g] = mn;
       l[g] *= alpha;
 #pragma unroll
-      for (int j = 0; j < DL; ++j) acc[g][j] *= alpha;
+      for (int j = 0; j < 8; ++j) acc[g][j] *= alpha;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        pw[r][g] = exp2f(sc[r][g] - mn);                 // 0 past L
-        l[g] += pw[r][g];
+        const float pw = exp2f(sc[r][g] - mn);           // 0 past the split
+        l[g] += pw;
+        if (sub == 0) sh_p[wave][r * PP + pr][g] = pw;
       }
     }
-    // values
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // values: acc[g][0..8) += p[g][t] * v[t][8 vl .. 8 vl + 8); rows past
+    // the length may hold anything (NaN * 0 is NaN): zeroed
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int t = t0 + r * PP + pr;
-      u32x4 w[DL / 8];
-      load_row<DL>(rv, static_cast<uint32_t>(t) * D * 2 + sub * DL * 2, w);
+    for (int i = 0; i < VI; ++i) {
+      const int tp = i * VPI + vp;
+      float pg[G];
 #pragma unroll
-      for (int i = 0; i < DL / 8; ++i) {
-        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+      for (int g = 0; g < G; ++g) pg[g] = sh_p[wave][tp][g];
+      const bool live = p0 + u0 + tp < p1;
+      const uint32_t wd[4] = {live ? vw[i].x : 0u, live ? vw[i].y : 0u, live ? vw[i].z : 0u, live ? vw[i].w : 0u};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float v0 = lo_f(wd[c]), v1 = hi_f(wd[c]);
+      for (int c = 0; c < 4; ++c) {
+        const float v0 = lo_f(wd[c]), v1 = hi_f(wd[c]);
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            acc[g][8 * i + 2 * c] = __builtin_fmaf(pw[r][g], v0, acc[g][8 * i + 2 * c]);
-            acc[g][8 * i + 2 * c + 1] = __builtin_fmaf(pw[r][g], v1, acc[g][8 * i + 2 * c + 1]);
-          }
+        for (int g = 0; g < G; ++g) {
+          acc[g][2 * c] = __builtin_fmaf(pg[g], v0, acc[g][2 * c]);
+          acc[g][2 * c + 1] = __builtin_fmaf(pg[g], v1, acc[g][2 * c + 1]);
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();                    // sh_p is rewritten by the next block
+  };
+
+  // the wave's blocks: u0 = wave * BP, + 4 BP, ...; the next block's loads are
+  // issued before the current block is computed (two register buffers)
+  constexpr int kStep = kAttnWaves * BP;
+  int u0 = wave * BP;
+  u32x4 ka[R][DL / 8], kb[R][DL / 8];
+  u32x4 va[VI], vb[VI];
+  load_blk(u0, ka, va);                                 // (issued before the length arrives)
+  const int n = p1 - p0;
+  if (u0 < n) {
+    while (true) {
+      load_blk(u0 + kStep, kb, vb);
+      do_blk(u0, ka, va);
+      u0 += kStep;
+      if (u0 >= n) break;
+      load_blk(u0 + kStep, ka, va);
+      do_blk(u0, kb, vb);
+      u0 += kStep;
+      if (u0 >= n) break;
+    }
   }
 
-  // the wave's totals: accumulators over its position lanes, sums over all
-  // lanes (each position counted by its SUB lanes)
+  // the wave's totals: accumulators over its value lanes of one slice, sums
+  // over all lanes (each position counted by its SUB key lanes)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l[g] = sum_lanes_from<1>(l[g]) * (1.f / SUB);
 #pragma unroll
-    for (int j = 0; j < DL; ++j) acc[g][j] = sum_lanes_from<SUB>(acc[g][j]);
+    for (int j = 0; j < 8; ++j) acc[g][j] = sum_lanes_from<VLN>(acc[g][j]);
   }
-  if (lane < SUB) {
+  if (lane < VLN) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int j = 0; j < DL; ++j) sh_acc[wave][g][sub * DL + j] = acc[g][j];
+      for (int j = 0; j < 8; ++j) sh_acc[wave][g][8 * vl + j] = acc[g][j];
   }
   if (lane == 0) {
 #pragma unroll
@@ -236,6 +326,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
 
   // the workgroup's (max, sum, accumulator) per head: waves in order
   const int tid = threadIdx.x;
+  float* rec_out = parts + (static_cast<size_t>(bh) * S + s) * part_floats<D, G>();
   for (int e = tid; e < G * D; e += kAttnThreads) {
     const int g = e / D, j = e - g * D;
     float M = sh_m[0][g];
@@ -251,9 +342,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
     if (S == 1) {
       out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / den;
     } else {
-      float* rec = parts + (static_cast<size_t>(bh) * S + s) * part_floats<D, G>();
-      rec[2 * G + e] = a;
-      if (j == 0) { rec[g] = M; rec[G + g] = den; }
+      rec_out[2 * G + e] = a;
+      if (j == 0) { rec_out[g] = M; rec_out[G + g] = den; }
     }
   }
   if (S == 1) return;
@@ -269,19 +359,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
   if (!sh_last) return;
   __threadfence();
   const float* rec0 = parts + static_cast<size_t>(bh) * S * part_floats<D, G>();
+  // per (split, head): its max and sum, one load each, in parallel
+  for (int e = tid; e < S * G; e += kAttnThreads) {
+    const int s2 = e / G, g = e - s2 * G;
+    sh_f[s2][g] = rec0[s2 * part_floats<D, G>() + g];
+    sh_sl[s2][g] = rec0[s2 * part_floats<D, G>() + G + g];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, sh_f[s2][tid]);
+    float den = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float ms = sh_f[s2][tid];
+      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      den += f * sh_sl[s2][tid];
+      sh_f[s2][tid] = f;
+    }
+    sh_den[tid] = den;
+  }
+  __syncthreads();
   for (int e = tid; e < G * D; e += kAttnThreads) {
     const int g = e / D, j = e - g * D;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, __builtin_nontemporal_load(rec0 + s2 * part_floats<D, G>() + g));
-    float a = 0.f, den = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float* rec = rec0 + s2 * part_floats<D, G>();
-      const float ms = __builtin_nontemporal_load(rec + g);
-      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      a += f * __builtin_nontemporal_load(rec + 2 * G + e);
-      den += f * __builtin_nontemporal_load(rec + G + g);
-    }
-    out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / den;
+    float a = 0.f;
+#pragma unroll 16
+    for (int s2 = 0; s2 < S; ++s2) a += sh_f[s2][g] * rec0[s2 * part_floats<D, G>() + 2 * G + e];
+    out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / sh_den[g];
   }
   if (tid == 0) __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -310,18 +413,24 @@ hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Splits: enough workgroups for about two per CU of a 256-CU device (the
-// same for every device, so the workspace size is a function of the shape
-// alone), each at least one block per wave; positions per split a multiple
-// of the waves' blocks.
+// Splits: up to about one workgroup per CU of a 256-CU device (the same
+// for every device, so the workspace size is a function of the shape
+// alone), at most 32, and at least two blocks per wave in a split, since
+// merging the splits costs a few memory round trips (a sweep of waves per
+// workgroup, blocks per wave, target workgroups and split cap on MI355X:
+// these defaults are best or within 3 % at contexts 512 - 32768, except
+// 8192, 13 % behind 8-wave workgroups); positions per split a multiple of
+// the waves' blocks.
 AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx) {
   const int G = n_q / n_kv;
-  const int bp = std::min(64, 131072 / (G * G * head_dim));
-  const int64_t unit = static_cast<int64_t>(kAttnWaves) * bp;       // positions of one round of blocks
+  const int pp = 4096 / (G * head_dim);
+  const int bp = std::max(pp, std::min(G * head_dim >= 1024 ? 8 : G >= 8 ? 16 : 32, 131072 / (G * G * head_dim)));
+  const int64_t unit = static_cast<int64_t>(kAttnWaves) * bp;       // one block per wave
   const int64_t units = (max_ctx + unit - 1) / unit;
-  const int64_t want = std::max<int64_t>(1, 512 / std::max(1, batch * n_kv));
+  const int64_t want = std::max<int64_t>(1, QGEMV_ATTN_TARGET_WGS / std::max(1, batch * n_kv));
+  const int64_t by_len = std::max<int64_t>(1, units / QGEMV_ATTN_MIN_BLOCKS);
   AttnPlan p;
-  p.splits = static_cast<int>(std::min<int64_t>(units, want));
+  p.splits = static_cast<int>(std::min<int64_t>(std::min<int64_t>(by_len, want), kMaxSplits));
   const int64_t per = (units + p.splits - 1) / p.splits;
   p.positions = static_cast<int>(per * unit);
   p.splits = static_cast<int>((max_ctx + p.positions - 1) / p.positions);

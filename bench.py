@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--peak-gib", type=float, default=4.0)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--per-kernel", action="store_true", help="also time every GEMV of the step alone")
+    p.add_argument("--no-attention", action="store_true",
+                   help="skip the decode-attention measurements (workload 2)")
     p.add_argument("--no-fused-layer", action="store_true",
                    help="skip the fused decode-layer chain (workload 2)")
     p.add_argument("--pmc-pass", action="store_true",
@@ -380,6 +382,46 @@ def pmc_pass(qg, torch, wl, steps):
                       "gemvs": [[g.name, g.M, g.K, b] for g, b in zip(wl.gemvs, wl.bytes)]}), flush=True)
 
 
+def attention_bench(qg, torch, rotate_bytes):
+    """Grouped-query decode attention at Llama-3.2-1B's heads (32 query, 8 key/value,
+    head dim 64): the infer page's contexts 512 and 2048 at batch 1, longer contexts,
+    and batch 8. Each configuration rotates through >= rotate_bytes of distinct caches;
+    bytes per call = the K and V rows read + q + out."""
+    n_q, n_kv, d = 32, 8, 64
+    out = []
+    for B, T in ((1, 512), (1, 2048), (1, 8192), (1, 32768), (8, 2048)):
+        per = 2 * B * n_kv * T * d * 2
+        n = max(2, math.ceil(rotate_bytes / per))
+        at = synth.make_attention(B, n_q, n_kv, d, T, seed=T + B, lens=[T] * B)
+        k0 = torch.from_numpy(at.k.view(np.int16)).to("cuda")
+        v0 = torch.from_numpy(at.v.view(np.int16)).to("cuda")
+        ks = [k0] + [k0.clone() for _ in range(n - 1)]
+        vs = [v0] + [v0.clone() for _ in range(n - 1)]
+        q = torch.from_numpy(at.q).to("cuda")
+        lens = torch.from_numpy(at.lens).to("cuda")
+        o = torch.empty((B, n_q, d), dtype=torch.float32, device="cuda")
+        ws = qg.attention_workspace(B, n_q, n_kv, d, T)
+        torch.cuda.synchronize()
+
+        def fn(i, h):
+            st = qg.lib().qgemv_attention_decode(q.data_ptr(), ks[i % n].data_ptr(), vs[i % n].data_ptr(),
+                                                 lens.data_ptr(), o.data_ptr(), B, n_q, n_kv, d, T, at.scale,
+                                                 ws.data_ptr(), h)
+            if st != qg.OK:
+                raise qg.QgemvError(st, "qgemv_attention_decode")
+        count = max(n * 2, 64)
+        g = capture(torch, fn, count)
+        time_graph(torch, g)
+        us = time_graph(torch, g, reps=3) * 1e3 / count
+        nbytes = per + 2 * B * n_q * d * 4
+        out.append({"batch": B, "ctx": T, "heads": [n_q, n_kv, d], "us": round(us, 3), "bytes": nbytes,
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        print(f"[bench] attention B={B} ctx={T}: {us:.2f} us, {out[-1]['GBps']} GB/s", file=sys.stderr, flush=True)
+        del g, ks, vs
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, seconds):
     """The oracle (fp64 dequantize + fp64 GEMV + argmax) on whole steps, one thread."""
     import oracle
@@ -441,6 +483,9 @@ def main():
         print(f"[bench] {mode}: {ms * 1e3:.2f} us/step, {nb / (ms * 1e-3) / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
         del g_warm, g_steps
+    attention = None
+    if cfg == 2 and not args.no_attention:
+        attention = attention_bench(qg, torch, args.rotate_gib * (1 << 30))
     fused_layer = None
     if cfg == 2 and not args.no_fused_layer:
         fl = FusedLayer(qg, torch, wl)
@@ -574,6 +619,8 @@ def main():
         out["per_kernel"] = per_kernel
     if fused_layer is not None:
         out["fused_layer"] = fused_layer
+    if attention is not None:
+        out["attention_decode"] = attention
     print(json.dumps(out), flush=True)
 
 
