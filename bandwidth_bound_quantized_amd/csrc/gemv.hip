@@ -560,22 +560,65 @@ struct AmShared {
   int left;
 };
 
+// Largest 64-bit key over the wave, in every lane: DPP inside 16-lane rows
+// (quad swaps, rotations by 4 and 8), then permlane butterflies across rows
+// (a swap of a register with itself returns rows (0,1,0,1) and (2,3,2,3)
+// for 32 lanes, (0,0,2,2) and (1,1,3,3) for 16).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
+  x = umax64(x, dpp_u64<0xB1>(x));             // quad_perm [1,0,3,2]
+  x = umax64(x, dpp_u64<0x4E>(x));             // quad_perm [2,3,0,1]
+  x = umax64(x, dpp_u64<0x124>(x));            // row_ror:4
+  x = umax64(x, dpp_u64<0x128>(x));            // row_ror:8
+  {
+    const auto l = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(x >> 32), false, false);
+    const uint32_t l0 = l[0], l1 = l[1], h0 = h[0], h1 = h[1];
+    x = umax64((static_cast<uint64_t>(h0) << 32) | l0, (static_cast<uint64_t>(h1) << 32) | l1);
+  }
+  {
+    const auto l = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(x >> 32), false, false);
+    const uint32_t l0 = l[0], l1 = l[1], h0 = h[0], h1 = h[1];
+    x = umax64((static_cast<uint64_t>(h0) << 32) | l0, (static_cast<uint64_t>(h1) << 32) | l1);
+  }
+  return x;
+}
+
 // A wave is done with the LM-head entry: fold its lanes' keys into the
-// workgroup's, count itself; the workgroup's last wave publishes the keys in
-// the workgroup's own workspace words (relaxed device-scope stores).
+// workgroup's (one wave-wide max per batch row, then one LDS max by one
+// lane), count itself; the workgroup's last wave publishes the keys in the
+// workgroup's own workspace words (relaxed device-scope stores).
+template <int NB>
 __device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __restrict__ slots,
                                          int batch, int lane) {
-  if (am.key != 0)
-    atomicMax(reinterpret_cast<unsigned long long*>(&sh->key[am.b]), static_cast<unsigned long long>(am.key));
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // Only LDS carries the hand-off, and LDS executes each wave's operations
+  // in order: a wave's key max is done before its count, and the last
+  // wave's reads come after every count. So no memory fence (a
+  // workgroup-scope release fence would also wait for this wave's
+  // outstanding global stores and prefetched weight loads); the asm
+  // statements only keep the compiler from moving LDS accesses across.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint64_t k = wave_umax64(am.b == b ? am.key : uint64_t{0});
+    if (lane == 0 && k != 0)
+      __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&sh->key[b]),
+                             static_cast<unsigned long long>(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
   int prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&sh->left, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0) prev = __hip_atomic_fetch_add(&sh->left, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   prev = __shfl(prev, 0);
+  asm volatile("" ::: "memory");
   if (prev == kWaves - 1) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (lane < batch)
-      __hip_atomic_store(slots + static_cast<size_t>(lane) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + blockIdx.x,
+      __hip_atomic_store(slots + static_cast<size_t>(lane) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + (blockIdx.x - 1),
                          sh->key[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   am.left = true;
@@ -745,7 +788,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       // the entry's row groups are one contiguous range of items
       const int am_end = tab.am + 1 < tab.n ? tab.e[tab.am + 1].start : tab.total;
       if (cur_j == tab.am && !am.left && (item >= am_end || item >= tab.total))
-        am_leave(am, am_sh, am_slots, batch, lane);
+        am_leave<NB>(am, am_sh, am_slots, batch, lane);
     }
     if (!more) break;
     if (switched) bias_sums();
@@ -754,10 +797,13 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
 }
 
 // Row groups of a wave: item, item + stride, ... (grid-stride over the table).
+// (with AM, workgroup 0 collects the argmax keys and the others work:
+// first = 1)
+template <int first = 0>
 __device__ __forceinline__ int first_item(int& stride) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  stride = gridDim.x * kWaves;
-  return blockIdx.x * kWaves + wave;
+  stride = (gridDim.x - first) * kWaves;
+  return (blockIdx.x - first) * kWaves + wave;
 }
 
 // One GEMV (or a table of GEMVs of one shape) with a fixed (R, NCH).
@@ -775,16 +821,19 @@ constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most workg
 constexpr int kFusedPerThread = kFusedSlots / kThreads;
 constexpr int kFusedSpinLimit = 1 << 20;
 
-// The fused argmax's last step, run by the launch's last workgroup after its
-// own GEMV work: wait until every workgroup has published its key for each
-// batch row (slots[b][w], nonzero once written), take the largest, write the
-// index, and clear the slots for the next call. All of a thread's slot loads
-// are in flight together; the wait is bounded (a key never published - which
-// needs a workgroup that never runs - gives idx -1 instead of a hang).
+// The fused argmax's last step, run by workgroup 0 of the launch, which does
+// no GEMV work: wait until every other workgroup has published its key for
+// each batch row (slots[b][w - 1] for workgroup w, nonzero once written),
+// take the largest, write the index, and clear the slots for the next call.
+// The argmax entry's row groups are the launch's first, so its keys are in
+// while the other entries still stream, and this wait overlaps them. All of
+// a thread's slot loads are in flight together; the wait is bounded (a key
+// never published - which needs a workgroup that never runs - gives idx -1
+// instead of a hang).
 __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, int batch,
                                                   int32_t* __restrict__ idx, uint64_t* red) {
   const int tid = threadIdx.x;
-  const int grid = gridDim.x;
+  const int grid = gridDim.x - 1;                       // workers (workgroups 1..)
   for (int b = 0; b < batch; ++b) {
     uint64_t* row = slots + static_cast<size_t>(b) * kFusedSlots;
     uint64_t v[kFusedPerThread];
@@ -847,12 +896,16 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
   __shared__ AmShared am_sh;
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
+    if (blockIdx.x == 0) {                      // the collector
+      fused_argmax_tail(slots, batch, idx, red);
+      return;
+    }
     if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
     if (threadIdx.x == 0) am_sh.left = 0;
     __syncthreads();
   }
   int stride;
-  int item = first_item(stride);
+  int item = first_item<AM ? 1 : 0>(stride);
   const int lane = threadIdx.x & 63;
   AmLane am;
   if (item < tab.total) {
@@ -860,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
     while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
     while (item < tab.total) {
       if constexpr (AM) {
-        if (j != tab.am && !am.left) am_leave(am, &am_sh, slots, batch, lane);
+        if (j > tab.am && !am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);   // past the entry
       }
       switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
@@ -877,9 +930,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
     }
   }
   if constexpr (AM) {
-    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
-    __syncthreads();
-    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
+    if (!am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);
   }
 }
 
@@ -1553,6 +1604,12 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
   extern __shared__ u32x4 lds_v4[];
   __shared__ AmShared am_sh;
   __shared__ uint64_t red[kWaves];
+  if constexpr (AM) {
+    if (blockIdx.x == 0) {                      // the collector (see fused_argmax_tail)
+      fused_argmax_tail(slots, batch, idx, red);
+      return;
+    }
+  }
   const uint32_t* xn = nullptr;
   if (fu.h != nullptr) {
     uint32_t* xs = reinterpret_cast<uint32_t*>(lds_v4);
@@ -1566,7 +1623,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
     __syncthreads();
   }
   int stride;
-  int item = first_item(stride);
+  int item = first_item<AM ? 1 : 0>(stride);
   const int lane = threadIdx.x & 63;
   AmLane am;
   if (item < tab.total) {
@@ -1574,9 +1631,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
     xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, &am_sh, slots, fu, xn);
   }
   if constexpr (AM) {
-    if (!am.left) am_leave(am, &am_sh, slots, batch, lane);
-    __syncthreads();
-    if (blockIdx.x == gridDim.x - 1) fused_argmax_tail(slots, batch, idx, red);
+    if (!am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);
   }
 }
 
@@ -1866,10 +1921,16 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
                          uint64_t* slots, int32_t* idx, hipStream_t st) {
   GemvTable<kGroupMax> tab{};
   tab.n = n;
-  tab.am = am >= 0 ? 0 : -1;            // the argmax entry goes first (its row groups first)
+  // the argmax entry goes first, so its keys are complete while the other
+  // entries still stream (the rest in the given order; sorting them by row
+  // group size measured slower)
+  int order[kGroupMax];
+  for (int t = 0; t < n; ++t) order[t] = am < 0 ? t : t == 0 ? am : (t <= am ? t - 1 : t);
+  tab.am = -1;
   int start = 0;
   for (int t = 0; t < n; ++t) {
-    const int i = am < 0 ? t : t == 0 ? am : (t <= am ? t - 1 : t);
+    const int i = order[t];
+    if (i == am) tab.am = t;
     tab.e[t] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
                           a[i].M, a[i].K, start, xreg_shape(R[i], nch[i])};
     start += (a[i].M + R[i] - 1) / R[i];
@@ -1882,9 +1943,11 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
   // workgroups per CU against a grid of 8 per CU).
   const int cus = device_cu_count();
   if (am >= 0) {
+    // workers plus the collector (workgroup 0), all resident at once: the
+    // collector waits for every worker's key
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_group_kernel<FMT, NB, kGroupMax, true>));
-    grid = std::min(grid, cus * per_cu);
+    grid = std::max(1, std::min(grid, cus * per_cu - 1)) + 1;
     gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<grid, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
@@ -2147,7 +2210,8 @@ hipError_t launch_fused_xreg(const GemvArgs& a, const Fusion& f, uint64_t* slots
   if (idx) {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_fused_kernel<FMT, NB, R, NCH, true>));
-    grid = std::max(1, std::min({grid, cus * std::min(per_cu, lds_cap), static_cast<int>(kFusedSlots)}));
+    // workers plus the collector (workgroup 0), all resident at once
+    grid = std::max(1, std::min({grid, cus * std::min(per_cu, lds_cap) - 1, static_cast<int>(kFusedSlots)})) + 1;
     gemv_xreg_fused_kernel<FMT, NB, R, NCH, true><<<grid, kThreads, lds, st>>>(tab, a.batch, slots, idx, f);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
