@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_attention_decode": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_i64,
                                            ctypes.c_float, c_vp, c_vp]),
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
+        "qgemv_grouped_class": (c_int, [c_int, c_i64, c_int]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
         "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
         "qgemv_status_str": (ctypes.c_char_p, [c_int]),
@@ -81,7 +82,7 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_flags",
            "qgemv_run_fused", "qgemv_run_grouped", "qgemv_attention_workspace_size", "qgemv_attention_decode",
-           "qgemv_run_grouped_argmax", "qgemv_argmax", "qgemv_stream_read",
+           "qgemv_run_grouped_argmax", "qgemv_grouped_class", "qgemv_argmax", "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
 
@@ -299,15 +300,17 @@ def grouped_descs(entries) -> "ctypes.Array":
     return arr
 
 
-ELEMS_PER_UNIT = {BF16: 8, INT8_G32: 16, Q4_0_G32: 32, INT4_G128: 32, INT8_ROW: 16, INT4_G64: 32}
+GROUP_ALONE, GROUP_XREG, GROUP_MFMA = 0, 1, 2
 
 
-def group_class(fmt: int, K: int, batch: int) -> int:
-    """0 if qgemv_run_grouped launches this GEMV alone, else its 16-byte units per
-    lane-column of a row (1..4); per the rule in qgemv.h (batch <= 2 and at most 4
-    units per lane-column), GEMVs with a nonzero class share one launch per format."""
-    nch = -(-K // (64 * ELEMS_PER_UNIT[fmt]))
-    return nch if (batch <= 2 and nch <= 4) else 0
+def grouped_class(fmt: int, K: int, batch: int) -> int:
+    """Which launch qgemv_run_grouped gives a GEMV of this (fmt, K, batch):
+    GROUP_XREG (one launch per format), GROUP_MFMA (one per format and K) or
+    GROUP_ALONE (qgemv_grouped_class)."""
+    st = _lib.qgemv_grouped_class(fmt, K, batch)
+    if st < 0:
+        raise QgemvError(st, "qgemv_grouped_class")
+    return st
 
 
 def run_grouped(descs, batch: int, stream=None) -> None:

@@ -924,6 +924,12 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
         QG_SHAPE(QGEMV_GROUP_R2, 2)
         QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
+        case xreg_shape(1, 8):                   // int8 at batch 1 only
+          if constexpr (is_int8_fmt(FMT) && NB == 1)
+            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots, Fusion{});
+          else
+            item = tab.total;
+          break;
 #undef QG_SHAPE
         default: item = tab.total;               // not produced by the host
       }
@@ -1863,7 +1869,8 @@ hipError_t launch_f(const GemvArgs& a, int R, int grid, size_t lds, hipStream_t 
 
 template <int FMT, int NB, int R, bool FUSED = false>
 void allow_big_lds() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, NB, R, FUSED>),
+  // (a failure here shows up as the error of the launch that needs it)
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, NB, R, FUSED>),
                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
@@ -1902,7 +1909,10 @@ hipError_t launch_xreg1(const GemvArgs& a, int R, int nch, int grid, hipStream_t
     case 1: return launch_xreg2<FMT, NB, 1>(a, R, grid, st);
     case 2: return launch_xreg2<FMT, NB, 2>(a, R, grid, st);
     case 3: return launch_xreg2<FMT, NB, 3>(a, R, grid, st);
-    default: return launch_xreg2<FMT, NB, 4>(a, R, grid, st);
+    case 4: return launch_xreg2<FMT, NB, 4>(a, R, grid, st);
+    default:
+      if constexpr (is_int8_fmt(FMT) && NB == 1) return launch_xreg3<FMT, NB, 1, 8>(a, grid, st);
+      else return hipErrorInvalidValue;          // (not produced by the host)
   }
 }
 
@@ -2088,16 +2098,27 @@ size_t gemv_lds_bytes(int fmt, int K, int batch) {
   return bytes;
 }
 
-bool gemv_uses_lds(int fmt, int K, int batch) {
+// Units per lane-column whose x a register-x kernel holds: 4, and 8 (taken
+// as one shape, rows one at a time) for int8 at batch 1, where 8 units of x
+// are 64 registers, as many as 4 units of a 4-bit format. The fused kernels,
+// whose row groups hold a gate/up pair, stop at 4.
+int xreg_max_units(int fmt, int batch, bool fused) {
+  return !fused && (fmt == QGEMV_INT8_G32 || fmt == QGEMV_INT8_ROW) && round_batch(batch) == 1 ? 8 : 4;
+}
+
+int xreg_units(int fmt, int K) {
   const int U = K / fmt_info(fmt).elems_per_unit;
   const int nch = (U + 63) / 64;
-  return !(round_batch(batch) <= 2 && nch <= 4);
+  return nch <= 4 || nch > 8 ? nch : 8;
+}
+
+bool gemv_uses_lds(int fmt, int K, int batch, bool fused) {
+  return !(round_batch(batch) <= 2 && xreg_units(fmt, K) <= xreg_max_units(fmt, batch, fused));
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
   const int cus = device_cu_count();
-  const int U = a.K / fmt_info(a.fmt).elems_per_unit;
-  const int nch = (U + 63) / 64;
+  const int nch = xreg_units(a.fmt, a.K);
   // batch invariance: every batch runs the kernels compiled for 8 batch rows
   // with launch shapes chosen from (fmt, M, K) alone, so a row's arithmetic
   // is the same at every batch (the register-x kernel is never used: its
@@ -2107,7 +2128,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
   if (!inv && !gemv_uses_lds(a.fmt, a.K, a.batch)) {
     // rows per step: up to 8 / NCH units in flight per lane, while keeping
     // at least two workgroups per CU
-    int R = std::min(QGEMV_XREG_MAX_R, nch == 1 ? 4 : nch == 2 ? 4 : 2);
+    int R = std::min(QGEMV_XREG_MAX_R, nch <= 2 ? 4 : nch <= 4 ? 2 : 1);
     while (R > 1 && (a.M + R - 1) / R < QGEMV_MIN_WAVES_PER_CU * cus) R >>= 1;
     const int groups = (a.M + R - 1) / R;
     const int wg_needed = (groups + kWaves - 1) / kWaves;
@@ -2143,8 +2164,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
 
 int gemv_group_class(int fmt, int K, int batch) {
   if (gemv_uses_lds(fmt, K, batch)) return 0;
-  const int U = K / fmt_info(fmt).elems_per_unit;
-  return (U + 63) / 64;
+  return xreg_units(fmt, K);
 }
 
 int gemv_group_max() { return kGroupMax; }
@@ -2178,7 +2198,7 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int a
   long total = 0;
   for (int i = 0; i < n; ++i) {
     nch[i] = gemv_group_class(a[i].fmt, a[i].K, a[i].batch);
-    R[i] = nch[i] == 1 ? (r4 ? 4 : 2) : nch[i] == 2 ? QGEMV_GROUP_R2 : QGEMV_GROUP_RLONG;
+    R[i] = nch[i] == 1 ? (r4 ? 4 : 2) : nch[i] == 2 ? QGEMV_GROUP_R2 : nch[i] <= 4 ? QGEMV_GROUP_RLONG : 1;
     total += (a[i].M + R[i] - 1) / R[i];
   }
   long cap = static_cast<long>(cus) * QGEMV_GROUP_MAX_WG_PER_CU;
@@ -2241,8 +2261,8 @@ hipError_t launch_fused_fmt(const GemvArgs& a, const Fusion& f, uint64_t* slots,
                             hipStream_t st) {
   const int cus = device_cu_count();
   const int nb = round_batch(a.batch);
-  if (!gemv_uses_lds(FMT, a.K, a.batch)) {
-    const int nch = gemv_group_class(FMT, a.K, a.batch);
+  if (!gemv_uses_lds(FMT, a.K, a.batch, true)) {
+    const int nch = xreg_units(FMT, a.K);
     const bool r4 = a.M / 4 >= QGEMV_MIN_WAVES_PER_CU * cus;
     if (nb == 1) return launch_fused_xreg_shape<FMT, 1>(a, nch, r4, f, slots, idx, st);
     return launch_fused_xreg_shape<FMT, 2>(a, nch, r4, f, slots, idx, st);

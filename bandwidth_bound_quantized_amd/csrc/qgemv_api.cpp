@@ -296,7 +296,7 @@ int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16
   if (st) return st;
   if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
   if (swiglu && (M % 2) != 0) return QGEMV_ESHAPE;
-  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch) &&
+  if (qgemv::gemv_uses_lds(fmt, static_cast<int>(K), batch, true) &&
       qgemv::gemv_lds_bytes(fmt, static_cast<int>(K), batch) + qgemv::kNormScratchBytes > 160 * 1024)
     return QGEMV_ESHAPE;
   if (!aligned(W, 16) || (fmt != QGEMV_BF16 && !aligned(scales, 4))) return QGEMV_EALIGN;
@@ -371,6 +371,13 @@ namespace {
 // The grouped launches of qgemv_run_grouped; am >= 0: entry am's launch also
 // computes the argmax of its output if the small-batch kernel takes it
 // (*fused = true), else the caller launches the argmax.
+// launch of qgemv_run_grouped an entry goes to (QGEMV_GROUP_*): the register-x
+// group of its format, the matrix-core group of its format and K, or alone
+int grouped_kind(int fmt, int K, int batch) {
+  return qgemv::gemv_group_class(fmt, K, batch) != 0 ? QGEMV_GROUP_XREG
+         : qgemv::gemv_mfma_groupable(fmt, K, batch) ? QGEMV_GROUP_MFMA : QGEMV_GROUP_ALONE;
+}
+
 int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t s, int am,
                      uint64_t* slots, int32_t* idx, bool* fused) {
   // GEMVs the register-x kernel takes are launched together, one launch per
@@ -381,14 +388,8 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
   std::vector<int> ids;
   std::vector<char> done(static_cast<size_t>(n), 0);
   if (fused) *fused = false;
-  // kind of launch an entry goes to: 1 register-x group (by format),
-  // 2 matrix-core group (by format and K), 0 alone
   std::vector<int> kind(static_cast<size_t>(n));
-  for (int i = 0; i < n; ++i) {
-    const qgemv_gemv_desc& h = gemvs[i];
-    kind[i] = qgemv::gemv_group_class(h.fmt, h.K, batch) != 0 ? 1
-              : qgemv::gemv_mfma_groupable(h.fmt, h.K, batch) ? 2 : 0;
-  }
+  for (int i = 0; i < n; ++i) kind[i] = grouped_kind(gemvs[i].fmt, gemvs[i].K, batch);
   for (int i = 0; i < n; ++i) {
     if (done[i]) continue;
     const qgemv_gemv_desc& g = gemvs[i];
@@ -398,20 +399,20 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
     for (int k = i; k < n; ++k) {
       const qgemv_gemv_desc& h = gemvs[k];
       if (done[k]) continue;
-      if (cls == 0 ? k != i
-                   : (h.fmt != g.fmt || kind[k] != cls || (cls == 2 && h.K != g.K)))
+      if (cls == QGEMV_GROUP_ALONE ? k != i
+                   : (h.fmt != g.fmt || kind[k] != cls || (cls == QGEMV_GROUP_MFMA && h.K != g.K)))
         continue;
       todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
       ids.push_back(k);
       done[k] = 1;
     }
-    const int maxn = cls == 0 ? 1 : qgemv::gemv_group_max();
+    const int maxn = cls == QGEMV_GROUP_ALONE ? 1 : qgemv::gemv_group_max();
     for (size_t off = 0; off < todo.size(); off += maxn) {
       const int cnt = static_cast<int>(std::min(todo.size() - off, static_cast<size_t>(maxn)));
       hipError_t e;
-      if (cls == 0) {
+      if (cls == QGEMV_GROUP_ALONE) {
         e = qgemv::launch_gemv(todo[off], s);
-      } else if (cls == 2) {
+      } else if (cls == QGEMV_GROUP_MFMA) {
         e = qgemv::launch_gemv_mfma_group(&todo[off], cnt, s);
       } else {
         int local_am = -1;
@@ -444,6 +445,15 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
   const int st = check_grouped(gemvs, n, batch);
   if (st) return st;
   return run_grouped_impl(gemvs, n, batch, static_cast<hipStream_t>(stream), -1, nullptr, nullptr, nullptr);
+}
+
+int qgemv_grouped_class(int fmt, int64_t K, int batch) {
+  if (!valid_fmt(fmt)) return QGEMV_EINVAL;
+  const int st = check_shape(fmt, 1, K);
+  if (st) return st;
+  if (batch < 1 || batch > QGEMV_MAX_BATCH) return QGEMV_ESHAPE;
+  const int k = static_cast<int>(K);
+  return grouped_kind(fmt, k, batch);
 }
 
 int qgemv_run_grouped_argmax(const qgemv_gemv_desc* gemvs, int n, int batch, int argmax_entry,

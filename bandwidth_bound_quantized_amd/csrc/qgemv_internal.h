@@ -54,9 +54,10 @@ constexpr size_t kNormScratchBytes = 1024;
 // (x as bf16 for the compiled batch, plus per-unit x sums for 4-bit formats).
 size_t gemv_lds_bytes(int fmt, int K, int batch);
 
-// Whether the GEMV of this shape stages x in LDS (batch > 2 or long rows);
-// otherwise each lane keeps its share of x in registers and no LDS is used.
-bool gemv_uses_lds(int fmt, int K, int batch);
+// Whether the GEMV of this shape (fused: through launch_gemv_fused) stages x
+// in LDS (batch > 2 or long rows); otherwise each lane keeps its share of x
+// in registers and no LDS is used.
+bool gemv_uses_lds(int fmt, int K, int batch, bool fused = false);
 
 // Launch the GEMV on `stream` (flags: QGEMV_FLAG_*). Shapes have been
 // validated by the caller.
@@ -70,7 +71,8 @@ hipError_t launch_gemv_fused(const GemvArgs& a, const Fusion& f, uint64_t* slots
 
 // Grouped launches of independent GEMVs (register-x kernel only).
 // gemv_group_class: 0 if (fmt, K, batch) needs another kernel, else the number
-// of 16-byte units per lane-column of a row (1..4); GEMVs of one format and
+// of 16-byte units per lane-column of a row (1..4, or 8 for int8 rows of
+// 65..128 units at batch 1); GEMVs of one format and
 // batch with a nonzero class can share a launch. launch_gemv_group:
 // n <= gemv_group_max() such GEMVs, already validated.
 // am >= 0: the launch also writes idx[b] = argmax of row b of a[am].y, using

@@ -126,9 +126,11 @@ class Workload:
         # per set: descriptors for one grouped call, and per launch class
         self.classes = {}
         for j, g in enumerate(self.gemvs):
-            # qgemv_run_grouped: one launch per format for the GEMVs with a
-            # nonzero class, one launch each for the others
-            key = (g.fmt, "grouped") if qg.group_class(g.fmt, g.K, B) else ("alone", j)
+            # qgemv_run_grouped: one small-batch launch per format, one
+            # matrix-core launch per format and K, one launch each for the others
+            cls = qg.grouped_class(g.fmt, g.K, B)
+            key = ((g.fmt, "grouped") if cls == qg.GROUP_XREG else
+                   (g.fmt, g.K, "mfma") if cls == qg.GROUP_MFMA else ("alone", j))
             self.classes.setdefault(key, []).append(j)
         self.descs = []
         self.class_descs = []

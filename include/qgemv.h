@@ -202,8 +202,8 @@ typedef struct {
  * 89-GEMV weight stream of a TinyLlama step measured here; the experts of a
  * mixture-of-experts layer are another).
  * Entries of one format that the small-batch kernel handles (batch <= 2 and
- * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit)
- * share launches (one per format, up to 64 entries each), and so do entries
+ * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit;
+ * int8 at batch 1 up to 512 units, K <= 8192) share launches (one per format, up to 64 entries each), and so do entries
  * of one format and K that the matrix-core kernel handles (batch 3..8, K a
  * multiple of 256 for Q4_0 and int4-g64, 128 for int8 and bf16, 512 for int4-g128, x in
  * LDS), so the per-launch start-up cost is paid once per group instead of
@@ -212,6 +212,22 @@ typedef struct {
  * for n > QGEMV_GROUP_MAX.
  */
 int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stream);
+
+/* launches of qgemv_run_grouped (qgemv_grouped_class) */
+#define QGEMV_GROUP_ALONE 0   /* a launch of its own */
+#define QGEMV_GROUP_XREG 1    /* the small-batch launch of its format */
+#define QGEMV_GROUP_MFMA 2    /* the matrix-core launch of its format and K */
+
+/*
+ * qgemv_grouped_class - which launch qgemv_run_grouped (and
+ * qgemv_run_grouped_argmax) gives an entry of this format, row length and
+ * batch: QGEMV_GROUP_XREG, QGEMV_GROUP_MFMA or QGEMV_GROUP_ALONE (the rule
+ * stated under qgemv_run_grouped). Host only, no launch; reads the current
+ * device's compute-unit count (the matrix-core plan depends on it). Returns
+ * the class, or EINVAL / ESHAPE (negative) for an unknown format, a K that
+ * the format does not allow, or a batch outside 1..8.
+ */
+int qgemv_grouped_class(int fmt, int64_t K, int batch);
 
 /* u64 words of workspace qgemv_argmax needs per batch row */
 #define QGEMV_ARGMAX_WS_WORDS_PER_ROW 2
@@ -248,8 +264,10 @@ int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_
  * When the small-batch kernel computes the argmax entry (batch <= 2, row
  * length as in qgemv_run_grouped), the argmax runs inside that launch: each
  * workgroup folds the logits it writes into one key per batch row and
- * publishes it in its own word of ws, and the launch's last workgroup takes
- * the largest; no separate launch and no second pass over the logits.
+ * publishes it in its own word of ws, and one workgroup of the launch, which
+ * does no GEMV work, collects the words while the other entries still
+ * stream and takes the largest; no separate launch and no second pass over
+ * the logits.
  * Otherwise the argmax is a qgemv_argmax launch after the GEMVs, on the same
  * stream, with the same ws. The logits (gemvs[argmax_entry].y) are written
  * in full either way.

@@ -309,6 +309,21 @@ def test_grouped_validation_errors_before_any_launch():
         assert L.qgemv_run_grouped(ctypes.cast(arr, ctypes.c_void_p), 4, 1, None) == want, bad
 
 
+def test_grouped_class_validation():
+    """qgemv_grouped_class rejects what qgemv_run_grouped would reject, before it
+    looks at the device."""
+    L = qg.lib()
+    assert L.qgemv_grouped_class(9, 2048, 1) == qg.EINVAL
+    assert L.qgemv_grouped_class(-1, 2048, 1) == qg.EINVAL
+    assert L.qgemv_grouped_class(qg.Q4_0_G32, 48, 1) == qg.ESHAPE
+    assert L.qgemv_grouped_class(qg.INT4_G128, 64, 1) == qg.ESHAPE
+    assert L.qgemv_grouped_class(qg.Q4_0_G32, 0, 1) == qg.ESHAPE
+    assert L.qgemv_grouped_class(qg.Q4_0_G32, 2048, 0) == qg.ESHAPE
+    assert L.qgemv_grouped_class(qg.Q4_0_G32, 2048, 9) == qg.ESHAPE
+    with pytest.raises(qg.QgemvError):
+        qg.grouped_class(qg.BF16, 2048, 10)
+
+
 def test_grouped_argmax_validation_errors_before_any_launch():
     L = qg.lib()
     arr = (qg.GemvDesc * 2)()

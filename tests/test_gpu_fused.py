@@ -106,6 +106,7 @@ SHAPES = [
     (qg.Q4_0_G32, 2048, 2048, 1), (qg.Q4_0_G32, 2050, 2048, 2), (qg.Q4_0_G32, 1024, 5632, 1),
     (qg.Q4_0_G32, 2048, 2048, 5), (qg.Q4_0_G32, 1026, 2048 + 32, 3),
     (qg.INT8_G32, 2048, 2048, 1), (qg.INT8_G32, 1536, 8192, 2), (qg.INT8_G32, 2048, 2048, 8),
+    (qg.INT8_G32, 1024, 8192, 1),
     (qg.INT4_G128, 2048, 2048, 1), (qg.INT4_G128, 2048, 8192, 4), (qg.INT4_G128, 514, 2048 + 128, 8),
     (qg.BF16, 2048, 2048, 1), (qg.BF16, 1000, 2048, 2), (qg.BF16, 1024, 2048, 3), (qg.BF16, 130, 5664, 6),
     (qg.INT8_ROW, 2048, 2048, 1), (qg.INT8_ROW, 2048, 2048, 8), (qg.INT8_ROW, 512, 2048 + 32, 4),

@@ -338,17 +338,31 @@ def test_grouped_decode_step_stream_89_gemvs(B):
 @pytest.mark.parametrize("B", [1, 2, 3, 8])
 def test_grouped_mixed_formats_ragged_and_fallback(B):
     """Formats and row lengths mixed in one call, ragged M, entries no grouped kernel
-    takes launched one by one (int8 K=8192 at B <= 2; K not a multiple of the
-    matrix-core step at B >= 3)."""
+    takes launched one by one (int8 K=8192 at B = 2; K not a multiple of the
+    matrix-core step at B >= 3). At B = 1 the int8 rows of 4608..8192 share the
+    grouped launch with the short ones, one row per wave step, including rows whose
+    unit count is not a multiple of 64 (K = 4608, 5632)."""
     shapes = [(synth.Q4_0_G32, 1, 2048), (synth.BF16, 65, 256), (synth.INT8_G32, 1000, 2048),
               (synth.Q4_0_G32, 63, 5632), (synth.INT4_G128, 300, 8192), (synth.INT8_G32, 70, 8192),
               (synth.Q4_0_G32, 4097, 2048), (synth.BF16, 7, 2048), (synth.INT4_G128, 129, 384),
               (synth.Q4_0_G32, 2, 96), (synth.INT8_ROW, 513, 2048), (synth.INT4_G64, 1029, 2048),
-              (synth.INT8_ROW, 40, 8192), (synth.INT4_G64, 3, 192)]
+              (synth.INT8_ROW, 40, 8192), (synth.INT4_G64, 3, 192), (synth.INT8_G32, 33, 5632),
+              (synth.INT8_ROW, 9, 4608)]
     gemvs = [synth.make_gemv(f"g{i}", f, M, K, B, 6, i, "o") for i, (f, M, K) in enumerate(shapes)]
     ys = _grouped(gemvs, B)
     for g, y in zip(gemvs, ys):
         assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=sample_rows(g.M), what=f"mixed {g.name}")
+
+
+def test_grouped_class_of_the_workload_shapes():
+    """The launches qgemv_grouped_class names for the shapes measured here."""
+    XR, MF, AL = qg.GROUP_XREG, qg.GROUP_MFMA, qg.GROUP_ALONE
+    cases = [(qg.Q4_0_G32, 2048, 1, XR), (qg.Q4_0_G32, 5632, 2, XR), (qg.INT4_G128, 8192, 1, XR),
+             (qg.INT8_G32, 8192, 1, XR), (qg.INT8_ROW, 4608, 1, XR), (qg.INT8_G32, 8192, 2, AL),
+             (qg.INT8_G32, 9216, 1, AL), (qg.BF16, 2048, 2, XR), (qg.BF16, 4096, 1, AL),
+             (qg.Q4_0_G32, 2048, 8, MF), (qg.INT8_G32, 8192, 3, MF), (qg.Q4_0_G32, 2048 + 32, 4, AL)]
+    for fmt, K, B, want in cases:
+        assert qg.grouped_class(fmt, K, B) == want, (qg.FMT_NAMES[fmt], K, B)
 
 
 def test_grouped_more_than_one_launch_per_class():
