@@ -546,19 +546,18 @@ struct GemvTable {
 // one unless the entry's (R, NCH) differs.
 // Fused-argmax state of a lane (see gemv_xreg_group_kernel): its running key
 // over the LM-head outputs it stored, their batch row, and whether its wave
-// has already handed its keys to the workgroup.
+// has already published its keys.
 struct AmLane {
   uint64_t key = 0;
   int b = 0;
   bool left = false;
 };
 
-// Fused-argmax LDS of a workgroup: the key per batch row and the number of
-// waves that have left the LM-head entry.
-struct AmShared {
-  uint64_t key[QGEMV_MAX_BATCH];
-  int left;
-};
+// Workspace word of this wave's argmax key (per batch row): waves of
+// workgroups 1.. in order (workgroup 0 collects).
+__device__ __forceinline__ int am_slot() {
+  return (static_cast<int>(blockIdx.x) - 1) * kWaves + static_cast<int>(threadIdx.x >> 6);
+}
 
 // Largest 64-bit key over the wave, in every lane: DPP inside 16-lane rows
 // (quad swaps, rotations by 4 and 8), then permlane butterflies across rows
@@ -590,37 +589,21 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
   return x;
 }
 
-// A wave is done with the LM-head entry: fold its lanes' keys into the
-// workgroup's (one wave-wide max per batch row, then one LDS max by one
-// lane), count itself; the workgroup's last wave publishes the keys in the
-// workgroup's own workspace words (relaxed device-scope stores).
+// A wave is done with the LM-head entry: one wave-wide max per batch row,
+// and lane b publishes row b's key in the wave's own workspace word (a
+// relaxed device-scope store; key 1, which never wins, if the wave stored no
+// output of the entry). No LDS and no counting among the workgroup's waves.
 template <int NB>
-__device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __restrict__ slots,
-                                         int batch, int lane) {
-  // Only LDS carries the hand-off, and LDS executes each wave's operations
-  // in order: a wave's key max is done before its count, and the last
-  // wave's reads come after every count. So no memory fence (a
-  // workgroup-scope release fence would also wait for this wave's
-  // outstanding global stores and prefetched weight loads); the asm
-  // statements only keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void am_leave(AmLane& am, uint64_t* __restrict__ slots, int batch, int lane) {
+  uint64_t mine = 1;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const uint64_t k = wave_umax64(am.b == b ? am.key : uint64_t{0});
-    if (lane == 0 && k != 0)
-      __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&sh->key[b]),
-                             static_cast<unsigned long long>(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == b) mine = umax64(k, 1);
   }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  int prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&sh->left, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  prev = __shfl(prev, 0);
-  asm volatile("" ::: "memory");
-  if (prev == kWaves - 1) {
-    if (lane < batch)
-      __hip_atomic_store(slots + static_cast<size_t>(lane) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + (blockIdx.x - 1),
-                         sh->key[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (lane < batch)
+    __hip_atomic_store(slots + static_cast<size_t>(lane) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + am_slot(),
+                       mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   am.left = true;
 }
 
@@ -630,7 +613,7 @@ __device__ __forceinline__ void am_leave(AmLane& am, AmShared* sh, uint64_t* __r
 // FUSED: the RMSNorm prologue and the epilogue of fu (one-entry tables).
 template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
-                                        int batch, int lane, AmLane& am, AmShared* am_sh,
+                                        int batch, int lane, AmLane& am,
                                         uint64_t* am_slots, const Fusion& fu,
                                         const uint32_t* xn = nullptr) {
   using T = Traits<FMT>;
@@ -788,7 +771,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       // the entry's row groups are one contiguous range of items
       const int am_end = tab.am + 1 < tab.n ? tab.e[tab.am + 1].start : tab.total;
       if (cur_j == tab.am && !am.left && (item >= am_end || item >= tab.total))
-        am_leave<NB>(am, am_sh, am_slots, batch, lane);
+        am_leave<NB>(am, am_slots, batch, lane);
     }
     if (!more) break;
     if (switched) bias_sums();
@@ -814,16 +797,17 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_kernel(const GemvTable<1> 
   if (item >= tab.total) return;                 // no barriers in this kernel
   int j = 0;
   AmLane am;
-  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, am, nullptr, nullptr, Fusion{});
+  xreg_run<FMT, NB, R, NCH, 1>(tab, j, item, stride, batch, threadIdx.x & 63, am, nullptr, Fusion{});
 }
 
-constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most workgroups per launch
+constexpr int kFusedSlots = QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;   // most worker waves per launch
+constexpr int kFusedMaxWorkers = kFusedSlots / kWaves;              // ... workgroups
 constexpr int kFusedPerThread = kFusedSlots / kThreads;
 constexpr int kFusedSpinLimit = 1 << 20;
 
 // The fused argmax's last step, run by workgroup 0 of the launch, which does
-// no GEMV work: wait until every other workgroup has published its key for
-// each batch row (slots[b][w - 1] for workgroup w, nonzero once written),
+// no GEMV work: wait until every wave of the other workgroups has published
+// its key for each batch row (slots[b][am_slot()], nonzero once written),
 // take the largest, write the index, and clear the slots for the next call.
 // The argmax entry's row groups are the launch's first, so its keys are in
 // while the other entries still stream, and this wait overlaps them. All of
@@ -833,7 +817,7 @@ constexpr int kFusedSpinLimit = 1 << 20;
 __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, int batch,
                                                   int32_t* __restrict__ idx, uint64_t* red) {
   const int tid = threadIdx.x;
-  const int grid = gridDim.x - 1;                       // workers (workgroups 1..)
+  const int grid = (gridDim.x - 1) * kWaves;            // worker waves (workgroups 1..)
   for (int b = 0; b < batch; ++b) {
     uint64_t* row = slots + static_cast<size_t>(b) * kFusedSlots;
     uint64_t v[kFusedPerThread];
@@ -880,29 +864,23 @@ __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, 
 // AM: also idx[b] = argmax of row b of entry tab.am's output (the LM-head
 // logits), in the same launch. The host puts that entry first, so its row
 // groups are taken in the first rounds. Every lane folds the outputs it
-// stores into a key; when a wave is done with the entry its keys meet the
-// workgroup's in LDS (64-bit max), and the workgroup's last such wave
-// publishes one key per batch row into the workgroup's own word of the
-// caller's workspace with a relaxed device-scope store (no two workgroups
-// touch one address: same-address atomics from hundreds of workgroups would
-// queue up). The launch's last workgroup collects the words at its end
-// (fused_argmax_tail), by which time they are normally all there. A
-// workgroup that stored no output of the entry publishes key 1, which never
-// wins.
+// stores into a key; when a wave is done with the entry it publishes one key
+// per batch row (a wave-wide max) into its own word of the caller's
+// workspace with a relaxed device-scope store (no two waves touch one
+// address: same-address atomics from thousands of waves would queue up).
+// Workgroup 0 does no GEMV work and collects the words (fused_argmax_tail),
+// most of them while the other entries still stream. A wave that stored no
+// output of the entry publishes key 1, which never wins.
 template <int FMT, int NB, int N, bool AM>
 __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTable<N> tab, int batch,
                                                                    uint64_t* __restrict__ slots,
                                                                    int32_t* __restrict__ idx) {
-  __shared__ AmShared am_sh;
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
     if (blockIdx.x == 0) {                      // the collector
       fused_argmax_tail(slots, batch, idx, red);
       return;
     }
-    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
-    if (threadIdx.x == 0) am_sh.left = 0;
-    __syncthreads();
   }
   int stride;
   int item = first_item<AM ? 1 : 0>(stride);
@@ -913,12 +891,12 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
     while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
     while (item < tab.total) {
       if constexpr (AM) {
-        if (j > tab.am && !am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);   // past the entry
+        if (j > tab.am && !am.left) am_leave<NB>(am, slots, batch, lane);   // past the entry
       }
       switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
         case xreg_shape(R_, C_): \
-          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots, Fusion{}); break;
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}); break;
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
@@ -926,7 +904,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
         case xreg_shape(1, 8):                   // int8 at batch 1 only
           if constexpr (is_int8_fmt(FMT) && NB == 1)
-            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, &am_sh, slots, Fusion{});
+            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{});
           else
             item = tab.total;
           break;
@@ -936,7 +914,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
     }
   }
   if constexpr (AM) {
-    if (!am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);
+    if (!am.left) am_leave<NB>(am, slots, batch, lane);
   }
 }
 
@@ -1608,7 +1586,6 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
                                                                    int32_t* __restrict__ idx,
                                                                    const Fusion fu) {
   extern __shared__ u32x4 lds_v4[];
-  __shared__ AmShared am_sh;
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
     if (blockIdx.x == 0) {                      // the collector (see fused_argmax_tail)
@@ -1623,21 +1600,16 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
     stage_norm_rows<NB>(fu, K, batch, xs, reinterpret_cast<float*>(xs + NB * (K >> 1)));
     xn = xs;
   }
-  if constexpr (AM) {
-    if (threadIdx.x < QGEMV_MAX_BATCH) am_sh.key[threadIdx.x] = 1;
-    if (threadIdx.x == 0) am_sh.left = 0;
-    __syncthreads();
-  }
   int stride;
   int item = first_item<AM ? 1 : 0>(stride);
   const int lane = threadIdx.x & 63;
   AmLane am;
   if (item < tab.total) {
     int j = 0;
-    xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, &am_sh, slots, fu, xn);
+    xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, slots, fu, xn);
   }
   if constexpr (AM) {
-    if (!am.left) am_leave<NB>(am, &am_sh, slots, batch, lane);
+    if (!am.left) am_leave<NB>(am, slots, batch, lane);
   }
 }
 
@@ -1957,7 +1929,7 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
     // collector waits for every worker's key
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_group_kernel<FMT, NB, kGroupMax, true>));
-    grid = std::max(1, std::min(grid, cus * per_cu - 1)) + 1;
+    grid = std::max(1, std::min({grid, cus * per_cu - 1, kFusedMaxWorkers})) + 1;
     gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<grid, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
@@ -2202,7 +2174,7 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int a
     total += (a[i].M + R[i] - 1) / R[i];
   }
   long cap = static_cast<long>(cus) * QGEMV_GROUP_MAX_WG_PER_CU;
-  if (am >= 0 && cap > kFusedSlots) cap = kFusedSlots;       // one argmax slot per workgroup
+  if (am >= 0 && cap > kFusedMaxWorkers) cap = kFusedMaxWorkers;   // one argmax slot per worker wave
   const int grid = static_cast<int>(std::max<long>(1, std::min<long>((total + kWaves - 1) / kWaves, cap)));
   return with_fmt(a[0].fmt, [&](auto F) {
     return launch_group1<decltype(F)::value>(a, R, nch, n, grid, am, slots, idx, stream);
@@ -2231,7 +2203,7 @@ hipError_t launch_fused_xreg(const GemvArgs& a, const Fusion& f, uint64_t* slots
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_fused_kernel<FMT, NB, R, NCH, true>));
     // workers plus the collector (workgroup 0), all resident at once
-    grid = std::max(1, std::min({grid, cus * std::min(per_cu, lds_cap) - 1, static_cast<int>(kFusedSlots)})) + 1;
+    grid = std::max(1, std::min({grid, cus * std::min(per_cu, lds_cap) - 1, kFusedMaxWorkers})) + 1;
     gemv_xreg_fused_kernel<FMT, NB, R, NCH, true><<<grid, kThreads, lds, st>>>(tab, a.batch, slots, idx, f);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(

@@ -263,7 +263,7 @@ int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_
  * producing kernel to save launches).
  * When the small-batch kernel computes the argmax entry (batch <= 2, row
  * length as in qgemv_run_grouped), the argmax runs inside that launch: each
- * workgroup folds the logits it writes into one key per batch row and
+ * wave folds the logits it writes into one key per batch row and
  * publishes it in its own word of ws, and one workgroup of the launch, which
  * does no GEMV work, collects the words while the other entries still
  * stream and takes the largest; no separate launch and no second pass over
