@@ -610,12 +610,16 @@ __device__ __forceinline__ void am_leave(AmLane& am, uint64_t* __restrict__ slot
 // With AM, every output of entry tab.am a lane stores also goes into the
 // lane's running argmax key, and after the wave's last row group of that
 // entry the wave hands its keys over (am_leave).
-// FUSED: the RMSNorm prologue and the epilogue of fu (one-entry tables).
+// FUSED: the RMSNorm prologue (into xn, when given) and the epilogue of fu
+// (one-entry tables).
+template <int NB>
+__device__ __forceinline__ void stage_norm_rows(const Fusion& fu, int K, int batch, uint32_t* xs, float* scr);
+
 template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
                                         int batch, int lane, AmLane& am,
                                         uint64_t* am_slots, const Fusion& fu,
-                                        const uint32_t* xn = nullptr) {
+                                        uint32_t* xn = nullptr) {
   using T = Traits<FMT>;
   static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
   constexpr int P = T::kPairs;
@@ -630,7 +634,9 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
   int woff[NCH], soff[NCH];
 
   // make entry j current: its geometry and this lane's x registers
-  auto enter = [&](int jj) {
+  // make entry j current: its geometry (enter_geom), then this lane's x
+  // registers (enter_x)
+  auto enter_geom = [&](int jj) {
     const TableEntry& e = tab.e[jj];
     W = e.W; S = e.S; Y = e.Y; M = e.M; start = e.start;
     next_start = (N > 1 && jj + 1 < tab.n) ? tab.e[jj + 1].start : tab.total;
@@ -643,6 +649,9 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
       woff[c] = t * 16;
       soff[c] = scale_index<FMT>(t) * 2;
     }
+  };
+  auto enter_x = [&](int jj) {
+    const TableEntry& e = tab.e[jj];
     // (fused prologue: x was normalized into LDS by the workgroup, xn)
     const uint32_t* xsrc = reinterpret_cast<const uint32_t*>(e.X);
     if constexpr (FUSED) {
@@ -654,6 +663,10 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
 #pragma unroll
       for (int c = 0; c < NCH; ++c) read_x<FMT>(xb, min(c * 64 + lane, U - 1), xr[b][c]);
     }
+  };
+  auto enter = [&](int jj) {
+    enter_geom(jj);
+    enter_x(jj);
   };
 
   u32x4 wv[R][NCH];
@@ -691,8 +704,28 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     }
   };
 
-  enter(j);
-  load_step(item - start);
+  if constexpr (FUSED) {
+    // The first row group's weight loads go out first: before the workgroup
+    // normalizes x into LDS (every wave of the workgroup takes part in that,
+    // with or without a row group of its own) and before this lane's x
+    // loads, so their latency overlaps the prologue's. (In the unfused
+    // kernels x is loaded first: issuing the weights first measured slower
+    // on the grouped launch with the argmax.)
+    const bool active = item < tab.total;
+    if (active) {
+      enter_geom(j);
+      load_step(item - start);
+    }
+    if (xn != nullptr) {
+      const int K0 = tab.e[0].K;
+      stage_norm_rows<NB>(fu, K0, batch, xn, reinterpret_cast<float*>(xn + NB * (K0 >> 1)));
+    }
+    if (!active) return item;
+    enter_x(j);
+  } else {
+    enter(j);
+    load_step(item - start);
+  }
   bias_sums();
 
   float acc[R][NB];
@@ -1593,18 +1626,14 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
       return;
     }
   }
-  const uint32_t* xn = nullptr;
-  if (fu.h != nullptr) {
-    uint32_t* xs = reinterpret_cast<uint32_t*>(lds_v4);
-    const int K = tab.e[0].K;
-    stage_norm_rows<NB>(fu, K, batch, xs, reinterpret_cast<float*>(xs + NB * (K >> 1)));
-    xn = xs;
-  }
+  // (with the prologue, every wave runs xreg_run, which normalizes x into
+  // LDS with the whole workgroup after issuing its first weight loads)
+  uint32_t* xn = fu.h != nullptr ? reinterpret_cast<uint32_t*>(lds_v4) : nullptr;
   int stride;
   int item = first_item<AM ? 1 : 0>(stride);
   const int lane = threadIdx.x & 63;
   AmLane am;
-  if (item < tab.total) {
+  if (xn != nullptr || item < tab.total) {
     int j = 0;
     xreg_run<FMT, NB, R, NCH, 1, AM, true>(tab, j, item, stride, batch, lane, am, slots, fu, xn);
   }

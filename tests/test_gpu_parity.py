@@ -312,7 +312,7 @@ def _grouped(gemvs, B):
 
 
 @pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (3, 1), (5, 1), (5, 2), (1, 2),
-                                   (2, 4), (2, 8), (3, 4), (5, 8), (1, 8)])
+                                   (2, 4), (2, 8), (3, 4), (5, 8), (1, 8), (6, 1), (6, 8)])
 def test_grouped_workload_parity(cfg, B):
     gemvs = [synth.make_gemv(sp.name, sp.fmt, sp.M, sp.K, B, sp.cfg, sp.layer, sp.proj)
              for sp in synth.workload_specs(cfg)]
@@ -427,7 +427,7 @@ def _grouped_argmax(gemvs, B, am, ws=None):
     return [it[4].cpu().numpy() for it in dev_items], idx.cpu().numpy(), ws
 
 
-@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (5, 1), (5, 2), (2, 4), (5, 8)])
+@pytest.mark.parametrize("cfg,B", [(2, 1), (2, 2), (5, 1), (5, 2), (2, 4), (5, 8), (6, 1), (6, 2), (6, 8)])
 def test_grouped_argmax_workloads(cfg, B):
     """The step's GEMVs and the LM-head argmax in one call (fused into the LM head's launch
     at B <= 2, a separate argmax launch otherwise): logits within the GEMV tolerance, the
