@@ -68,6 +68,9 @@
 #ifndef QGEMV_NT_LOADS
 #define QGEMV_NT_LOADS 1          // stream weights with non-temporal loads
 #endif
+#ifndef QGEMV_GROUP_CONTIG_MIN
+#define QGEMV_GROUP_CONTIG_MIN 8  // grouped launch: row groups per wave from which waves take contiguous ranges
+#endif
 #ifndef QGEMV_MFMA_TARGET_WAVES_PER_CU
 #define QGEMV_MFMA_TARGET_WAVES_PER_CU 16  // matrix-core kernel: waves per CU worth aiming for
 #endif
@@ -527,7 +530,7 @@ struct GemvTable {
   int n;        // entries
   int total;    // row groups over all entries
   int am;       // entry whose outputs the fused argmax reads (grouped launch with argmax)
-  int pad;
+  int contig;   // nonzero: each wave takes one contiguous range of row groups (grouped launch)
   TableEntry e[N];
 };
 
@@ -539,11 +542,12 @@ struct GemvTable {
 //
 // The kernel walks a table of GEMVs (one entry for qgemv_run, up to N for a
 // grouped launch of independent GEMVs): the row groups of all entries are
-// numbered consecutively and waves take them in a grid-stride loop, so one
-// launch streams every entry's weights and pays the launch and ramp-up cost
-// once. A wave reloads its x registers when its next row group belongs to
-// another entry, and issues that group's loads before reducing the current
-// one unless the entry's (R, NCH) differs.
+// numbered consecutively and waves take them in a grid-stride loop (or, in
+// a grouped launch with many row groups per wave, one contiguous range
+// each), so one launch streams every entry's weights and pays the launch
+// and ramp-up cost once. A wave reloads its x registers when its next row
+// group belongs to another entry, and issues that group's loads before
+// reducing the current one unless the entry's (R, NCH) differs.
 // Fused-argmax state of a lane (see gemv_xreg_group_kernel): its running key
 // over the LM-head outputs it stored, their batch row, and whether its wave
 // has already published its keys.
@@ -619,7 +623,8 @@ template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = 
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
                                         int batch, int lane, AmLane& am,
                                         uint64_t* am_slots, const Fusion& fu,
-                                        uint32_t* xn = nullptr) {
+                                        uint32_t* xn = nullptr, int end = -1) {
+  if (end < 0) end = tab.total;                  // row groups item, item + stride, ... below end
   using T = Traits<FMT>;
   static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
   constexpr int P = T::kPairs;
@@ -711,7 +716,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     // loads, so their latency overlaps the prologue's. (In the unfused
     // kernels x is loaded first: issuing the weights first measured slower
     // on the grouped launch with the argmax.)
-    const bool active = item < tab.total;
+    const bool active = item < end;
     if (active) {
       enter_geom(j);
       load_step(item - start);
@@ -756,7 +761,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     const int cur_j = j;
     float* cur_Y = Y;
     item += stride;
-    bool more = item < tab.total;
+    bool more = item < end;
     bool switched = false;
     if (more) {
       if constexpr (N > 1) {
@@ -803,7 +808,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     if constexpr (AM) {
       // the entry's row groups are one contiguous range of items
       const int am_end = tab.am + 1 < tab.n ? tab.e[tab.am + 1].start : tab.total;
-      if (cur_j == tab.am && !am.left && (item >= am_end || item >= tab.total))
+      if (cur_j == tab.am && !am.left && (item >= am_end || item >= end))
         am_leave<NB>(am, am_slots, batch, lane);
     }
     if (!more) break;
@@ -917,19 +922,30 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
   }
   int stride;
   int item = first_item<AM ? 1 : 0>(stride);
+  int end = tab.total;
+  if (tab.contig) {
+    // one contiguous range of row groups per wave (waves in order), so a
+    // wave stays in one entry for many steps instead of reloading x at
+    // almost every step
+    const int nw = stride, wid = item;
+    const int per = tab.total / nw, rem = tab.total % nw;
+    item = wid * per + min(wid, rem);
+    end = item + per + (wid < rem ? 1 : 0);
+    stride = 1;
+  }
   const int lane = threadIdx.x & 63;
   AmLane am;
-  if (item < tab.total) {
+  if (item < end) {
     int j = 0;
     while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
-    while (item < tab.total) {
+    while (item < end) {
       if constexpr (AM) {
         if (j > tab.am && !am.left) am_leave<NB>(am, slots, batch, lane);   // past the entry
       }
       switch (tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
         case xreg_shape(R_, C_): \
-          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}); break;
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end); break;
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
@@ -937,7 +953,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
         case xreg_shape(1, 8):                   // int8 at batch 1 only
           if constexpr (is_int8_fmt(FMT) && NB == 1)
-            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{});
+            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end);
           else
             item = tab.total;
           break;
@@ -1959,11 +1975,13 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_group_kernel<FMT, NB, kGroupMax, true>));
     grid = std::max(1, std::min({grid, cus * per_cu - 1, kFusedMaxWorkers})) + 1;
+    tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * (grid - 1) * kWaves;
     gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<grid, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
   } else {
     static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
         &gemv_xreg_group_kernel<FMT, NB, kGroupMax, false>));
     grid = std::min(grid, cus * per_cu);
+    tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * grid * kWaves;
     gemv_xreg_group_kernel<FMT, NB, kGroupMax, false><<<grid, kThreads, 0, st>>>(tab, a[0].batch, nullptr, nullptr);
   }
   return hipGetLastError();

@@ -443,6 +443,25 @@ def test_grouped_argmax_workloads(cfg, B):
     assert (ws.cpu().numpy() == 0).all()
 
 
+@pytest.mark.parametrize("B", [1, 2])
+def test_grouped_argmax_decode_step_stream_contiguous_ranges(B):
+    """The 89-GEMV decode-step stream with the LM-head argmax in one call at B <= 2: about
+    38 row groups per wave, so every wave takes one contiguous range of them (the LM head's
+    rows go to the first few hundred waves only). Sampled rows of every GEMV against the
+    oracle, the index bit-exact against the oracle's argmax of the GPU's own logits, ws
+    back to zero."""
+    gemvs = synth.make_workload(4, B)
+    am = len(gemvs) - 1
+    ys, idx, ws = _grouped_argmax(gemvs, B, am)
+    rng = np.random.default_rng(11)
+    for g, y in zip(gemvs, ys):
+        rows = np.unique(np.concatenate([[0, g.M - 1], rng.choice(g.M, 30, replace=False)]))
+        assert np.isfinite(y).all(), g.name
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=rows, what=f"stream {g.name}")
+    assert (idx == oracle.argmax_ref(ys[am])).all(), (idx, oracle.argmax_ref(ys[am]))
+    assert (ws.cpu().numpy() == 0).all()
+
+
 def test_grouped_argmax_ties_across_workgroups():
     """bf16 LM head whose rows give exactly 0 except rows made negative: the maximum 0.0 is
     tied at rows far apart (different waves and workgroups); the lowest index must win,
