@@ -447,8 +447,8 @@ def cpu_baseline(wl, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
-                          "of the GEMV is described in DESIGN.md but not built",
+        print(json.dumps({"error": "qgemv runs on one GPU; a step is not sharded across GPUs, "
+                          "so --gpus above 1 is not supported",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
