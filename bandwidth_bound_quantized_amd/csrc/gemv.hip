@@ -852,35 +852,47 @@ constexpr int kFusedSpinLimit = 1 << 20;
 // a thread's slot loads are in flight together; the wait is bounded (a key
 // never published - which needs a workgroup that never runs - gives idx -1
 // instead of a hang).
+//
+// kFusedChunk: a thread's words are taken that many at a time (their loads
+// in flight together). All at once (kFusedPerThread) is fastest when the
+// keys arrive early and the workers need more registers than the collector
+// anyway (the grouped launch); 4 keeps the collector's registers, which set
+// the whole kernel's budget, below a small worker's (the fused single GEMV).
+template <int kFusedChunk>
 __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, int batch,
                                                   int32_t* __restrict__ idx, uint64_t* red) {
+  static_assert(kFusedPerThread % kFusedChunk == 0, "collector chunks");
   const int tid = threadIdx.x;
   const int grid = (gridDim.x - 1) * kWaves;            // worker waves (workgroups 1..)
   for (int b = 0; b < batch; ++b) {
     uint64_t* row = slots + static_cast<size_t>(b) * kFusedSlots;
-    uint64_t v[kFusedPerThread];
-#pragma unroll
-    for (int k = 0; k < kFusedPerThread; ++k) v[k] = 0;
-    bool pending = true;
-    for (int spin = 0; pending && spin < kFusedSpinLimit; ++spin) {
-#pragma unroll
-      for (int k = 0; k < kFusedPerThread; ++k) {
-        const int w = tid + k * kThreads;
-        if (w < grid && v[k] == 0) v[k] = __hip_atomic_load(row + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      pending = false;
-#pragma unroll
-      for (int k = 0; k < kFusedPerThread; ++k) pending |= (tid + k * kThreads < grid) && v[k] == 0;
-      if (pending) __builtin_amdgcn_s_sleep(2);
-    }
     uint64_t key = 1;
+    bool pending = false;
+    for (int k0 = 0; k0 < kFusedPerThread && k0 * kThreads < grid; k0 += kFusedChunk) {
+      uint64_t v[kFusedChunk];
 #pragma unroll
-    for (int k = 0; k < kFusedPerThread; ++k) {
-      const int w = tid + k * kThreads;
-      if (w < grid) {
-        key = umax64(key, v[k]);
-        __hip_atomic_store(row + w, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = 0; k < kFusedChunk; ++k) v[k] = 0;
+      pending = true;
+      for (int spin = 0; pending && spin < kFusedSpinLimit; ++spin) {
+#pragma unroll
+        for (int k = 0; k < kFusedChunk; ++k) {
+          const int w = tid + (k0 + k) * kThreads;
+          if (w < grid && v[k] == 0) v[k] = __hip_atomic_load(row + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        pending = false;
+#pragma unroll
+        for (int k = 0; k < kFusedChunk; ++k) pending |= (tid + (k0 + k) * kThreads < grid) && v[k] == 0;
+        if (pending) __builtin_amdgcn_s_sleep(2);
       }
+#pragma unroll
+      for (int k = 0; k < kFusedChunk; ++k) {
+        const int w = tid + (k0 + k) * kThreads;
+        if (w < grid) {
+          key = umax64(key, v[k]);
+          __hip_atomic_store(row + w, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (pending) break;                                // bounded wait ran out: idx -1
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) key = umax64(key, __shfl_xor(key, o));
@@ -916,7 +928,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
     if (blockIdx.x == 0) {                      // the collector
-      fused_argmax_tail(slots, batch, idx, red);
+      fused_argmax_tail<kFusedPerThread>(slots, batch, idx, red);
       return;
     }
   }
@@ -1638,7 +1650,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_fused_kernel(const GemvTab
   __shared__ uint64_t red[kWaves];
   if constexpr (AM) {
     if (blockIdx.x == 0) {                      // the collector (see fused_argmax_tail)
-      fused_argmax_tail(slots, batch, idx, red);
+      fused_argmax_tail<4>(slots, batch, idx, red);
       return;
     }
   }
