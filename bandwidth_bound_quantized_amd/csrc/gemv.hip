@@ -961,6 +961,12 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
+        case xreg_shape(8, 1):                   // batch 1, contiguous ranges only
+          if constexpr (NB == 1)
+            item = xreg_run<FMT, NB, 8, 1, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end);
+          else
+            item = end;
+          break;
         QG_SHAPE(QGEMV_GROUP_R2, 2)
         QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
         case xreg_shape(1, 8):                   // int8 at batch 1 only
@@ -1956,7 +1962,7 @@ constexpr int kGroupMax = 64;       // GEMVs per grouped launch (kernel-argument
 // Entries of one format and batch with their (R, NCH) already chosen; am >= 0:
 // also the argmax of entry am's output (into idx, through slots).
 template <int FMT, int NB>
-hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n, int grid, int am,
+hipError_t launch_group2(const GemvArgs* a, const int* R_in, const int* nch, int n, int grid, int am,
                          uint64_t* slots, int32_t* idx, hipStream_t st) {
   GemvTable<kGroupMax> tab{};
   tab.n = n;
@@ -1965,36 +1971,51 @@ hipError_t launch_group2(const GemvArgs* a, const int* R, const int* nch, int n,
   // group size measured slower)
   int order[kGroupMax];
   for (int t = 0; t < n; ++t) order[t] = am < 0 ? t : t == 0 ? am : (t <= am ? t - 1 : t);
-  tab.am = -1;
-  int start = 0;
-  for (int t = 0; t < n; ++t) {
-    const int i = order[t];
-    if (i == am) tab.am = t;
-    tab.e[t] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
-                          a[i].M, a[i].K, start, xreg_shape(R[i], nch[i])};
-    start += (a[i].M + R[i] - 1) / R[i];
-  }
-  tab.total = start;
+  int R[kGroupMax];
+  for (int i = 0; i < n; ++i) R[i] = R_in[i];
+  auto build = [&]() {
+    tab.am = -1;
+    int start = 0;
+    for (int t = 0; t < n; ++t) {
+      const int i = order[t];
+      if (i == am) tab.am = t;
+      tab.e[t] = TableEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
+                            a[i].M, a[i].K, start, xreg_shape(R[i], nch[i])};
+      start += (a[i].M + R[i] - 1) / R[i];
+    }
+    tab.total = start;
+  };
+  build();
   // The grid is at most what is resident at once (workgroups per CU from the
   // kernel's register budget): a second, partial round of workgroups would
   // restart row groups' x loads and leave most CUs idle at its end
   // (measured: 15.1 vs 17.3 us for the TinyLlama set at 3 resident
   // workgroups per CU against a grid of 8 per CU).
   const int cus = device_cu_count();
+  static const int per_cu_am = resident_per_cu(reinterpret_cast<const void*>(
+      &gemv_xreg_group_kernel<FMT, NB, kGroupMax, true>));
+  static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
+      &gemv_xreg_group_kernel<FMT, NB, kGroupMax, false>));
+  // (with the argmax: workers plus the collector, workgroup 0, all resident
+  // at once, since the collector waits for every worker's key)
+  const int workers = am >= 0 ? std::max(1, std::min({grid, cus * per_cu_am - 1, kFusedMaxWorkers}))
+                              : std::min(grid, cus * per_cu);
+  tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * workers * kWaves;
+  if (tab.contig && NB == 1) {
+    // contiguous ranges: the short rows eight at a time (more bytes in
+    // flight per wave; the tail balance that favours four is moot here)
+    bool any = false;
+    for (int i = 0; i < n; ++i)
+      if (nch[i] == 1 && R[i] == 4) { R[i] = 8; any = true; }
+    if (any) {
+      build();
+      tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * workers * kWaves;
+    }
+  }
   if (am >= 0) {
-    // workers plus the collector (workgroup 0), all resident at once: the
-    // collector waits for every worker's key
-    static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
-        &gemv_xreg_group_kernel<FMT, NB, kGroupMax, true>));
-    grid = std::max(1, std::min({grid, cus * per_cu - 1, kFusedMaxWorkers})) + 1;
-    tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * (grid - 1) * kWaves;
-    gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<grid, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
+    gemv_xreg_group_kernel<FMT, NB, kGroupMax, true><<<workers + 1, kThreads, 0, st>>>(tab, a[0].batch, slots, idx);
   } else {
-    static const int per_cu = resident_per_cu(reinterpret_cast<const void*>(
-        &gemv_xreg_group_kernel<FMT, NB, kGroupMax, false>));
-    grid = std::min(grid, cus * per_cu);
-    tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * grid * kWaves;
-    gemv_xreg_group_kernel<FMT, NB, kGroupMax, false><<<grid, kThreads, 0, st>>>(tab, a[0].batch, nullptr, nullptr);
+    gemv_xreg_group_kernel<FMT, NB, kGroupMax, false><<<workers, kThreads, 0, st>>>(tab, a[0].batch, nullptr, nullptr);
   }
   return hipGetLastError();
 }
