@@ -2009,7 +2009,11 @@ hipError_t launch_group2(const GemvArgs* a, const int* R_in, const int* nch, int
       if (nch[i] == 1 && R[i] == 4) { R[i] = 8; any = true; }
     if (any) {
       build();
-      tab.contig = tab.total >= QGEMV_GROUP_CONTIG_MIN * workers * kWaves;
+      if (tab.total < QGEMV_GROUP_CONTIG_MIN * workers * kWaves) {
+        // (too few row groups per wave at eight rows: keep four)
+        for (int i = 0; i < n; ++i) R[i] = R_in[i];
+        build();
+      }
     }
   }
   if (am >= 0) {

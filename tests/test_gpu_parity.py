@@ -365,6 +365,20 @@ def test_grouped_class_of_the_workload_shapes():
         assert qg.grouped_class(fmt, K, B) == want, (qg.FMT_NAMES[fmt], K, B)
 
 
+def test_grouped_contiguous_ranges_at_four_rows():
+    """40 Q4_0 GEMVs of 3000x2048 at B=1: about 10 row groups of four rows per wave, so
+    the waves take contiguous ranges, but at eight rows per step they would get fewer than
+    eight each, so the launch keeps four. Sampled rows of every GEMV against the oracle."""
+    B = 1
+    gemvs = [synth.make_gemv(f"c{i}", synth.Q4_0_G32, 3000, 2048, B, 6, 200 + i, "gate_up") for i in range(40)]
+    ys = _grouped(gemvs, B)
+    rng = np.random.default_rng(13)
+    for g, y in zip(gemvs, ys):
+        rows = np.unique(np.concatenate([[0, g.M - 1], rng.choice(g.M, 30, replace=False)]))
+        assert np.isfinite(y).all(), g.name
+        assert_parity(g.fmt, g.w, g.s, g.x, g.M, g.K, B, y, rows=rows, what=g.name)
+
+
 def test_grouped_more_than_one_launch_per_class():
     """130 small Q4_0 GEMVs: more than the 64 entries one launch's table holds."""
     B = 1
