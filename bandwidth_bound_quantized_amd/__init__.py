@@ -204,10 +204,10 @@ def attention_workspace_size(batch: int, n_q: int, n_kv: int, head_dim: int, max
 
 
 def attention_workspace(batch: int, n_q: int, n_kv: int, head_dim: int, max_ctx: int, device="cuda"):
-    """A zero-filled workspace for attention_decode (its counters are left zero by every call)."""
+    """A workspace for attention_decode (the splits' partial results; contents on entry do not matter)."""
     import torch
     n = attention_workspace_size(batch, n_q, n_kv, head_dim, max_ctx)
-    return torch.zeros((n + 15) // 16 * 4, dtype=torch.int32, device=device)
+    return torch.empty((n + 15) // 16 * 4, dtype=torch.int32, device=device)
 
 
 def attention_decode(q, k_cache, v_cache, ctx_lens, out, batch: int, n_q: int, n_kv: int, head_dim: int,

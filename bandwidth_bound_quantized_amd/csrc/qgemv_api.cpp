@@ -335,7 +335,7 @@ int qgemv_attention_workspace_size(int batch, int n_q, int n_kv, int head_dim, i
   const int st = check_attention_shape(batch, n_q, n_kv, head_dim, max_ctx);
   if (st) return st;
   const qgemv::AttnPlan p = qgemv::attention_plan(batch, n_q, n_kv, head_dim, max_ctx);
-  *bytes = p.counter_bytes + p.part_bytes;
+  *bytes = std::max<size_t>(256, p.part_bytes);         // (never zero: ws is always a real buffer)
   return QGEMV_OK;
 }
 

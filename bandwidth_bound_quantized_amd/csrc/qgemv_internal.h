@@ -111,12 +111,11 @@ struct AttnArgs {
   void* ws;
 };
 // How the context is split: `splits` workgroups per (sequence, key/value
-// head), `positions` each; the workspace holds counter_bytes of arrival
-// counters (zero between calls) and part_bytes of per-split records.
+// head), `positions` each; the workspace holds part_bytes of per-split
+// records (none with one split).
 struct AttnPlan {
   int splits = 1;
   int positions = 0;
-  size_t counter_bytes = 0;
   size_t part_bytes = 0;
 };
 AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx);

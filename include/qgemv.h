@@ -351,9 +351,10 @@ int qgemv_run_fused(int fmt, const void* W, const uint16_t* scales, const uint16
  *   0 <= t < ctx_lens[b].
  *
  * qgemv_attention_workspace_size - bytes of device workspace a call with
- * this shape needs (*bytes; host only, no HIP calls). The workspace must be
- * all zero before its first use; every call leaves its counters zero again.
- * Calls that may run concurrently need distinct workspaces.
+ * this shape needs (*bytes, at least 256; host only, no HIP calls). It holds
+ * the splits' partial results between the call's two kernels; its contents
+ * on entry do not matter. Calls that may run concurrently need distinct
+ * workspaces.
  * Errors: EINVAL (null bytes), ESHAPE (as below).
  */
 int qgemv_attention_workspace_size(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx,
@@ -373,9 +374,10 @@ int qgemv_attention_workspace_size(int batch, int n_q, int n_kv, int head_dim, i
  * Shapes: batch >= 1, n_kv >= 1, n_q = G * n_kv with G in {1, 2, 4, 8},
  * head_dim 64 or 128, 1 <= max_ctx with (max_ctx + 64) * head_dim * 2 < 2^32;
  * scale > 0 and finite (1/sqrt(head_dim) for Llama models).
- * Float32 arithmetic on the bf16 cache values. One launch; asynchronous on
- * `stream`. Errors: EINVAL (null pointer, non-finite or non-positive
- * scale), ESHAPE, EALIGN, EHIP.
+ * Float32 arithmetic on the bf16 cache values. One launch, or two when the
+ * context is split over several workgroups (the second merges the splits);
+ * asynchronous on `stream`. Errors: EINVAL (null pointer, non-finite or
+ * non-positive scale), ESHAPE, EALIGN, EHIP.
  */
 int qgemv_attention_decode(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
                            const int32_t* ctx_lens, float* out, int batch, int n_q, int n_kv,

@@ -214,7 +214,10 @@ def test_attention_workspace_and_validation():
     n = ctypes.c_size_t()
     # Llama-3.2-1B heads at context 2048: 8 splits of 256 positions per key/value head
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, ctypes.byref(n)) == qg.OK
-    assert n.value == 256 + 8 * 8 * (2 * 4 + 4 * 64) * 4
+    assert n.value == 8 * 8 * (2 * 4 + 4 * 64) * 4
+    # one split (short context): no records, the 256-byte minimum
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 256, ctypes.byref(n)) == qg.OK
+    assert n.value == 256
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, None) == qg.EINVAL
     for args in ((1, 24, 8, 64, 2048), (1, 32, 8, 96, 2048), (1, 32, 8, 64, 0), (0, 32, 8, 64, 16),
                  (1, 32, 0, 64, 16), (1, 32, 8, 128, 1 << 24)):

@@ -60,9 +60,7 @@ def test_attention_parity(B, n_q, n_kv, d, T):
     at = synth.make_attention(B, n_q, n_kv, d, T, seed=B * 1000 + n_q + T)
     out, ws = gpu_attention(at, n_q, n_kv, d, T)
     check(at, out, f"B={B} {n_q}/{n_kv} d={d} T={T}")
-    # counters left zero for the next call; the same inputs give the same bits
-    n_cnt = (B * n_kv * 4 + 255) // 256 * 64
-    assert (ws[:n_cnt] == 0).all()
+    # the workspace reused as it was left: the same inputs give the same bits
     out2, _ = gpu_attention(at, n_q, n_kv, d, T, ws=ws)
     assert (out.view(np.uint32) == out2.view(np.uint32)).all()
 
