@@ -46,7 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define QGEMV_ATTN_WAVES 4        // waves per workgroup
 #endif
 #ifndef QGEMV_ATTN_MIN_BLOCKS
-#define QGEMV_ATTN_MIN_BLOCKS 2   // blocks per wave before the context is split further
+#define QGEMV_ATTN_MIN_BLOCKS 1   // blocks per wave before the context is split further
 #endif
 #ifndef QGEMV_ATTN_TARGET_WGS
 #define QGEMV_ATTN_TARGET_WGS 256 // workgroups worth splitting for
@@ -420,12 +420,12 @@ hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
 
 // Splits: up to about one workgroup per CU of a 256-CU device (the same
 // for every device, so the workspace size is a function of the shape
-// alone), at most 32, and at least two blocks per wave in a split, since
-// merging the splits costs a few memory round trips (a sweep of waves per
-// workgroup, blocks per wave, target workgroups and split cap on MI355X:
-// these defaults are best or within 3 % at contexts 512 - 32768, except
-// 8192, 13 % behind 8-wave workgroups); positions per split a multiple of
-// the waves' blocks.
+// alone), at most 32, and down to one block per wave in a split: with the
+// merge in a kernel of its own a split costs one record write and one read
+// (a sweep of blocks per wave, target workgroups and split cap on MI355X:
+// one block per wave is 20 % faster than two at context 2048 and equal from
+// 8192 up; more target workgroups or a cap of 64 were no faster);
+// positions per split a multiple of the waves' blocks.
 AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx) {
   const int G = n_q / n_kv;
   const int pp = 4096 / (G * head_dim);

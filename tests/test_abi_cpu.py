@@ -212,11 +212,11 @@ def test_run_fused_validation_errors_before_any_launch():
 def test_attention_workspace_and_validation():
     L = qg.lib()
     n = ctypes.c_size_t()
-    # Llama-3.2-1B heads at context 2048: 8 splits of 256 positions per key/value head
+    # Llama-3.2-1B heads at context 2048: 16 splits of 128 positions per key/value head
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, ctypes.byref(n)) == qg.OK
-    assert n.value == 8 * 8 * (2 * 4 + 4 * 64) * 4
+    assert n.value == 8 * 16 * (2 * 4 + 4 * 64) * 4
     # one split (short context): no records, the 256-byte minimum
-    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 256, ctypes.byref(n)) == qg.OK
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 128, ctypes.byref(n)) == qg.OK
     assert n.value == 256
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, None) == qg.EINVAL
     for args in ((1, 24, 8, 64, 2048), (1, 32, 8, 96, 2048), (1, 32, 8, 64, 0), (0, 32, 8, 64, 16),
