@@ -1228,11 +1228,81 @@ __device__ __forceinline__ void block_rms_factors(const Fusion& fu, int K, int b
 // xs[b][0..K) = bf16(h[b][k] * r_b * g[k]) for b < NB (rows past the batch
 // zero), 8 elements per 16-byte chunk. Barriers inside; every thread must
 // call it.
+//
+// One pass at batch <= 2 with at most two chunks of a row per thread (K <=
+// 16 * threads): thread t loads chunks t and t + threads of every row and
+// the matching g once, sums its squares (chunk t's eight elements, then
+// chunk t + threads'), the waves' sums go through LDS, and every thread adds
+// them in wave order for the factors of its rows, then scales the values it
+// holds. Otherwise h is read twice (block_rms_factors, then the scaling).
+// Either way a row's sum of squares is taken in an order set by K and the
+// workgroup size alone, not by the batch.
 template <int NB>
 __device__ __forceinline__ void stage_norm_rows(const Fusion& fu, int K, int batch, uint32_t* xs, float* scr) {
-  block_rms_factors<NB>(fu, K, batch, scr);
   const int row_chunks = K / 8, nxc = NB * row_chunks;
   const int nt = static_cast<int>(blockDim.x);
+  if constexpr (NB <= 2) {
+    if (row_chunks <= 2 * nt) {
+      const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+      f32x4 h0[NB][2], h1[NB][2];
+      u32x4 gg[2];
+      bool have[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = tid + u * nt;
+        have[u] = c < row_chunks;
+        gg[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) { h0[b][u] = f32x4{0.f, 0.f, 0.f, 0.f}; h1[b][u] = h0[b][u]; }
+        if (have[u]) {
+          gg[u] = *reinterpret_cast<const u32x4*>(fu.g + 8 * c);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            // rows past the batch re-read the last row (in bounds; stored as zero)
+            const float* hr = fu.h + static_cast<size_t>(min(b, batch - 1)) * K + 8 * c;
+            h0[b][u] = *reinterpret_cast<const f32x4*>(hr);
+            h1[b][u] = *reinterpret_cast<const f32x4*>(hr + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float sq = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sq = __builtin_fmaf(h0[b][u][e], h0[b][u][e], sq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sq = __builtin_fmaf(h1[b][u][e], h1[b][u][e], sq);
+        }
+        const float t = wave_sum(sq);
+        if (lane == 0) scr[wave * QGEMV_MAX_BATCH + b] = t;
+      }
+      __syncthreads();
+      const int nw = nt >> 6;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float t = 0.f;
+        for (int w = 0; w < nw; ++w) t += scr[w * QGEMV_MAX_BATCH + b];
+        const float r = b < batch ? rms_factor(t, K, fu.eps) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (!have[u]) continue;
+          const u32x4 g = gg[u];
+          const f32x4 a = h0[b][u], c = h1[b][u];
+          u32x4 v = {pack_bf16(a.x * r * bf16_lo(g.x), a.y * r * bf16_hi(g.x)),
+                     pack_bf16(a.z * r * bf16_lo(g.y), a.w * r * bf16_hi(g.y)),
+                     pack_bf16(c.x * r * bf16_lo(g.z), c.y * r * bf16_hi(g.z)),
+                     pack_bf16(c.z * r * bf16_lo(g.w), c.w * r * bf16_hi(g.w))};
+          if (b >= batch) v = u32x4{0u, 0u, 0u, 0u};
+          reinterpret_cast<u32x4*>(xs)[b * row_chunks + tid + u * nt] = v;
+        }
+      }
+      __syncthreads();
+      return;
+    }
+  }
+  block_rms_factors<NB>(fu, K, batch, scr);
   // rounds of four chunks per thread (their loads issued together) while
   // all four exist, then one chunk per round
   int base = threadIdx.x;
