@@ -58,6 +58,10 @@ constexpr int kAttnWaves = QGEMV_ATTN_WAVES;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = QGEMV_ATTN_MAX_SPLITS;
+#ifndef QGEMV_ATTN_MERGE_EARLY
+#define QGEMV_ATTN_MERGE_EARLY 8  // most splits whose accumulators the merge loads up front
+#endif
+constexpr int kMergeEarly = QGEMV_ATTN_MERGE_EARLY;
 
 template <int D, int G>
 struct AttnShape {
@@ -351,42 +355,71 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(
 // Merge of the S split records of one (b, key/value head) per workgroup:
 // per head, the largest split maximum M, the splits' weights 2^(m_s - M) and
 // the total weight, then each output the weighted sum of the splits'
-// accumulators over the total.
+// accumulators over the total. One thread per (split, head) works out its
+// weight; the accumulators of each thread's first output are loaded together
+// with the maxima and sums, so the merge makes one memory round trip.
 template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float* __restrict__ parts,
                                                                   float* __restrict__ out, int n_kv, int S) {
-  __shared__ float sh_f[kMaxSplits][G], sh_sl[kMaxSplits][G];
-  __shared__ float sh_den[G];
+  static_assert(kMaxSplits * G <= kAttnThreads, "one thread per (split, head)");
+  __shared__ float sh_m[kMaxSplits][G], sh_f[kMaxSplits][G], sh_fl[kMaxSplits][G];
   const int bh = blockIdx.x;
   const int b = bh / n_kv, kvh = bh - b * n_kv;
   const int tid = threadIdx.x;
-  const float* rec0 = parts + static_cast<size_t>(bh) * S * part_floats<D, G>();
-  // per (split, head): its max and sum, one load each, in parallel
-  for (int e = tid; e < S * G; e += kAttnThreads) {
-    const int s2 = e / G, g = e - s2 * G;
-    sh_f[s2][g] = rec0[s2 * part_floats<D, G>() + g];
-    sh_sl[s2][g] = rec0[s2 * part_floats<D, G>() + G + g];
+  constexpr int PF = part_floats<D, G>();
+  const float* rec0 = parts + static_cast<size_t>(bh) * S * PF;
+  // with few splits, this thread's first output's accumulators of every
+  // split are loaded together with the maxima and sums (one memory round
+  // trip); with more, after the weights (holding them all was slower)
+  const bool early = S <= kMergeEarly;
+  float pre[kMergeEarly];
+#pragma unroll
+  for (int s2 = 0; s2 < kMergeEarly; ++s2)
+    pre[s2] = (early && s2 < S && tid < G * D) ? rec0[s2 * PF + 2 * G + tid] : 0.f;
+  float sl = 0.f;
+  if (tid < S * G) {
+    const int s2 = tid / G, g = tid - s2 * G;
+    sh_m[s2][g] = rec0[s2 * PF + g];
+    sl = rec0[s2 * PF + G + g];
   }
   __syncthreads();
-  if (tid < G) {
+  // the weight of each (split, head), one per thread
+  if (tid < S * G) {
+    const int s2 = tid / G, g = tid - s2 * G;
     float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, sh_f[s2][tid]);
-    float den = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float ms = sh_f[s2][tid];
-      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      den += f * sh_sl[s2][tid];
-      sh_f[s2][tid] = f;
-    }
-    sh_den[tid] = den;
+    for (int t = 0; t < S; ++t) M = fmaxf(M, sh_m[t][g]);
+    const float ms = sh_m[s2][g];
+    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    sh_f[s2][g] = f;
+    sh_fl[s2][g] = f * sl;
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += kAttnThreads) {
+  // output e from the accumulators acc(s2)
+  auto store = [&](int e, float a, float den) {
     const int g = e / D, j = e - g * D;
-    float a = 0.f;
+    out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / den;
+  };
+  if (early && tid < G * D) {
+    const int g = tid / D;
+    float den = 0.f, a = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMergeEarly; ++s2) {
+      if (s2 < S) {
+        den += sh_fl[s2][g];
+        a += sh_f[s2][g] * pre[s2];
+      }
+    }
+    store(tid, a, den);
+  }
+  for (int e = early ? tid + kAttnThreads : tid; e < G * D; e += kAttnThreads) {
+    const int g = e / D;
+    float den = 0.f, a = 0.f;
 #pragma unroll 16
-    for (int s2 = 0; s2 < S; ++s2) a += sh_f[s2][g] * rec0[s2 * part_floats<D, G>() + 2 * G + e];
-    out[(static_cast<size_t>(b) * n_kv * G + kvh * G + g) * D + j] = a / sh_den[g];
+    for (int s2 = 0; s2 < S; ++s2) {
+      den += sh_fl[s2][g];
+      a += sh_f[s2][g] * rec0[s2 * PF + 2 * G + e];
+    }
+    store(e, a, den);
   }
 }
 
