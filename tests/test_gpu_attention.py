@@ -52,7 +52,9 @@ def check(at, out, what=""):
 # group size, one-split and many-split plans, ragged lengths
 SHAPES = [(1, 32, 8, 64, 512), (1, 32, 8, 64, 2048), (4, 32, 8, 64, 2048), (8, 32, 8, 64, 512),
           (1, 32, 4, 64, 2048), (2, 32, 4, 64, 1000), (1, 8, 8, 128, 4096), (3, 16, 8, 128, 777),
-          (1, 32, 8, 128, 2048), (2, 64, 8, 128, 1500), (1, 8, 4, 64, 8192), (5, 4, 4, 64, 130)]
+          (1, 32, 8, 128, 2048), (2, 64, 8, 128, 1500), (1, 8, 4, 64, 8192), (5, 4, 4, 64, 130),
+          # up to 8 splits with more outputs per (sequence, KV head) than merge threads
+          (8, 64, 8, 128, 300), (1, 16, 4, 128, 600)]
 
 
 @pytest.mark.parametrize("B,n_q,n_kv,d,T", SHAPES, ids=[f"b{b}-{q}x{k}-d{d}-ctx{t}" for b, q, k, d, t in SHAPES])
