@@ -142,3 +142,105 @@ def test_attention_planted_mistakes_are_caught(monkeypatch, name):
     except Exception:
         caught = True
     assert caught, f"planted mistake {name} went unnoticed"
+
+
+# ------------------------------------------------ the parity check itself
+# parity_report is the pass/fail rule every GPU attention test applies:
+# pass iff the output is finite and |out - ref| <= 1e-3 * A + 1e-5. These
+# pins drive it with hand-picked outputs on both sides of that bound.
+def _report_pins_ok() -> bool:
+    ref = np.array([[[1.0, -2.0, 0.0, 5.0]]])
+    A = np.array([[[10.0, 4.0, 0.0, 1000.0]]])          # bounds 0.01001, 0.00401, 1e-5, 1.00001
+    r = oatt.parity_report(ref.copy(), ref, A)
+    if not (r["ok"] and r["n"] == 4 and r["n_bad"] == 0 and r["max_err_over_bound"] == 0.0):
+        return False
+    inside = ref + np.array([[[0.010009, -0.004009, 0.0000099, -1.0000099]]])
+    r = oatt.parity_report(inside, ref, A)
+    if not r["ok"] or not (0.99 < r["max_err_over_bound"] <= 1.0):
+        return False
+    # each output pushed just outside its own bound, one at a time, either sign
+    for i, e in enumerate((0.010011, 0.004011, 0.0000101, 1.0000101)):
+        for sgn in (1.0, -1.0):
+            out = ref.copy()
+            out[0, 0, i] += sgn * e
+            r = oatt.parity_report(out, ref, A)
+            if r["ok"] or r["n_bad"] != 1 or not (1.0 < r["max_err_over_bound"] < 1.02):
+                return False
+    # values far off in the negative direction fail (all four bounds are below 3)
+    r = oatt.parity_report(ref - 3.0, ref, A)
+    if r["ok"] or r["n_bad"] != 4:
+        return False
+    # non-finite outputs fail and count as infinitely far, even where the bound is huge
+    bigA = np.full_like(A, 1e300)
+    for bad in (np.nan, np.inf, -np.inf):
+        out = ref.copy()
+        out[0, 0, 2] = bad
+        r = oatt.parity_report(out, ref, bigA)
+        if r["ok"] or r["n_bad"] != 1 or r["max_err_over_bound"] != np.inf:
+            return False
+    return True
+
+
+def test_attention_parity_report_definition():
+    assert _report_pins_ok()
+
+
+_orig_report = oatt.parity_report
+
+
+def _mut_report_abs_tol(scale):
+    def f(out_gpu, out_ref, A):
+        old = oatt.ABS_TOL
+        oatt.ABS_TOL = old * scale
+        try:
+            return _orig_report(out_gpu, out_ref, A)
+        finally:
+            oatt.ABS_TOL = old
+    return f
+
+
+def _mut_report_rel_tol(out_gpu, out_ref, A):
+    old = oatt.REL_TOL
+    oatt.REL_TOL = 1e-2
+    try:
+        return _orig_report(out_gpu, out_ref, A)
+    finally:
+        oatt.REL_TOL = old
+
+
+def _mut_report_no_finite(out_gpu, out_ref, A):
+    og = np.asarray(out_gpu, dtype=np.float64)
+    err = np.abs(og - out_ref)
+    bound = oatt.REL_TOL * A + oatt.ABS_TOL
+    with np.errstate(invalid="ignore"):
+        ok = ~(err > bound)
+        ratio = err / bound
+    return {"ok": bool(ok.all()), "n": int(ok.size), "n_bad": int((~ok).sum()),
+            "max_err_over_bound": float(np.nanmax(ratio))}
+
+
+def _mut_report_signed(out_gpu, out_ref, A):
+    og = np.asarray(out_gpu, dtype=np.float64)
+    err = og - out_ref
+    bound = oatt.REL_TOL * A + oatt.ABS_TOL
+    finite = np.isfinite(og)
+    ok = finite & (err <= bound)
+    ratio = np.where(finite, np.abs(err) / bound, np.inf)
+    return {"ok": bool(ok.all()), "n": int(ok.size), "n_bad": int((~ok).sum()),
+            "max_err_over_bound": float(ratio.max())}
+
+
+REPORT_MUTANTS = {"abs_tol_x10": _mut_report_abs_tol(10.0), "abs_tol_zero": _mut_report_abs_tol(0.0),
+                  "rel_tol_1e-2": _mut_report_rel_tol, "finite_check_dropped": _mut_report_no_finite,
+                  "signed_error": _mut_report_signed}
+
+
+@pytest.mark.parametrize("name", sorted(REPORT_MUTANTS))
+def test_attention_report_planted_mistakes_are_caught(monkeypatch, name):
+    assert _report_pins_ok()
+    monkeypatch.setattr(oatt, "parity_report", REPORT_MUTANTS[name])
+    try:
+        caught = not _report_pins_ok()
+    except Exception:
+        caught = True
+    assert caught, f"planted mistake {name} went unnoticed"

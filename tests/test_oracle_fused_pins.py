@@ -135,6 +135,78 @@ def test_swiglu_pairing_and_library():
     assert _swiglu_pins_ok()
 
 
+# The upper side of swiglu_bound: the bound must hold when the paired GEMV
+# outputs sit anywhere within their own tolerances (the propagation terms),
+# and it must not be loose - on inputs where one term dominates, the worst
+# achievable error comes within 15 % of it.
+def _bf16_of_f32(a32):
+    return oformats.bf16_to_f64(torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))
+                                .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def _act_f32(g, u):
+    """silu(g) * u evaluated in float32 and rounded once to bf16."""
+    g32 = np.asarray(g, dtype=np.float32)
+    u32 = np.asarray(u, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return _bf16_of_f32((g32 / (np.float32(1) + np.exp(-g32))) * u32)
+
+
+def _swiglu_bound_pins_ok() -> bool:
+    # hand-worked values. Gate 0, up 2, tolerances 0.01 / 0.02: silu(0) = 0, so
+    # the bound is 1.1 * 0.01 * (2 + 0.02) = 0.02222 times (1 + 2^-8 + 2^-20).
+    # Gate 1, up -3, tolerances 0 / 0.5: silu(1) = 1 / (1 + 1/e) = 0.73105857863,
+    # propagation 0.5 * 0.73105857863 = 0.36552928932, magnitude 3 * 0.73105857863
+    # + 0.36552928932 = 2.55870502521, bound 0.36552928932 + 2.55870502521 *
+    # (2^-8 + 2^-20) = 0.37552667099.
+    y = np.array([[0.0, 2.0, 1.0, -3.0]])
+    t = np.array([[0.01, 0.02, 0.0, 0.5]])
+    b = ofused.swiglu_bound(y, t)
+    if b.shape != (1, 2) or abs(b[0, 0] - 0.0223068180656) > 1e-12 or abs(b[0, 1] - 0.37552667099) > 1e-10:
+        return False
+    # containment: random outputs and tolerances, the pair moved to every corner
+    # of its tolerance box and to random interior points
+    rng = np.random.default_rng(11)
+    n = 20_000
+    g = rng.uniform(-8, 8, n)
+    u = rng.uniform(-8, 8, n)
+    tg = rng.uniform(0, 0.3, n) * rng.choice([0.0, 0.01, 1.0], n)
+    tu = rng.uniform(0, 0.3, n) * rng.choice([0.0, 0.01, 1.0], n)
+    yref = np.stack([g, u], axis=1).reshape(1, -1)
+    tol = np.stack([tg, tu], axis=1).reshape(1, -1)
+    bound = ofused.swiglu_bound(yref, tol)[0]
+    exact = ofused.swiglu_ref(yref)[0]
+    moves = [(sg, su) for sg in (-1.0, 1.0) for su in (-1.0, 1.0)]
+    moves += [tuple(rng.uniform(-1, 1, 2)) for _ in range(4)]
+    for sg, su in moves:
+        err = np.abs(_act_f32(g + sg * tg, u + su * tu) - exact)
+        if not (err <= bound).all():
+            return False
+    # tightness: each case is dominated by one term of the bound
+    #   gate at silu's steepest point (t ~ 2.4, slope 1.0998) moved by its tolerance,
+    #   up moved by its tolerance next to a large silu(gate),
+    #   zero tolerances (the bf16 rounding alone, at a value just below a midpoint)
+    cases = [(2.4, 10.0, 0.1, 0.0, +1, 0), (8.0, 0.0, 0.0, 1.0, 0, +1), (-8.0, 0.0, 0.0, 1.0, 0, -1)]
+    for gg, uu, tgg, tuu, sg, su in cases:
+        yy = np.array([[gg, uu]])
+        bb = ofused.swiglu_bound(yy, np.array([[tgg, tuu]]))[0, 0]
+        err = abs(_act_f32(gg + sg * tgg, uu + su * tuu)[0] - ofused.swiglu_ref(yy)[0, 0])
+        if not (0.85 * bb <= err <= bb):
+            return False
+    # the rounding term alone: an activation halfway up a bf16 interval
+    # (1 + 2^-8 - 2^-12) rounds down by nearly half a unit = 2^-8 relative
+    gg = 30.0                                   # silu(30) = 30 to float32 precision
+    uu = (1.0 + 2.0 ** -8 - 2.0 ** -12) / 30.0
+    yy = np.array([[gg, uu]])
+    bb = ofused.swiglu_bound(yy, np.zeros_like(yy))[0, 0]
+    err = abs(_act_f32(gg, uu)[0] - ofused.swiglu_ref(yy)[0, 0])
+    return bool(0.85 * bb <= err <= bb)
+
+
+def test_swiglu_bound_value_containment_and_tightness():
+    assert _swiglu_bound_pins_ok()
+
+
 def test_residual_bound_covers_one_float32_add():
     rng = np.random.default_rng(4)
     r = rng.standard_normal(100_000).astype(np.float32) * 30
@@ -186,6 +258,39 @@ def _mut_silu_sigmoid(t):
     return 1.0 / (1.0 + np.exp(-t))
 
 
+_orig_swiglu_bound = ofused.swiglu_bound
+
+
+def _mut_bound_times(k):
+    return lambda y, t: k * _orig_swiglu_bound(y, t)
+
+
+def _mut_bound_no_prop(y, t):
+    return _orig_swiglu_bound(y, np.zeros_like(np.asarray(y, dtype=np.float64)))
+
+
+def _mut_bound_no_up_term(y, t):
+    """The |silu(g)| * tol_u term dropped (only the gate's error propagated)."""
+    t = np.array(t, dtype=np.float64)
+    t[:, 1::2] = 0.0
+    return _orig_swiglu_bound(y, t)
+
+
+def _mut_bound_no_gate_term(y, t):
+    """The silu-slope * tol_g term dropped (only the up value's error propagated)."""
+    t = np.array(t, dtype=np.float64)
+    t[:, 0::2] = 0.0
+    return _orig_swiglu_bound(y, t)
+
+
+def _mut_bound_no_rounding(y, t):
+    """The final bf16 rounding left out of the bound."""
+    y = np.asarray(y, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    g, u = y[:, 0::2], y[:, 1::2]
+    return 1.1 * t[:, 0::2] * (np.abs(u) + t[:, 1::2]) + np.abs(ofused.silu(g)) * t[:, 1::2] + 1e-30
+
+
 FUSED_MUTANTS = {
     "rmsnorm_eps_dropped": [("rmsnorm_ref", _mut_rms_no_eps)],
     "rmsnorm_sum_not_mean": [("rmsnorm_ref", _mut_rms_sum)],
@@ -194,12 +299,19 @@ FUSED_MUTANTS = {
     "swiglu_gate_up_swapped": [("swiglu_ref", _mut_swiglu_swapped)],
     "swiglu_halves_not_pairs": [("swiglu_ref", _mut_swiglu_halves)],
     "silu_is_sigmoid": [("silu", _mut_silu_sigmoid)],
+    "swiglu_bound_x4": [("swiglu_bound", _mut_bound_times(4.0))],
+    "swiglu_bound_x8": [("swiglu_bound", _mut_bound_times(8.0))],
+    "swiglu_bound_prop_dropped": [("swiglu_bound", _mut_bound_no_prop)],
+    "swiglu_bound_up_term_dropped": [("swiglu_bound", _mut_bound_no_up_term)],
+    "swiglu_bound_gate_term_dropped": [("swiglu_bound", _mut_bound_no_gate_term)],
+    "swiglu_bound_rounding_dropped": [("swiglu_bound", _mut_bound_no_rounding)],
 }
 
 
 def _fused_pins_pass() -> bool:
     try:
-        return _bf16_pins_ok() and _rmsnorm_pins_ok() and _swiglu_pins_ok()
+        return (_bf16_pins_ok() and _rmsnorm_pins_ok() and _swiglu_pins_ok()
+                and _swiglu_bound_pins_ok())
     except Exception:
         return False
 

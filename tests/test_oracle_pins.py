@@ -375,3 +375,122 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     for mod, attr, repl in MUTANTS[name]:
         monkeypatch.setattr(mod, attr, repl)
     assert not _all_pins_pass(), f"planted mistake {name} went unnoticed"
+
+
+# ------------------------------------------- chunked rows and row subsets
+# gemv_ref walks the output rows in chunks of chunk_rows (1024 by default)
+# and can be asked for any subset of rows; every GPU parity test on a matrix
+# taller than one chunk goes through that slicing. These pins compare it,
+# row by row, with the exact rational brute force above on matrices taller
+# than one chunk and on scattered, unsorted, repeated row subsets.
+def _brute_rows(fmt, g, K, rows):
+    """Exact (y, a) as Fractions for the listed rows of a generated case."""
+    B = g.x.shape[0]
+    xs = [[_frac_bf16(g.x[b, k]) for k in range(K)] for b in range(B)]
+    ys, As = [], []
+    for m in rows:
+        wts = [_brute_weight(fmt, g.w, g.s, int(m), k, K) for k in range(K)]
+        ys.append([sum((wts[k] * xs[b][k] for k in range(K)), Fraction(0)) for b in range(B)])
+        As.append([sum((abs(wts[k] * xs[b][k]) for k in range(K)), Fraction(0)) for b in range(B)])
+    return ys, As
+
+
+def _rows_agree(y, a, ys, As, K) -> bool:
+    for i, (yr, ar) in enumerate(zip(ys, As)):
+        for b in range(len(yr)):
+            tol = Fraction(K) * Fraction(2) ** -52 * ar[b]
+            if abs(Fraction(float(y[b, i])) - yr[b]) > tol or abs(Fraction(float(a[b, i])) - ar[b]) > tol:
+                return False
+    return True
+
+
+def _chunk_pins_ok() -> bool:
+    # 2100 rows: two full 1024-row chunks and a 52-row tail; every row checked
+    for fmt, K in ((synth.Q4_0_G32, 32), (synth.INT8_G32, 32)):
+        M = 2100
+        g = synth.make_gemv("t", fmt, M, K, 2, cfg=9, layer=40 + fmt, proj="o")
+        y, a = oracle.gemv_ref(fmt, g.w, g.s, g.x, M, K)
+        if y.shape != (2, M) or not _rows_agree(y, a, *_brute_rows(fmt, g, K, range(M)), K):
+            return False
+    # small chunks with a ragged last chunk, and a scattered, unsorted row
+    # subset with repeats that crosses chunk boundaries
+    rng = np.random.default_rng(41)
+    for fmt, K, M in ((synth.INT4_G128, 128, 50), (synth.INT8_ROW, 64, 50), (synth.BF16, 32, 50)):
+        g = synth.make_gemv("t", fmt, M, K, 2, cfg=9, layer=50 + fmt, proj="o")
+        y, a = oracle.gemv_ref(fmt, g.w, g.s, g.x, M, K, chunk_rows=7)
+        if not _rows_agree(y, a, *_brute_rows(fmt, g, K, range(M)), K):
+            return False
+        rows = np.concatenate([rng.permutation(M)[:23], [0, M - 1, 7, 7]])
+        y, a = oracle.gemv_ref(fmt, g.w, g.s, g.x, M, K, rows=rows, chunk_rows=5)
+        if y.shape != (2, rows.size) or not _rows_agree(y, a, *_brute_rows(fmt, g, K, rows), K):
+            return False
+    # the chunking changes nothing: one chunk and many chunks give equal bits
+    g = synth.make_gemv("t", synth.Q4_0_G32, 300, 256, 3, cfg=9, layer=60, proj="o")
+    y1, a1 = oracle.gemv_ref(synth.Q4_0_G32, g.w, g.s, g.x, 300, 256, chunk_rows=300)
+    y2, a2 = oracle.gemv_ref(synth.Q4_0_G32, g.w, g.s, g.x, 300, 256, chunk_rows=13)
+    return bool((y1 == y2).all() and (a1 == a2).all())
+
+
+def test_chunked_rows_and_row_subsets_brute_force():
+    assert _chunk_pins_ok()
+
+
+_orig_row_slice = ogemv._row_slice
+
+
+def _mut_chunk_off_by_one(fmt, w, s, x_bits, M, K, rows=None, chunk_rows=1024):
+    """Chunks that step one row too far: the first row of every later chunk
+    is never computed (and the tail reads one row short)."""
+    x = oformats.bf16_to_f64(np.asarray(x_bits).reshape(-1, K))
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.zeros((x.shape[0], rows.size)); a = np.zeros_like(y)
+    for c0 in range(0, rows.size, chunk_rows + 1):
+        r = rows[c0:c0 + chunk_rows]
+        wr, sr = _orig_row_slice(fmt, w, s, M, K, r)
+        Wh = oformats.dequantize(fmt, wr, sr, K)
+        y[:, c0:c0 + r.size] = (Wh @ x.T).T
+        a[:, c0:c0 + r.size] = (np.abs(Wh) @ np.abs(x).T).T
+    return y, a
+
+
+def _mut_scales_chunk_relative(fmt, w, s, M, K, rows):
+    """Scale rows indexed relative to the chunk instead of the matrix."""
+    wr, _ = _orig_row_slice(fmt, w, s, M, K, rows)
+    if s is None:
+        return wr, None
+    sr = np.asarray(s).reshape(M, -1)[np.asarray(rows) - np.asarray(rows).min()]
+    return wr, sr
+
+
+def _mut_scales_sorted_rows(fmt, w, s, M, K, rows):
+    """Scale rows taken in sorted order while the codes keep the requested order."""
+    wr, _ = _orig_row_slice(fmt, w, s, M, K, rows)
+    if s is None:
+        return wr, None
+    return wr, np.asarray(s).reshape(M, -1)[np.sort(np.asarray(rows))]
+
+
+def _mut_rows_ignored(fmt, w, s, x_bits, M, K, rows=None, chunk_rows=1024):
+    """A subset request answered with the first len(rows) rows."""
+    n = M if rows is None else len(rows)
+    return _orig_gemv(fmt, w, s, x_bits, M, K, None if rows is None else np.arange(n), chunk_rows)
+
+
+CHUNK_MUTANTS = {
+    "chunk_step_off_by_one": [(oracle, "gemv_ref", _mut_chunk_off_by_one)],
+    "scale_rows_chunk_relative": [(ogemv, "_row_slice", _mut_scales_chunk_relative)],
+    "scale_rows_sorted": [(ogemv, "_row_slice", _mut_scales_sorted_rows)],
+    "row_subset_ignored": [(oracle, "gemv_ref", _mut_rows_ignored)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_MUTANTS))
+def test_chunk_planted_mistakes_are_caught(monkeypatch, name):
+    assert _chunk_pins_ok()
+    for mod, attr, repl in CHUNK_MUTANTS[name]:
+        monkeypatch.setattr(mod, attr, repl)
+    try:
+        caught = not _chunk_pins_ok()
+    except Exception:
+        caught = True
+    assert caught, f"planted mistake {name} went unnoticed"
