@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "qgemv_run_grouped_argmax": (c_int, [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
         "qgemv_grouped_class": (c_int, [c_int, c_i64, c_int]),
         "qgemv_argmax": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp]),
+        "qgemv_argmax_noalloc": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp]),
         "qgemv_stream_read": (c_int, [c_vp, c_sz, c_vp, c_int, c_int, c_vp]),
         "qgemv_status_str": (ctypes.c_char_p, [c_int]),
         "qgemv_last_hip_error": (c_int, []),
@@ -82,7 +83,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTS = ("qgemv_packed_size", "qgemv_pack", "qgemv_quantize", "qgemv_run", "qgemv_run_flags",
            "qgemv_run_fused", "qgemv_run_grouped", "qgemv_attention_workspace_size", "qgemv_attention_decode",
-           "qgemv_run_grouped_argmax", "qgemv_grouped_class", "qgemv_argmax", "qgemv_stream_read",
+           "qgemv_run_grouped_argmax", "qgemv_grouped_class", "qgemv_argmax", "qgemv_argmax_noalloc",
+           "qgemv_stream_read",
            "qgemv_status_str", "qgemv_last_hip_error", "qgemv_version")
 
 
@@ -362,6 +364,15 @@ def argmax(logits, V: int, batch: int, ws, idx, stream=None) -> None:
         raise ValueError("ws too small")
     st = _lib.qgemv_argmax(lp, V, batch, wsp, ip, _stream_handle(stream))
     _check(st, "qgemv_argmax")
+
+
+def argmax_noalloc(logits, V: int, batch: int, idx, stream=None) -> None:
+    """qgemv_argmax with the library's static per-device workspace (see qgemv.h)."""
+    import torch
+    lp = _dev_ptr(logits, "logits", torch.float32)
+    ip = _dev_ptr(idx, "idx", torch.int32)
+    st = _lib.qgemv_argmax_noalloc(lp, V, batch, ip, _stream_handle(stream))
+    _check(st, "qgemv_argmax_noalloc")
 
 
 def argmax_workspace(batch: int, device="cuda"):

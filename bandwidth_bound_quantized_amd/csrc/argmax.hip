@@ -13,6 +13,8 @@
 //
 // Order of values (argmax_key.h): NaN above everything (every NaN equal, so
 // the first NaN wins), then the IEEE order with -0.0 == +0.0.
+#include <mutex>
+
 #include "argmax_key.h"
 #include "qgemv_internal.h"
 #include "qgemv.h"
@@ -147,6 +149,61 @@ hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws
   else
     argmax_kernel<false><<<grid, kThreads, 0, stream>>>(logits, V, static_cast<int>(slices), ws, idx);
   return hipGetLastError();
+}
+
+// ------------------------------------------------- argmax without allocation
+// The workspace of launch_argmax_noalloc: one copy per GPU for the life of the
+// process (a code-object global). In host code `scratch` names a host-side
+// stand-in, not device memory: the kernels get the device address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+constexpr int kScratchWords = QGEMV_ARGMAX_NOALLOC_MAX_BATCH * QGEMV_ARGMAX_WS_WORDS_PER_ROW;
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint64_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+// The current device's copy of `scratch`. The first call on a device looks up
+// its address and clears it with a kernel on `stream` (ahead of the caller's
+// argmax in stream order; a kernel rather than a memset so that a first call
+// made under graph capture records an ordinary kernel node).
+hipError_t device_scratch(hipStream_t stream, uint64_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    uint64_t* ptr = nullptr;
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    zero_words_kernel<<<1, 64, 0, stream>>>(ptr, kScratchWords);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx,
+                                 hipStream_t stream) {
+  if (batch < 1 || batch > QGEMV_ARGMAX_NOALLOC_MAX_BATCH) return hipErrorInvalidValue;
+  uint64_t* ws = nullptr;
+  const hipError_t e = device_scratch(stream, &ws);
+  if (e != hipSuccess) return e;
+  // the kernel leaves every word it uses zero again (the last slice of a row
+  // resets the row's two words), so the scratch is zero at every call's start
+  return launch_argmax(logits, V, batch, ws, idx, stream);
 }
 
 }  // namespace qgemv

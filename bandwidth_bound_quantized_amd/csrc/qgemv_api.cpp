@@ -479,6 +479,13 @@ int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_
   return record_hip(qgemv::launch_argmax(logits, V, batch, ws, idx, static_cast<hipStream_t>(stream)));
 }
 
+int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx, void* stream) {
+  if (!logits || !idx) return QGEMV_EINVAL;
+  if (V < 1 || V > 0x7FFFFFFF || batch < 1 || batch > QGEMV_ARGMAX_NOALLOC_MAX_BATCH) return QGEMV_ESHAPE;
+  if (!aligned(logits, 4) || !aligned(idx, 4)) return QGEMV_EALIGN;
+  return record_hip(qgemv::launch_argmax_noalloc(logits, V, batch, idx, static_cast<hipStream_t>(stream)));
+}
+
 int qgemv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll,
                       void* stream) {
   if (!buf || !sink) return QGEMV_EINVAL;

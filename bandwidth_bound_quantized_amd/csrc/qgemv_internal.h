@@ -94,6 +94,11 @@ hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream);
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                          hipStream_t stream);
 
+// The argmax with its workspace in the library's per-device static scratch
+// (qgemv_argmax_noalloc); batch <= QGEMV_ARGMAX_NOALLOC_MAX_BATCH.
+hipError_t launch_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx,
+                                 hipStream_t stream);
+
 // Quantizer (bf16 -> codes + scales) on the device; err may be null.
 hipError_t launch_quantize(int fmt, const uint16_t* w, int64_t M, int64_t K, void* codes, uint16_t* scales,
                            int32_t* err, hipStream_t stream);

@@ -43,7 +43,9 @@
  *     exceptions or aborts, as in the Mini Inference Engine page's block
  *     pool, whose out-of-memory result is a sentinel);
  *   - the library never allocates device memory, never frees, never keeps a
- *     caller pointer past the call and never synchronizes a stream;
+ *     caller pointer past the call and never synchronizes a stream; its only
+ *     device state is qgemv_argmax_noalloc's static workspace (128 bytes per
+ *     GPU, part of the loaded code object);
  *   - the caller owns every buffer; device entry points run asynchronously
  *     on the caller's stream (hipStream_t passed as void*, NULL = the null
  *     stream); reading W and scales from several streams at once is safe;
@@ -250,6 +252,31 @@ int qgemv_grouped_class(int fmt, int64_t K, int batch);
  */
 int qgemv_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,
                  void* stream);
+
+/* Largest batch qgemv_argmax_noalloc accepts (the rows its static scratch holds). */
+#define QGEMV_ARGMAX_NOALLOC_MAX_BATCH 8
+
+/*
+ * qgemv_argmax_noalloc - qgemv_argmax for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernel, semantics and results,
+ * with the workspace taken from a static array inside the library instead of
+ * a caller buffer. The array holds QGEMV_ARGMAX_NOALLOC_MAX_BATCH rows of
+ * QGEMV_ARGMAX_WS_WORDS_PER_ROW u64 words (128 bytes); each GPU the library
+ * runs on keeps its own copy until the process ends. The first call on a
+ * device (the current device, which must own `stream`) looks the array up
+ * and clears it with a small kernel on `stream` ahead of the argmax; every
+ * call leaves it zero again. Device pointers: logits float32 [batch][V]
+ * (4-byte aligned), idx int32 [batch] (4-byte aligned).
+ * 1 <= batch <= QGEMV_ARGMAX_NOALLOC_MAX_BATCH (else ESHAPE, nothing
+ * launched), 1 <= V <= 2^31 - 1. No hipMalloc, hipFree or other allocation.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (concurrent streams, or host threads driving one device) race and
+ * can return wrong indices; serialize them, or use qgemv_argmax with a
+ * workspace per stream. Asynchronous on `stream`.
+ * Errors: EINVAL (null pointer), ESHAPE, EALIGN, EHIP.
+ */
+int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx, void* stream);
 
 /* u64 words of workspace qgemv_run_grouped_argmax needs per batch row */
 #define QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW 4096

@@ -265,6 +265,14 @@ def test_argmax_and_stream_read_validation():
     assert L.qgemv_argmax(FAKE, 10, 9, FAKE, FAKE, None) == qg.ESHAPE
     assert L.qgemv_argmax(FAKE + 2, 10, 1, FAKE, FAKE, None) == qg.EALIGN
     assert L.qgemv_argmax(FAKE, 10, 1, FAKE + 4, FAKE, None) == qg.EALIGN
+    # the no-allocation argmax rejects a batch beyond its static workspace before any HIP call
+    assert L.qgemv_argmax_noalloc(None, 10, 1, FAKE, None) == qg.EINVAL
+    assert L.qgemv_argmax_noalloc(FAKE, 10, 1, None, None) == qg.EINVAL
+    assert L.qgemv_argmax_noalloc(FAKE, 0, 1, FAKE, None) == qg.ESHAPE
+    assert L.qgemv_argmax_noalloc(FAKE, 10, 0, FAKE, None) == qg.ESHAPE
+    assert L.qgemv_argmax_noalloc(FAKE, 10, 9, FAKE, None) == qg.ESHAPE
+    assert L.qgemv_argmax_noalloc(FAKE + 2, 10, 1, FAKE, None) == qg.EALIGN
+    assert L.qgemv_argmax_noalloc(FAKE, 10, 1, FAKE + 1, None) == qg.EALIGN
     assert L.qgemv_stream_read(FAKE, 0, FAKE, 0, 4, None) == qg.ESHAPE
     assert L.qgemv_stream_read(FAKE, 24, FAKE, 0, 4, None) == qg.ESHAPE
     assert L.qgemv_stream_read(FAKE, 32, FAKE, 0, 3, None) == qg.EINVAL
