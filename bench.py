@@ -1,26 +1,40 @@
 """Bench: fused-dequant decode GEMV throughput on one MI355X (gfx950).
 
-One "step" is one pass of the whole hot path over one batch: every GEMV of
-the workload (qgemv_run) and, where the workload ends in an LM head, the
-argmax of its logits (qgemv_argmax). The default workload is the Q4_0-g32
-GEMV set at TinyLlama-1.1B decode shapes (qkv 2560x2048, o 2048x2048,
-gate_up 11264x2048, down 2048x5632, lm_head 32000x2048) at batch 1, plus
-the argmax over the 32000 logits.
+The headline ("step") is the Q4_0-g32 GEMV set at TinyLlama-1.1B decode
+shapes (qkv 2560x2048, o 2048x2048, gate_up 11264x2048, down 2048x5632,
+lm_head 32000x2048) at batch 1 plus the argmax over the 32000 logits, run as
+one qgemv_run_grouped_argmax call. Beside it, the default run measures every
+workload the metric names:
+  1  bf16 GEMV 2048x2048, batch 1
+  2  the headline set at batch 1 (and at batch 8: the matrix-core path)
+  3  int8-g32 GEMV set at Llama-3.2-1B shapes, batch 1
+  4  the TinyLlama decode-step weight stream (22 layers x 4 GEMVs + LM head
+     + argmax) at batch 1, 2, 4, 8
+  5  int4-g128 FFN + int8-g32 LM head 128256x2048 + argmax, batch 1 and 8
+each GEMV of workloads 1-3 also alone, every figure next to the streaming-read
+kernel over the same number of bytes (the size-matched ceiling: what one
+launch of that size can reach on this GPU) and the measured peak over 4 GiB.
 
 Inputs are synthetic and seeded (synth), resident in HBM before timing, and
 rotated through >= 1 GiB of distinct device copies so that the 256 MB
-Infinity Cache cannot serve them. The timed steps are captured once in a
-HIP graph (the decode step of the infer page is a CUDA graph too) and
-replayed; events on the launch stream bracket exactly --steps steps.
+Infinity Cache cannot serve them. Every figure is timed the same way: a HIP
+graph of N calls rotating through the copies is captured once, replayed once
+untimed, then replayed in `--trials` trials, each bracketed by events on the
+launch stream; a trial's time / N is one sample, and the figure is the
+median sample with the 10th and 90th percentiles. The headline's graph holds
+exactly --steps steps (after a graph of --warmup steps).
 
 Reported (one JSON line):
-  value            algorithmic bytes per step / time per step (GB/s)
-  roofline         dominant kernel (largest bytes per launch): its bytes per
-                   launch / its average launch duration, against 8 TB/s
-  measured_peak    best rate of the streaming-read kernel over 4 GiB
-  cpu_baseline     the fp64 CPU oracle on one step, one thread
+  value            algorithmic bytes per step / median time per step (GB/s)
+  value_sequential the same GEMVs as a dependent chain: one launch per GEMV,
+                   then the argmax launch
+  roofline         the dominant kernel (the headline step is one launch)
+  configs          per workload: us, GB/s, % of the measured peak, % of the
+                   8 TB/s spec, and the size-matched ceiling
+  measured_peak    best median rate of the streaming-read kernel over 4 GiB
+  cpu_baseline     the fp64 CPU oracle on whole steps, all cores and one thread
 Algorithmic bytes per GEMV = code bytes + scale bytes + x (2*B*K) + y (4*B*M);
-argmax = 4*B*V read + 4*B written.
+a separate argmax = 4*B*V read + 4*B written; a fused argmax = 4*B written.
 """
 from __future__ import annotations
 
@@ -28,6 +42,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -41,6 +56,10 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+WORKLOAD_KEYS = {1: "bf16_gemv_2048x2048", 2: "q4_0_g32_tinyllama_gemv_set+argmax",
+                 3: "int8_g32_llama32_1b_gemv_set", 4: "q4_0_g32_tinyllama_decode_step_89_gemvs+argmax",
+                 5: "int4_g128_ffn+int8_g32_lm_head+argmax",
+                 6: "q4_0_g32_llama32_1b_layer_gemvs+int8_row_lm_head+argmax"}
 
 
 def recorded_traffic(kernel_label, workload_name, batch):
@@ -64,21 +83,21 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    p.add_argument("--trials", type=int, default=11, help="timed replays per figure (median, p10, p90)")
+    p.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6],
+                   help="time only this workload's step (focused run, e.g. under a profiler)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-peak", action="store_true")
     p.add_argument("--peak-gib", type=float, default=4.0)
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--per-kernel", action="store_true", help="also time every GEMV of the step alone")
-    p.add_argument("--no-attention", action="store_true",
-                   help="skip the decode-attention measurements (workload 2)")
-    p.add_argument("--no-fused-layer", action="store_true",
-                   help="skip the fused decode-layer chain (workload 2)")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU leg")
+    p.add_argument("--per-kernel", action="store_true", help="focused run: also time every GEMV alone")
+    p.add_argument("--no-attention", action="store_true", help="skip the decode-attention measurements")
+    p.add_argument("--no-fused-layer", action="store_true", help="skip the fused decode-layer chain")
     p.add_argument("--pmc-pass", action="store_true",
                    help="only run calibration kernels (a 64 MiB streaming read, a 64 MiB fill) and "
-                        "--steps eager steps, for hardware-counter collection")
+                        "--steps eager steps of --workload, for hardware-counter collection")
     p.add_argument("--size-sweep", action="store_true",
                    help="only time the streaming-read kernel at GEMV-like sizes (size-matched ceilings)")
     return p.parse_args()
@@ -89,56 +108,113 @@ def gemv_bytes(qg, fmt, M, K, B):
     return w + s + 2 * B * K + 4 * B * M
 
 
-class Workload:
-    """Device-resident inputs for one workload, replicated n_sets times."""
+def stats(samples):
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
 
-    def __init__(self, qg, torch, cfg, B, rotate_bytes):
+
+def capture(torch, fn, count):
+    """Capture fn(i, stream) for i in range(count) into one graph on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0, s.cuda_stream)          # eager warm call (loads code objects)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(count):
+            fn(i, h)
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_ms(torch, g):
+    """One timed replay of g (events on the stream the graph is launched on)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def time_calls(torch, fn, count, trials):
+    """Median / p10 / p90 over `trials` replays of a graph of `count` calls, in us per call."""
+    g = capture(torch, fn, count)
+    replay_ms(torch, g)
+    samples = [replay_ms(torch, g) * 1e3 / count for _ in range(trials)]
+    del g
+    return stats(samples)
+
+
+def rate(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
+# ------------------------------------------------------------------ inputs
+class Weights:
+    """Device copies of a workload's codes and scales, n_sets distinct copies."""
+
+    def __init__(self, torch, gemvs, rotate_bytes):
+        self.gemvs = gemvs
+        resident = sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0) for g in gemvs)
+        self.resident = resident
+        self.n_sets = max(1, math.ceil(rotate_bytes / resident))
+        base = []
+        for g in gemvs:
+            W = torch.from_numpy(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8)).to("cuda")
+            S = torch.from_numpy(g.s.reshape(-1).view(np.int16)).to("cuda") if g.s is not None else None
+            base.append((W, S))
+        self.sets = [base] + [[(W.clone(), None if S is None else S.clone()) for W, S in base]
+                              for _ in range(self.n_sets - 1)]
+        torch.cuda.synchronize()
+
+
+class Workload:
+    """One workload at one batch: device weights (shared across batches), x, y,
+    argmax buffers per rotation set, and the call descriptors."""
+
+    def __init__(self, qg, torch, cfg, B, weights: Weights):
         self.qg, self.torch, self.cfg, self.B = qg, torch, cfg, B
-        self.gemvs = synth.make_workload(cfg, B)
+        self.gemvs = weights.gemvs
+        self.n_sets = weights.n_sets
         self.has_argmax = synth.WORKLOAD_ARGMAX[cfg]
         self.bytes = [gemv_bytes(qg, g.fmt, g.M, g.K, B) for g in self.gemvs]
         self.argmax_bytes = 4 * B * self.gemvs[-1].M + 4 * B if self.has_argmax else 0
         self.step_bytes = sum(self.bytes) + self.argmax_bytes
         # with the argmax inside the LM head's launch the logits are not read again
         self.fused_bytes = sum(self.bytes) + (4 * B if self.has_argmax else 0)
-        resident = sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0) for g in self.gemvs)
-        self.n_sets = max(1, math.ceil(rotate_bytes / resident))
+        self.resident = weights.resident
         dev = "cuda"
+        xs = [torch.from_numpy(np.ascontiguousarray(g.x[:B]).view(np.int16)).to(dev) for g in self.gemvs]
         self.sets = []
-        base = []
-        for g in self.gemvs:
-            W = torch.from_numpy(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8)).to(dev)
-            S = torch.from_numpy(g.s.reshape(-1).view(np.int16)).to(dev) if g.s is not None else None
-            X = torch.from_numpy(g.x.view(np.int16)).to(dev)
-            base.append((W, S, X))
         for i in range(self.n_sets):
             items = []
-            for (W, S, X), g in zip(base, self.gemvs):
-                Wi = W if i == 0 else W.clone()
-                Si = None if S is None else (S if i == 0 else S.clone())
+            for (W, S), X, g in zip(weights.sets[i], xs, self.gemvs):
                 Xi = X if i == 0 else X.clone()
                 Y = torch.empty((B, g.M), dtype=torch.float32, device=dev)
-                items.append((Wi, Si, Xi, Y))
+                items.append((W, S, Xi, Y))
             ws = qg.fused_argmax_workspace(B) if self.has_argmax else None
             idx = torch.empty(B, dtype=torch.int32, device=dev) if self.has_argmax else None
             self.sets.append((items, ws, idx))
         torch.cuda.synchronize()
-        # per set: descriptors for one grouped call, and per launch class
+        # launch classes of qgemv_run_grouped: one small-batch launch per format,
+        # one matrix-core launch per format and K, one launch each for the others
         self.classes = {}
         for j, g in enumerate(self.gemvs):
-            # qgemv_run_grouped: one small-batch launch per format, one
-            # matrix-core launch per format and K, one launch each for the others
             cls = qg.grouped_class(g.fmt, g.K, B)
             key = ((g.fmt, "grouped") if cls == qg.GROUP_XREG else
                    (g.fmt, g.K, "mfma") if cls == qg.GROUP_MFMA else ("alone", j))
             self.classes.setdefault(key, []).append(j)
         self.descs = []
-        self.class_descs = []
         for items, _, _ in self.sets:
             ent = [(g.fmt, W, S, X, Y, g.M, g.K) for (W, S, X, Y), g in zip(items, self.gemvs)]
             self.descs.append(qg.grouped_descs(ent))
-            self.class_descs.append({k: qg.grouped_descs([ent[j] for j in js])
-                                     for k, js in self.classes.items()})
         # raw pointers for the launch loop (argument marshalling only)
         self.ptrs = []
         for items, ws, idx in self.sets:
@@ -148,6 +224,8 @@ class Workload:
                               idx.data_ptr() if idx is not None else None))
 
     def step(self, i, stream_handle):
+        """One qgemv_run launch per GEMV (as a chain of dependent GEMVs must run), then
+        the argmax launch."""
         qg = self.qg
         p, wsp, ip = self.ptrs[i % self.n_sets]
         for (wp, sp, xp, yp), g in zip(p, self.gemvs):
@@ -158,7 +236,7 @@ class Workload:
                 raise qg.QgemvError(st, "qgemv_argmax")
 
     def step_grouped(self, i, stream_handle):
-        """All GEMVs of the step in one qgemv_run_grouped call, then the argmax."""
+        """All GEMVs in one qgemv_run_grouped call, then the argmax launch."""
         qg = self.qg
         p, wsp, ip = self.ptrs[i % self.n_sets]
         qg.run_grouped_ptr(self.descs[i % self.n_sets], self.B, stream_handle)
@@ -168,37 +246,24 @@ class Workload:
                 raise qg.QgemvError(st, "qgemv_argmax")
 
     def step_fused(self, i, stream_handle):
-        """The step's GEMVs and the LM-head argmax in one qgemv_run_grouped_argmax call
-        (the argmax runs inside the LM head's launch where the small-batch kernel takes it)."""
-        qg = self.qg
+        """The GEMVs and the LM-head argmax in one qgemv_run_grouped_argmax call."""
         p, wsp, ip = self.ptrs[i % self.n_sets]
-        qg.run_grouped_argmax_ptr(self.descs[i % self.n_sets], self.B, len(self.gemvs) - 1, wsp, ip,
-                                  stream_handle)
+        self.qg.run_grouped_argmax_ptr(self.descs[i % self.n_sets], self.B, len(self.gemvs) - 1, wsp, ip,
+                                       stream_handle)
 
-    def launch_class(self, key, i, stream_handle):
-        """One launch class as the step runs it: with the LM-head argmax fused in if the
-        class holds the LM head."""
-        am = len(self.gemvs) - 1
-        descs = self.class_descs[i % self.n_sets][key]
-        if self.has_argmax and am in self.classes[key]:
-            p, wsp, ip = self.ptrs[i % self.n_sets]
-            self.qg.run_grouped_argmax_ptr(descs, self.B, self.classes[key].index(am), wsp, ip,
-                                           stream_handle)
-        else:
-            self.qg.run_grouped_ptr(descs, self.B, stream_handle)
-
-    def class_bytes(self, key):
-        return sum(self.bytes[j] for j in self.classes[key])
-
-    def class_label(self, key):
-        names = "+".join(self.gemvs[j].name for j in self.classes[key][:6])
-        more = f"+{len(self.classes[key]) - 6} more" if len(self.classes[key]) > 6 else ""
-        return f"{names}{more}"
+    def best_step(self):
+        """The call a decode step of independent GEMVs uses, and its bytes."""
+        if self.has_argmax:
+            return self.step_fused, self.fused_bytes
+        return self.step_grouped, self.step_bytes
 
     def launch_one(self, j, i, stream_handle):
         g = self.gemvs[j]
         wp, sp, xp, yp = self.ptrs[i % self.n_sets][0][j]
         self.qg.run_ptr(g.fmt, wp, sp, xp, yp, g.M, g.K, self.B, stream_handle)
+
+    def launch_count(self, k=4, lo=64):
+        return max(self.n_sets * k, lo)
 
 
 class FusedLayer:
@@ -268,53 +333,64 @@ class FusedLayer:
             self.op(k, i, stream_handle)
 
 
-def capture(torch, fn, count):
-    """Capture fn(i) for i in range(count) into one graph on a side stream."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn(0, s.cuda_stream)          # eager warm call (loads code objects)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        h = torch.cuda.current_stream().cuda_stream
-        for i in range(count):
-            fn(i, h)
-    torch.cuda.synchronize()
-    return g
+# -------------------------------------------------------- streaming reads
+class StreamCeiling:
+    """The streaming-read kernel over n bytes, rotated through >= rotate_bytes of
+    distinct buffers: the size-matched ceiling of a launch that moves n bytes.
+    Best median over a small grid x loads-in-flight sweep; one pool, reused."""
+
+    def __init__(self, qg, torch, rotate_bytes, trials):
+        self.qg, self.torch, self.trials = qg, torch, trials
+        self.rotate_bytes = int(rotate_bytes)
+        self.cus = torch.cuda.get_device_properties(0).multi_processor_count
+        self.pool = torch.full((self.rotate_bytes // 4 + (1 << 20),), 3, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(64 * self.cus, dtype=torch.int32, device="cuda")
+        self.cache = {}
+
+    def __call__(self, nbytes):
+        nbytes = max(4096, int(nbytes) // 4096 * 4096)
+        if nbytes in self.cache:
+            return self.cache[nbytes]
+        qg, torch = self.qg, self.torch
+        n = max(2, min(512, self.rotate_bytes // nbytes))
+        if n * nbytes > self.pool.numel() * 4:
+            n = max(1, self.pool.numel() * 4 // nbytes)
+        base = self.pool.data_ptr()
+        best = None
+        for grid in (2 * self.cus, 4 * self.cus, 8 * self.cus):
+            for unroll in (1, 2, 4):
+                def fn(i, h, grid=grid, unroll=unroll):
+                    st = qg.lib().qgemv_stream_read(base + (i % n) * nbytes, nbytes, self.sink.data_ptr(),
+                                                    grid, unroll, h)
+                    if st != qg.OK:
+                        raise qg.QgemvError(st, "qgemv_stream_read")
+                s = time_calls(torch, fn, max(2 * n, 32), self.trials)
+                if best is None or s["median"] < best[0]["median"]:
+                    best = (s, grid, unroll)
+        s, grid, unroll = best
+        out = {"us": round(s["median"], 3), "GBps": round(rate(nbytes, s["median"]), 1), "bytes": nbytes,
+               "grid": grid, "unroll": unroll}
+        self.cache[nbytes] = out
+        return out
 
 
-def time_graph(torch, g, reps=1):
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
-
-
-def measure_peak(qg, torch, gib):
-    """Best streaming-read rate over a gib-GiB buffer, sweeping grid and loads in flight."""
+def measure_peak(qg, torch, gib, trials):
+    """Best median streaming-read rate over a gib-GiB buffer, sweeping grid and loads in flight."""
     nbytes = int(gib * (1 << 30)) // 16 * 16
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(1)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
     best = (0.0, None)
-    sweep = []
+    h = torch.cuda.current_stream().cuda_stream
     for grid_per_cu in (4, 8, 16, 32):
         for unroll in (2, 4, 8, 16):
             grid = grid_per_cu * cus
-            h = torch.cuda.current_stream().cuda_stream
             qg.stream_read(buf, nbytes, sink, grid=grid, unroll=unroll)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             times = []
-            for _ in range(5):
+            for _ in range(trials):
                 e0.record()
                 qg.lib().qgemv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, h)
                 e1.record()
@@ -322,48 +398,21 @@ def measure_peak(qg, torch, gib):
                 times.append(e0.elapsed_time(e1))
             ms = float(np.median(times))
             gbps = nbytes / (ms * 1e-3) / 1e9
-            sweep.append({"grid": grid, "unroll": unroll, "GBps": round(gbps, 1)})
             if gbps > best[0]:
-                best = (gbps, {"grid": grid, "unroll": unroll, "ms": ms})
+                best = (gbps, {"grid": grid, "unroll": unroll, "ms": round(ms, 4),
+                               "p10_GBps": round(nbytes / (np.percentile(times, 90) * 1e-3) / 1e9, 1),
+                               "p90_GBps": round(nbytes / (np.percentile(times, 10) * 1e-3) / 1e9, 1)})
     del buf
     torch.cuda.empty_cache()
-    return best[0], best[1], sweep
+    return best[0], best[1]
 
 
-def size_sweep(qg, torch, rotate_bytes):
-    """Streaming-read kernel at small sizes, rotated through >= rotate_bytes of distinct
-    buffers: the size-matched ceiling a kernel of that many bytes can reach."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    out = []
+def size_sweep(qg, torch, rotate_bytes, trials):
+    ceil = StreamCeiling(qg, torch, rotate_bytes, trials)
     for mb in (1, 2, 2.36, 4, 8, 13, 16, 32, 37, 64, 128, 256):
-        nbytes = int(mb * (1 << 20)) // 4096 * 4096
-        n = max(4, math.ceil(rotate_bytes / nbytes))
-        pool = torch.empty(n * nbytes // 4, dtype=torch.int32, device="cuda")
-        pool.fill_(3)
-        sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
-        best = None
-        for grid in (cus, 2 * cus, 4 * cus, 8 * cus):
-            for unroll in (1, 2, 4):
-                base = pool.data_ptr()
-
-                def fn(i, h, grid=grid, unroll=unroll):
-                    st = qg.lib().qgemv_stream_read(base + (i % n) * nbytes, nbytes, sink.data_ptr(),
-                                                    grid, unroll, h)
-                    if st != qg.OK:
-                        raise qg.QgemvError(st, "qgemv_stream_read")
-                g = capture(torch, fn, n)
-                time_graph(torch, g)
-                us = time_graph(torch, g, reps=3) * 1e3 / n
-                if best is None or us < best[0]:
-                    best = (us, grid, unroll)
-                del g
-        us, grid, unroll = best
-        out.append({"MiB": mb, "bytes": nbytes, "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
-                    "grid": grid, "unroll": unroll, "rotation": n})
-        print(json.dumps(out[-1]), flush=True)
-        del pool
-        torch.cuda.empty_cache()
-    return out
+        r = ceil(int(mb * (1 << 20)))
+        r["MiB"] = mb
+        print(json.dumps(r), flush=True)
 
 
 def pmc_pass(qg, torch, wl, steps):
@@ -377,14 +426,15 @@ def pmc_pass(qg, torch, wl, steps):
     buf.fill_(3)                                                   # writes exactly 64 MiB
     torch.cuda.synchronize()
     h = torch.cuda.current_stream().cuda_stream
+    fn, _ = wl.best_step()
     for i in range(steps):
-        (wl.step_fused if wl.has_argmax else wl.step_grouped)(i, h)
+        fn(i, h)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_pass": True, "calib_bytes": nbytes, "steps": steps,
                       "gemvs": [[g.name, g.M, g.K, b] for g, b in zip(wl.gemvs, wl.bytes)]}), flush=True)
 
 
-def attention_bench(qg, torch, rotate_bytes):
+def attention_bench(qg, torch, rotate_bytes, trials):
     """Grouped-query decode attention at Llama-3.2-1B's heads (32 query, 8 key/value,
     head dim 64): the infer page's contexts 512 and 2048 at batch 1, longer contexts,
     and batch 8. Each configuration rotates through >= rotate_bytes of distinct caches;
@@ -411,37 +461,125 @@ def attention_bench(qg, torch, rotate_bytes):
                                                  ws.data_ptr(), h)
             if st != qg.OK:
                 raise qg.QgemvError(st, "qgemv_attention_decode")
-        count = max(n * 2, 64)
-        g = capture(torch, fn, count)
-        time_graph(torch, g)
-        us = time_graph(torch, g, reps=3) * 1e3 / count
+        s = time_calls(torch, fn, max(n * 2, 64), trials)
         nbytes = per + 2 * B * n_q * d * 4
-        out.append({"batch": B, "ctx": T, "heads": [n_q, n_kv, d], "us": round(us, 3), "bytes": nbytes,
-                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
-        print(f"[bench] attention B={B} ctx={T}: {us:.2f} us, {out[-1]['GBps']} GB/s", file=sys.stderr, flush=True)
-        del g, ks, vs
+        out.append({"batch": B, "ctx": T, "heads": [n_q, n_kv, d], "us": round(s["median"], 3),
+                    "p10_us": round(s["p10"], 3), "p90_us": round(s["p90"], 3), "bytes": nbytes,
+                    "GBps": round(rate(nbytes, s["median"]), 1)})
+        print(f"[bench] attention B={B} ctx={T}: {s['median']:.2f} us, {out[-1]['GBps']} GB/s",
+              file=sys.stderr, flush=True)
+        del ks, vs
         torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle (fp64 dequantize + fp64 GEMV + argmax) on whole steps, one thread."""
+# ------------------------------------------------------------ CPU baseline
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_leg(gemvs, has_argmax, seconds, threads):
+    """The oracle (fp64 dequantize + fp64 GEMV + argmax) on whole steps. threads=None:
+    the BLAS/OpenMP pools as the process found them (all the cores it may use)."""
     import oracle
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    def run():
         t0 = time.perf_counter()
         steps = 0
         while True:
             last = None
-            for g in wl.gemvs:
+            for g in gemvs:
                 last, _ = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K)
-            if wl.has_argmax:
+            if has_argmax:
                 oracle.argmax_ref(last.astype(np.float32))
             steps += 1
             el = time.perf_counter() - t0
             if el >= seconds or steps >= 50:
-                break
-    return steps, el
+                return steps, el
+    if threads is None:
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        steps, el = run()
+    else:
+        with threadpool_limits(threads):
+            used = threads
+            steps, el = run()
+    return steps, el, used
+
+
+# --------------------------------------------------------------- figures
+def figure(nbytes, s, peak, ceil=None):
+    us = s["median"]
+    gbps = rate(nbytes, us)
+    out = {"us": round(us, 3), "p10_us": round(s["p10"], 3), "p90_us": round(s["p90"], 3),
+           "bytes": int(nbytes), "GBps": round(gbps, 1), "pct_of_spec_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    if peak:
+        out["pct_of_measured_peak"] = round(100 * gbps / peak, 2)
+    if ceil is not None:
+        out["stream_ceiling"] = {"us": ceil["us"], "GBps": ceil["GBps"]}
+        out["pct_of_size_matched_ceiling"] = round(100 * ceil["us"] / us, 1)
+    return out
+
+
+def workload_figures(qg, torch, cfg, batches, weights, trials, peak, ceil, per_gemv):
+    """Every batch of one workload: its decode step as one call (and, at the first
+    batch, every GEMV alone when per_gemv)."""
+    out = {"workload": WORKLOAD_KEYS[cfg], "gemvs": [[g.name, g.M, g.K] for g in weights.gemvs][:6] +
+           ([["...", len(weights.gemvs)]] if len(weights.gemvs) > 6 else []),
+           "rotation_sets": weights.n_sets}
+    for B in batches:
+        wl = Workload(qg, torch, cfg, B, weights)
+        fn, nb = wl.best_step()
+        s = time_calls(torch, fn, wl.launch_count(2, 32), trials)
+        f = figure(nb, s, peak, ceil(nb) if ceil else None)
+        f["call"] = "qgemv_run_grouped_argmax" if wl.has_argmax else "qgemv_run_grouped"
+        out[f"B{B}"] = f
+        print(f"[bench] workload {cfg} B={B}: {f['us']:.2f} us, {f['GBps']} GB/s", file=sys.stderr, flush=True)
+        if per_gemv and B == batches[0] and len(wl.gemvs) > 1:
+            rows = []
+            for j, g in enumerate(wl.gemvs):
+                sj = time_calls(torch, lambda i, h, j=j: wl.launch_one(j, i, h), wl.launch_count(4, 64), trials)
+                fj = figure(wl.bytes[j], sj, peak, ceil(wl.bytes[j]) if ceil else None)
+                fj.update({"name": g.name, "M": g.M, "K": g.K})
+                rows.append(fj)
+            out[f"B{B}"]["per_gemv"] = rows
+        del wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def focused(qg, torch, args):
+    """--workload N: the step of one workload at one batch (and optionally every GEMV
+    alone), for profiler runs."""
+    cfg = args.workload
+    B = args.batch if args.batch is not None else synth.WORKLOAD_BATCHES[cfg][0]
+    weights = Weights(torch, synth.make_workload(cfg, max(B, 1)), args.rotate_gib * (1 << 30))
+    wl = Workload(qg, torch, cfg, B, weights)
+    if args.pmc_pass:
+        pmc_pass(qg, torch, wl, args.steps)
+        return
+    fn, nb = wl.best_step()
+    warm = capture(torch, fn, max(1, args.warmup))
+    replay_ms(torch, warm)
+    g = capture(torch, fn, args.steps)
+    samples = [replay_ms(torch, g) / args.steps for _ in range(args.trials)]
+    s = stats(samples)
+    out = {"workload": WORKLOAD_KEYS[cfg], "batch": B, "ms_per_step": round(s["median"], 6),
+           "p10_ms": round(s["p10"], 6), "p90_ms": round(s["p90"], 6), "bytes_per_step": nb,
+           "GBps": round(rate(nb, s["median"] * 1e3), 1)}
+    if args.per_kernel:
+        out["per_gemv"] = []
+        for j, gm in enumerate(wl.gemvs):
+            sj = time_calls(torch, lambda i, h, j=j: wl.launch_one(j, i, h), wl.launch_count(4, 64), args.trials)
+            out["per_gemv"].append({"name": gm.name, "M": gm.M, "K": gm.K, "us": round(sj["median"], 3),
+                                    "GBps": round(rate(wl.bytes[j], sj["median"]), 1)})
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -455,126 +593,114 @@ def main():
     import bandwidth_bound_quantized_amd as qg
 
     torch.cuda.set_device(0)
+    rotate = args.rotate_gib * (1 << 30)
     if args.size_sweep:
-        size_sweep(qg, torch, args.rotate_gib * (1 << 30))
+        size_sweep(qg, torch, rotate, args.trials)
         return
-    cfg = args.workload
-    B = args.batch if args.batch is not None else synth.WORKLOAD_BATCHES[cfg][0]
-    wl = Workload(qg, torch, cfg, B, args.rotate_gib * (1 << 30))
-    if args.pmc_pass:
-        pmc_pass(qg, torch, wl, args.steps)
+    if args.workload is not None:
+        focused(qg, torch, args)
         return
-    print(f"[bench] workload {cfg} B={B}: {len(wl.gemvs)} GEMVs, {wl.step_bytes} B/step, "
-          f"{wl.n_sets} rotation sets", file=sys.stderr, flush=True)
-
-    # ---- timed steps (graph of exactly `steps` steps, rotating through the sets).
-    # grouped: the step's GEMVs (independent inputs) in one qgemv_run_grouped call;
-    # sequential: one qgemv_run launch per GEMV, as a decode step whose GEMVs
-    # depend on each other must run them.
-    results = {}
-    modes = [("sequential", wl.step), ("grouped", wl.step_grouped)]
-    if wl.has_argmax:
-        modes.append(("fused", wl.step_fused))
-    for mode, fn in modes:
-        g_warm = capture(torch, fn, max(1, args.warmup))
-        time_graph(torch, g_warm)
-        g_steps = capture(torch, fn, args.steps)
-        ms = time_graph(torch, g_steps) / args.steps
-        results[mode] = ms
-        nb = wl.fused_bytes if mode == "fused" else wl.step_bytes
-        print(f"[bench] {mode}: {ms * 1e3:.2f} us/step, {nb / (ms * 1e-3) / 1e9:.1f} GB/s",
-              file=sys.stderr, flush=True)
-        del g_warm, g_steps
-    attention = None
-    if cfg == 2 and not args.no_attention:
-        attention = attention_bench(qg, torch, args.rotate_gib * (1 << 30))
-    fused_layer = None
-    if cfg == 2 and not args.no_fused_layer:
-        fl = FusedLayer(qg, torch, wl)
-        g_warm = capture(torch, fl.step, max(1, args.warmup))
-        time_graph(torch, g_warm)
-        g_steps = capture(torch, fl.step, args.steps)
-        ms_fl = time_graph(torch, g_steps) / args.steps
-        del g_warm, g_steps
-        per_op = []
-        if args.per_kernel:
-            for k in range(5):
-                n = max(wl.n_sets * 4, 64)
-                gk = capture(torch, lambda i, h, k=k: fl.op(k, i, h), n)
-                time_graph(torch, gk)
-                us = time_graph(torch, gk, reps=3) * 1e3 / n
-                gp = capture(torch, lambda i, h, k=k: wl.launch_one(k, i, h), n)
-                time_graph(torch, gp)
-                us_p = time_graph(torch, gp, reps=3) * 1e3 / n
-                per_op.append({"op": FusedLayer.NAMES[k], "fused_us": round(us, 3), "plain_gemv_us": round(us_p, 3)})
-                del gk, gp
-        fused_layer = {
-            "chain": "qkv(RMSNorm) -> o(+=residual) -> gate_up(RMSNorm, SwiGLU of paired rows) -> "
-                     "down(+=residual) -> lm_head(RMSNorm, argmax): 5 dependent qgemv_run_fused launches",
-            "us_per_step": round(ms_fl * 1e3, 3), "bytes_per_step": fl.bytes,
-            "GBps": round(fl.bytes / (ms_fl * 1e-3) / 1e9, 1),
-            "plain_sequential_us_per_step": round(results["sequential"] * 1e3, 3),
-            "plain_sequential_launches": len(wl.gemvs) + 1}
-        if per_op:
-            fused_layer["per_op"] = per_op
-        print(f"[bench] fused layer chain: {ms_fl * 1e3:.2f} us/step, {fused_layer['GBps']} GB/s",
-              file=sys.stderr, flush=True)
-    ms_per_step = results["fused"] if wl.has_argmax else results["grouped"]
-    value = (wl.fused_bytes if wl.has_argmax else wl.step_bytes) / (ms_per_step * 1e-3) / 1e9
-    value_seq = wl.step_bytes / (results["sequential"] * 1e-3) / 1e9
-    value_grp = wl.step_bytes / (results["grouped"] * 1e-3) / 1e9
-
-    # ---- dominant kernel: the grouped launch with the most bytes, timed alone
-    dom_key = max(wl.classes, key=wl.class_bytes)
-    n_dom = max(wl.n_sets * 4, 64)
-    if dom_key[0] == "alone":
-        dom_fn = (lambda i, h, j=dom_key[1]: wl.launch_one(j, i, h))
-    else:
-        dom_fn = (lambda i, h: wl.launch_class(dom_key, i, h))
-    g_dom = capture(torch, dom_fn, n_dom)
-    time_graph(torch, g_dom)
-    dom_us = time_graph(torch, g_dom, reps=3) * 1e3 / n_dom
-    dom_bytes = wl.class_bytes(dom_key)
-    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
-
-    per_kernel = []
-    if args.per_kernel:
-        for j, gm in enumerate(wl.gemvs):
-            n = max(wl.n_sets * 4, 64)
-            gj = capture(torch, lambda i, h, j=j: wl.launch_one(j, i, h), n)
-            time_graph(torch, gj)
-            us = time_graph(torch, gj, reps=3) * 1e3 / n
-            per_kernel.append({"name": gm.name, "M": gm.M, "K": gm.K, "us": round(us, 3),
-                               "GBps": round(wl.bytes[j] / (us * 1e-6) / 1e9, 1)})
-            del gj
+    t_start = time.perf_counter()
 
     peak = None
     if not args.no_peak:
-        peak_gbps, peak_cfg, sweep = measure_peak(qg, torch, args.peak_gib)
+        peak_gbps, peak_cfg = measure_peak(qg, torch, args.peak_gib, max(args.trials, 7))
         peak = {"GBps": round(peak_gbps, 1), "config": peak_cfg, "buffer_GiB": args.peak_gib}
-        print(f"[bench] measured streaming-read peak {peak_gbps:.1f} GB/s {peak_cfg}",
-              file=sys.stderr, flush=True)
+        print(f"[bench] measured streaming-read peak {peak_gbps:.1f} GB/s {peak_cfg}", file=sys.stderr, flush=True)
+    pk = peak["GBps"] if peak else None
+    ceil = StreamCeiling(qg, torch, rotate, args.trials)
+
+    # ---- the headline: workload 2 at batch 1, graphs of exactly --steps steps
+    w2 = Weights(torch, synth.make_workload(2, 8), rotate)
+    wl = Workload(qg, torch, 2, 1, w2)
+    print(f"[bench] workload 2 B=1: {len(wl.gemvs)} GEMVs, {wl.fused_bytes} B/step, {wl.n_sets} rotation sets",
+          file=sys.stderr, flush=True)
+    modes = {}
+    for mode, fn in (("fused", wl.step_fused), ("grouped", wl.step_grouped), ("sequential", wl.step)):
+        warm = capture(torch, fn, max(1, args.warmup))
+        replay_ms(torch, warm)
+        del warm
+        g = capture(torch, fn, args.steps)
+        modes[mode] = stats([replay_ms(torch, g) / args.steps for _ in range(args.trials)])
+        del g
+        nb = wl.fused_bytes if mode == "fused" else wl.step_bytes
+        print(f"[bench] {mode}: {modes[mode]['median'] * 1e3:.2f} us/step, "
+              f"{rate(nb, modes[mode]['median'] * 1e3):.1f} GB/s", file=sys.stderr, flush=True)
+    ms_per_step = modes["fused"]["median"]
+    fused_bytes, step_bytes = wl.fused_bytes, wl.step_bytes
+    value = rate(fused_bytes, ms_per_step * 1e3)
+
+    # per GEMV alone (the same inputs), and the step's ceiling
+    per_gemv = []
+    for j, g in enumerate(wl.gemvs):
+        sj = time_calls(torch, lambda i, h, j=j: wl.launch_one(j, i, h), wl.launch_count(4, 64), args.trials)
+        fj = figure(wl.bytes[j], sj, pk, ceil(wl.bytes[j]))
+        fj.update({"name": g.name, "M": g.M, "K": g.K})
+        per_gemv.append(fj)
+
+    fused_layer = None
+    if not args.no_fused_layer:
+        fl = FusedLayer(qg, torch, wl)
+        s = time_calls(torch, fl.step, wl.launch_count(2, 32), args.trials)
+        fused_layer = {
+            "chain": "qkv(RMSNorm) -> o(+=residual) -> gate_up(RMSNorm, SwiGLU of paired rows) -> "
+                     "down(+=residual) -> lm_head(RMSNorm, argmax): 5 dependent qgemv_run_fused launches",
+            "us_per_step": round(s["median"], 3), "p10_us": round(s["p10"], 3), "p90_us": round(s["p90"], 3),
+            "bytes_per_step": fl.bytes, "GBps": round(rate(fl.bytes, s["median"]), 1),
+            "plain_sequential_us_per_step": round(modes["sequential"]["median"] * 1e3, 3)}
+        print(f"[bench] fused layer chain: {s['median']:.2f} us/step", file=sys.stderr, flush=True)
+        del fl
+    del wl
+
+    # ---- every workload the metric names
+    configs = {}
+    w1 = Weights(torch, synth.make_workload(1, 1), rotate)
+    configs["1"] = workload_figures(qg, torch, 1, [1], w1, args.trials, pk, ceil, False)
+    del w1
+    b1 = figure(fused_bytes, {k: v * 1e3 for k, v in modes["fused"].items() if k != "n"}, pk, ceil(fused_bytes))
+    b1.update({"call": "qgemv_run_grouped_argmax", "per_gemv": per_gemv})
+    configs["2"] = {"workload": WORKLOAD_KEYS[2], "gemvs": [[g.name, g.M, g.K] for g in w2.gemvs],
+                    "rotation_sets": w2.n_sets, "B1": b1}
+    b8 = workload_figures(qg, torch, 2, [8], w2, args.trials, pk, ceil, False)
+    configs["2"]["B8"] = b8["B8"]
+    del w2
+    torch.cuda.empty_cache()
+    w3 = Weights(torch, synth.make_workload(3, 1), rotate)
+    configs["3"] = workload_figures(qg, torch, 3, [1], w3, args.trials, pk, ceil, True)
+    del w3
+    torch.cuda.empty_cache()
+    w4 = Weights(torch, synth.make_workload(4, 8), rotate)
+    configs["4"] = workload_figures(qg, torch, 4, [1, 2, 4, 8], w4, args.trials, pk, ceil, False)
+    del w4
+    torch.cuda.empty_cache()
+    w5 = Weights(torch, synth.make_workload(5, 8), rotate)
+    configs["5"] = workload_figures(qg, torch, 5, [1, 8], w5, args.trials, pk, ceil, False)
+    del w5
+    torch.cuda.empty_cache()
+
+    attention = None
+    if not args.no_attention:
+        attention = attention_bench(qg, torch, rotate, args.trials)
 
     cpu = None
     if not args.no_cpu_baseline:
-        steps, el = cpu_baseline(wl, args.cpu_seconds)
-        cpu = {"value": round(wl.step_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+        g2 = synth.make_workload(2, 1)
+        nbytes = sum(gemv_bytes(qg, g.fmt, g.M, g.K, 1) for g in g2) + 4 * 32000 + 4
+        steps_a, el_a, used_a = cpu_leg(g2, True, args.cpu_seconds, None)
+        steps_1, el_1, _ = cpu_leg(g2, True, args.cpu_seconds, 1)
+        cpu = {"value": round(nbytes * steps_a / el_a / 1e9, 4), "unit": "GB/s", "cores": int(used_a),
                "kind": "oracle",
-               "sample": f"{steps} whole step(s) of workload {cfg} (all {len(wl.gemvs)} GEMVs"
-                         f"{' + argmax' if wl.has_argmax else ''}), fp64, one thread, {el:.1f} s"}
+               "sample": f"{steps_a} whole step(s) of the Q4_0 TinyLlama set at batch 1 (5 GEMVs + argmax), "
+                         f"fp64, {el_a:.1f} s, BLAS threads as found ({used_a})",
+               "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0)),
+               "one_thread": {"value": round(nbytes * steps_1 / el_1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{steps_1} whole step(s), {el_1:.1f} s"}}
+        print(f"[bench] cpu oracle: {cpu['value']} GB/s ({used_a} threads), "
+              f"{cpu['one_thread']['value']} GB/s (1 thread)", file=sys.stderr, flush=True)
 
-    names = {1: "bf16_gemv_2048x2048", 2: "q4_0_g32_tinyllama_gemv_set+argmax",
-             3: "int8_g32_llama32_1b_gemv_set", 4: "q4_0_g32_tinyllama_decode_step_89_gemvs+argmax",
-             5: "int4_g128_ffn+int8_g32_lm_head+argmax",
-             6: "q4_0_g32_llama32_1b_layer_gemvs+int8_row_lm_head+argmax"}
-    dtypes = {1: "bf16", 2: "q4_0", 3: "int8", 4: "q4_0", 5: "int4/int8", 6: "q4_0/int8"}
-    if dom_key[0] == "alone":
-        dom_label = f"qgemv_run {wl.gemvs[dom_key[1]].name}"
-    elif wl.has_argmax and len(wl.gemvs) - 1 in wl.classes[dom_key]:
-        dom_label = f"qgemv_run_grouped_argmax launch [{wl.class_label(dom_key)}+argmax]"
-    else:
-        dom_label = f"qgemv_run_grouped launch [{wl.class_label(dom_key)}]"
-    traffic = recorded_traffic(dom_label, names[cfg], B)
+    traffic = recorded_traffic("qgemv_run_grouped_argmax launch [qkv+o+gate_up+down+lm_head+argmax]",
+                               WORKLOAD_KEYS[2], 1)
+    dom_us = ms_per_step * 1e3
     out = {
         "metric": "fused-dequant GEMV achieved HBM GB/s and % of peak (bf16/int8/Q4_0, batch 1)",
         "value": round(value, 1),
@@ -583,46 +709,49 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
-        "value_sequential": round(value_seq, 1),
-        "ms_per_step_sequential": round(results["sequential"], 6),
-        "value_grouped_separate_argmax": round(value_grp, 1) if wl.has_argmax else None,
-        "ms_per_step_grouped_separate_argmax": round(results["grouped"], 6) if wl.has_argmax else None,
+        "p10_ms_per_step": round(modes["fused"]["p10"], 6),
+        "p90_ms_per_step": round(modes["fused"]["p90"], 6),
+        "trials": args.trials,
+        "value_sequential": round(rate(step_bytes, modes["sequential"]["median"] * 1e3), 1),
+        "ms_per_step_sequential": round(modes["sequential"]["median"], 6),
+        "value_grouped_separate_argmax": round(rate(step_bytes, modes["grouped"]["median"] * 1e3), 1),
+        "ms_per_step_grouped_separate_argmax": round(modes["grouped"]["median"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtypes[cfg],
+        "dtype": "q4_0",
         "data": "synthetic (seeded; same shapes and value distributions as the workload)",
-        "config": {"workload": names[cfg], "batch": B,
-                   "gemvs": [[g.name, g.M, g.K] for g in wl.gemvs][:6] + (
-                       [["...", len(wl.gemvs)]] if len(wl.gemvs) > 6 else []),
-                   "bytes_per_step": wl.fused_bytes if wl.has_argmax else wl.step_bytes,
-                   "rotation_sets": wl.n_sets,
-                   "rotation_bytes": wl.n_sets * sum(g.w.nbytes + (g.s.nbytes if g.s is not None else 0)
-                                                     for g in wl.gemvs),
-                   "execution": "value: the step's independent GEMVs (one launch per format) and, "
-                                "with an LM head, its argmax in one qgemv_run_grouped_argmax call "
-                                "(the argmax inside the LM head's launch at batch <= 2); "
-                                "value_grouped_separate_argmax: qgemv_run_grouped + qgemv_argmax; "
-                                "value_sequential: one qgemv_run launch per GEMV + qgemv_argmax",
-                   "timing": "HIP graph of exactly `steps` steps, events on the launch stream"},
+        "config": {"workload": WORKLOAD_KEYS[2], "batch": 1,
+                   "gemvs": configs["2"]["gemvs"],
+                   "bytes_per_step": int(fused_bytes),
+                   "execution": "value: the step's independent GEMVs and the LM-head argmax in one "
+                                "qgemv_run_grouped_argmax call (one launch; the argmax inside it); "
+                                "value_sequential: the dependent-chain figure, one qgemv_run launch per "
+                                "GEMV then qgemv_argmax; value_grouped_separate_argmax: qgemv_run_grouped "
+                                "+ qgemv_argmax",
+                   "timing": f"median (p10, p90) of {args.trials} trials, each one replay of a HIP graph "
+                             f"of exactly `steps` steps after a graph of `warmup` steps; events on the "
+                             f"launch stream"},
         "pct_of_spec_8TBps": round(100 * value / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": dom_label,
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3),
-                     "launches": n_dom},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "gemv_xreg_group_kernel<Q4_0, 1 batch row, argmax> "
+                               "(qgemv_run_grouped_argmax: the whole step is this one launch)",
+                     "bytes_per_launch": int(fused_bytes), "avg_launch_us": round(dom_us, 3),
+                     "timing": "the headline's median step (one launch per step), graph-replayed"},
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     if peak is not None:
         out["measured_peak"] = peak
         out["pct_of_measured_peak"] = round(100 * value / peak["GBps"], 2)
-        out["roofline"]["pct_of_measured_peak"] = round(100 * dom_gbps / peak["GBps"], 2)
-    if per_kernel:
-        out["per_kernel"] = per_kernel
+        out["roofline"]["pct_of_measured_peak"] = round(100 * value / peak["GBps"], 2)
+    out["roofline"]["pct_of_size_matched_ceiling"] = configs["2"]["B1"].get("pct_of_size_matched_ceiling")
     if fused_layer is not None:
         out["fused_layer"] = fused_layer
     if attention is not None:
         out["attention_decode"] = attention
+    out["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(out), flush=True)
 
 
