@@ -71,24 +71,6 @@
 #ifndef QGEMV_GROUP_CONTIG_MIN
 #define QGEMV_GROUP_CONTIG_MIN 8  // grouped launch: row groups per wave from which waves take contiguous ranges
 #endif
-#ifndef QGEMV_MFMA_TARGET_WAVES_PER_CU
-#define QGEMV_MFMA_TARGET_WAVES_PER_CU 16  // matrix-core kernel: waves per CU worth aiming for
-#endif
-#ifndef QGEMV_MFMA_MAX_WAVES_PER_CU
-#define QGEMV_MFMA_MAX_WAVES_PER_CU 16     // ... and the most that fit (register budget)
-#endif
-#ifndef QGEMV_MFMA_COPY_BEFORE_SWAP
-#define QGEMV_MFMA_COPY_BEFORE_SWAP 0      // see mfma_units (compute)
-#endif
-#ifndef QGEMV_MFMA_SCALE_SHFL
-#define QGEMV_MFMA_SCALE_SHFL 1            // see mfma_units (scale loads)
-#endif
-#ifndef QGEMV_MFMA_FORCE_KS
-#define QGEMV_MFMA_FORCE_KS 0              // nonzero: fixed K split (if it divides the steps)
-#endif
-#ifndef QGEMV_MFMA_FORCE_TW
-#define QGEMV_MFMA_FORCE_TW 0              // nonzero: fixed tiles per workgroup
-#endif
 
 namespace qgemv {
 namespace {
@@ -991,149 +973,17 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
 //
 // From batch 3 on, the dot-product kernels above spend one dot2 instruction
 // per weight pair and batch row and become bound by the vector ALUs instead
-// of HBM. This kernel hands the products to the matrix cores:
-// v_mfma_f32_16x16x32_bf16 with A = x (16 rows: the batch rows, the rest
-// padding) and B = 32 dequantized weights of 16 weight rows, so that
-// D[b][i] is the dot product of batch row b and weight row i over one
-// 32-position "chunk" of K. The vector ALUs only unpack codes (exactly, as
-// above) and apply each group's scale to its chunk's D tile.
+// of HBM. The matrix-core kernel below hands the products to
+// v_mfma_f32_4x4x4bf16_1k; the vector ALUs only unpack codes (exactly, as
+// above) and apply each unit's scale.
 //
-// Lane (i, q) = (lane % 16, lane / 16) loads 16 bytes of weight row i at
-// byte 16q of every 64-byte slice of the row, so each load instruction of a
-// wave reads 64 contiguous bytes of 16 rows. For the quantized formats the
-// four lanes of a row then exchange dwords with permlane swaps, after which
-// each lane holds, for each chunk of the slice, the 8 codes of k positions
-// 8q..8q+7 of that chunk. Which K elements those positions are depends on
-// how the format packs codes (chunk_elem below); x is staged in LDS in that
-// same order, so A and B always agree.
-//
-// In the D tile, lane (i, q) holds batch rows 4q..4q+3 of weight row i, so a
-// group's scale is one value per lane. The 4-bit formats' offset of 8 is
-// removed with the same identity as above, summed per group:
-// sum_g d_g sum(q x) - 8 sum_g d_g sum_g(x); the second term is itself a
-// small product of the scales with the per-group x sums and runs on the
-// float32 matrix instruction (v_mfma_f32_16x16x4_f32), four groups at a time.
-//
-// Work split: a workgroup has TW x KS waves; each of TW tiles of 16 rows is
-// shared by KS waves that take equal contiguous ranges of the row's steps
-// (a step is kSlices 64-byte slices). The KS partial tiles are added in LDS
-// in a fixed order. A "unit" is TW consecutive tiles; a workgroup takes a
-// contiguous range of units (of one GEMV, or of several GEMVs of one K in a
-// grouped launch); every wave issues the loads of its next step before
-// computing the current one.
+// Work split: a workgroup takes a contiguous range of 8- or 16-row tiles of
+// one GEMV (in a grouped launch, the workgroups are shared out among the
+// GEMVs of one format, whatever their K); its waves split the range's
+// (tile, step) pairs evenly (see mfma_tiles).
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int FMT> struct MfmaFmt;
-#ifndef QGEMV_MFMA_SLICES_BF16
-#define QGEMV_MFMA_SLICES_BF16 4
-#endif
-#ifndef QGEMV_MFMA_SLICES_INT8
-#define QGEMV_MFMA_SLICES_INT8 2
-#endif
-#ifndef QGEMV_MFMA_SLICES_Q4
-#define QGEMV_MFMA_SLICES_Q4 2
-#endif
-#ifndef QGEMV_MFMA_SLICES_INT4
-#define QGEMV_MFMA_SLICES_INT4 4
-#endif
-// kSlices: 64-byte row slices per step (per lane: 16 bytes each);
-// kChunksPerSlice: 32-position MFMA chunks per slice; kGroups: scale groups
-// per step; kChunksPerGroup: chunks sharing one scale; kStepElems: K
-// elements per step.
-template <> struct MfmaFmt<QGEMV_BF16> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_BF16;
-  static constexpr int kChunksPerSlice = 1;
-  static constexpr int kGroups = 0;
-  static constexpr int kChunksPerGroup = 0;
-  static constexpr int kStepElems = 32 * kSlices;
-};
-template <> struct MfmaFmt<QGEMV_INT8_G32> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT8;
-  static constexpr int kChunksPerSlice = 2;
-  static constexpr int kGroups = 2 * kSlices;
-  static constexpr int kChunksPerGroup = 1;
-  static constexpr int kStepElems = 64 * kSlices;
-};
-template <> struct MfmaFmt<QGEMV_Q4_0_G32> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_Q4;
-  static constexpr int kChunksPerSlice = 4;
-  static constexpr int kGroups = 4 * kSlices;
-  static constexpr int kChunksPerGroup = 1;
-  static constexpr int kStepElems = 128 * kSlices;
-};
-template <> struct MfmaFmt<QGEMV_INT4_G128> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT4;
-  static constexpr int kChunksPerSlice = 4;
-  static constexpr int kGroups = kSlices;
-  static constexpr int kChunksPerGroup = 4;
-  static constexpr int kStepElems = 128 * kSlices;
-};
-// int8-row: no group scales inside a step; the row's scale multiplies the
-// finished dot product in the store
-template <> struct MfmaFmt<QGEMV_INT8_ROW> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_INT8;
-  static constexpr int kChunksPerSlice = 2;
-  static constexpr int kGroups = 0;
-  static constexpr int kChunksPerGroup = 0;
-  static constexpr int kStepElems = 64 * kSlices;
-};
-template <> struct MfmaFmt<QGEMV_INT4_G64> {
-  static constexpr int kSlices = QGEMV_MFMA_SLICES_Q4;
-  static constexpr int kChunksPerSlice = 4;
-  static constexpr int kGroups = 2 * kSlices;
-  static constexpr int kChunksPerGroup = 2;
-  static constexpr int kStepElems = 128 * kSlices;
-};
-
-// K element at position pos (0..31) of chunk c; position pos = 8q + 4h + j
-// is the j-th code of half h of lane row q after the exchange.
-//   bf16  : slice = chunk, lane row q loaded elements 8q..8q+7.
-//   int8  : slice = 2 chunks (groups); after one 32-lane swap, lane row q of
-//           chunk 0 holds elements 0-7, 16-23, 8-15, 24-31 for q = 0..3.
-//   Q4_0  : slice = 4 blocks; after the 4x4 dword transpose, lane row q holds
-//           byte dword q of each block: low nibbles 4q..4q+3, high nibbles
-//           16+4q..16+4q+3.
-//   int4-g128: slice = 1 group of 128; lane row q of chunk c holds byte
-//           dword q of the group's quarter c: elements 16c+4q.. (low) and
-//           64+16c+4q.. (high).
-//   int4-g64: slice = 2 groups of 64; chunk c is half c&1 of group c>>1:
-//           elements 16(c&1)+4q.. (low) and 32+16(c&1)+4q.. (high).
-//   int8-row: as int8-g32.
-template <int FMT>
-__device__ __forceinline__ int chunk_elem(int c, int pos) {
-  const int q = pos >> 3, h = (pos >> 2) & 1, j = pos & 3;
-  if constexpr (FMT == QGEMV_BF16) return 32 * c + pos;
-  else if constexpr (is_int8_fmt(FMT)) return 32 * c + 16 * (q & 1) + 8 * (q >> 1) + 4 * h + j;
-  else if constexpr (FMT == QGEMV_Q4_0_G32) return 32 * c + 16 * h + 4 * q + j;
-  else if constexpr (FMT == QGEMV_INT4_G64) return 64 * (c >> 1) + 32 * h + 16 * (c & 1) + 4 * q + j;
-  else return 128 * (c >> 2) + 64 * h + 16 * (c & 3) + 4 * q + j;
-}
-
-__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-  const uint32_t r0 = r[0], r1 = r[1];
-  x = r0; y = r1;
-}
-__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-  const uint32_t r0 = r[0], r1 = r[1];
-  x = r0; y = r1;
-}
-
-// Four codes (one dword) of a 4-bit chunk -> 8 bf16 B-operand values.
-__device__ __forceinline__ bf16x8_t nibbles_to_b(uint32_t d) {
-  const uint32_t lo = d & 0x0F0F0F0Fu;
-  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
-  const u32x4 v = {
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true))};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // Four int8 codes -> two bf16 pairs (in byte order).
 __device__ __forceinline__ void int8x4_to_bf16(uint32_t d, uint32_t& p0, uint32_t& p1) {
@@ -1145,24 +995,13 @@ __device__ __forceinline__ void int8x4_to_bf16(uint32_t d, uint32_t& p0, uint32_
   p1 = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
-__device__ __forceinline__ bf16x8_t int8_to_b(uint32_t d0, uint32_t d1) {
-  uint32_t p0, p1, p2, p3;
-  int8x4_to_bf16(d0, p0, p1);
-  int8x4_to_bf16(d1, p2, p3);
-  const u32x4 v = {p0, p1, p2, p3};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-__device__ __forceinline__ float scale_of(const uint32_t* s, int g) {
-  const uint32_t w = s[g >> 1];
-  return half_to_float(static_cast<uint16_t>((g & 1) ? (w >> 16) : w));
-}
-
 constexpr int kMfmaMaxThreads = 1024;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// rows per matrix-core tile: 2 (batch 5..8) or 4 (batch 3..4) groups of 4
+template <int NB> constexpr int kMfmaTileRows = NB == 8 ? 8 : 16;
 
-// One GEMV of a matrix-core launch. Its tiles are taken in "units" of TW
-// tiles (TW = waves per workgroup / KS); ustart numbers the entry's first
-// unit in the launch.
+// One GEMV of a matrix-core launch: workgroups wg0 .. wg0 + nwg - 1 of the
+// launch take contiguous, balanced ranges of its 16-row tiles.
 struct MfmaEntry {
   const uint8_t* W;
   const uint16_t* S;
@@ -1170,17 +1009,15 @@ struct MfmaEntry {
   float* Y;
   int M;
   int K;
-  int ustart;
-  int pad;
+  int wg0;
+  int nwg;
 };
 
-// Up to N GEMVs of one format, K and batch (by value: kernel arguments).
+// Up to N GEMVs of one format and batch, any K (by value: kernel arguments).
 template <int N>
 struct MfmaTable {
   int n;
-  int units;    // over all entries
-  int KS;       // waves sharing a tile
-  int pad;
+  int pad[3];
   MfmaEntry e[N];
 };
 
@@ -1343,370 +1180,421 @@ __device__ __forceinline__ void stage_norm_rows(const Fusion& fu, int K, int bat
 // Units [g0, g1) of one entry (the body of the matrix-core kernel).
 // FUSED: the operations of fu fused in (prologue in the x staging, epilogue
 // in the store); the LDS then ends with kNormScratchBytes of scratch.
+// ---- matrix-core kernel (batch 3..8) -------------------------------------
+// The products go to v_mfma_f32_4x4x4bf16_1k: 16 independent 4 x 4 x 4
+// blocks per instruction. Block b (lanes 4b .. 4b + 3) takes its own stretch
+// of K, so a lane group needs only four weight rows at one position of K:
+//   A (x):       lane 4b + i holds 4 consecutive x values of batch row i
+//   B (weights): lane 4b + j holds the same 4 positions of weight row j
+//   D:           lane 4b + j, register r: sum over the 4 positions, batch
+//                row r, weight row j
+// A load instruction reads 4 rows x 256 bytes (lane 4b + j: row j, 16-byte
+// unit b), and the unit's codes feed the B operand in place: no lane
+// exchange. A unit is one scale group or a part of one (4-bit: 32 weights,
+// int8: 16, bf16: 8), so each lane applies one scale per unit to its D
+// registers; the 4-bit offset (codes stored as w + 8) is removed by starting
+// each unit's chain at -8 * (sum of the unit's x), the bias identity of the
+// Rust page's Lesson 6. At the end of a tile each lane's running sums are
+// added across the 16 lane groups (permlane swaps, then DPP row rotations).
+// Batch rows come in halves of 4 (batch 5..8: two A operands per position,
+// each B operand used twice).
+template <int FMT> struct M4 {
+  static constexpr int kUnitElems = Traits<FMT>::kElems;    // weights per 16-byte unit
+  static constexpr int kSub = kUnitElems / 4;               // MFMA positions of 4 per unit
+  static constexpr int kStepElems = 16 * kUnitElems;        // a step: 16 units of each row
+  static constexpr bool kBias = Traits<FMT>::kBias;         // 4-bit: the -8 offset
+  // scales: 0 none, -1 one per row, else units per scale group
+  static constexpr int kUnitsPerScale = Traits<FMT>::kUnitsPerScale;
+};
+
+// K element of the first of the 4 positions of MFMA step s of unit u
+// (nibble order: Q4_0 element j / j + 16, g64 j / j + 32, g128 j / j + 64 in
+// the low / high nibble of byte j; a 4-bit unit is a 16-byte quarter (g128),
+// half (g64) or all (Q4_0) of its group's codes)
+template <int FMT>
+__device__ __forceinline__ int m4_elem(int u, int s) {
+  if constexpr (FMT == QGEMV_BF16) return 8 * u + 4 * s;
+  else if constexpr (is_int8_fmt(FMT)) return 16 * u + 4 * s;
+  else {
+    const int d = s >> 1, h = s & 1;               // dword d, low (0) or high (1) nibbles
+    if constexpr (FMT == QGEMV_Q4_0_G32) return 32 * u + 16 * h + 4 * d;
+    else if constexpr (FMT == QGEMV_INT4_G64) return 64 * (u >> 1) + 16 * (u & 1) + 32 * h + 4 * d;
+    else return 128 * (u >> 2) + 16 * (u & 3) + 64 * h + 4 * d;
+  }
+}
+
+// B operand (4 bf16) of MFMA step s of a unit's 16 code bytes
+template <int FMT>
+__device__ __forceinline__ v4i16 m4_b(const u32x4& w, int s) {
+  uint32_t lo, hi;
+  if constexpr (FMT == QGEMV_BF16) {
+    lo = s ? w.z : w.x;
+    hi = s ? w.w : w.y;
+  } else if constexpr (is_int8_fmt(FMT)) {
+    const uint32_t d = s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
+    int8x4_to_bf16(d, lo, hi);
+  } else {
+    const int di = s >> 1;
+    const uint32_t d = di == 0 ? w.x : di == 1 ? w.y : di == 2 ? w.z : w.w;
+    const uint32_t n = (s & 1) ? ((d >> 4) & 0x0F0F0F0Fu) : (d & 0x0F0F0F0Fu);
+    // a byte q in 0..15 read as e4m3 is q * 2^-9: the conversion's scale 2^9 makes it exact
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(n, 512.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(n, 512.0f, true));
+  }
+  const u32x2 v = {lo, hi};
+  return __builtin_bit_cast(v4i16, v);
+}
+
+// x in LDS: batch row r, element e at byte r * m4_xrow(K) + 136 * (e / 64) +
+// 2 * (e % 64): 64-element runs padded by 8 bytes and a row stride of 8 * c
+// bytes past a multiple of 128, so that the 16 lanes an A read serves
+// together fall on distinct bank pairs (c from the format's unit pattern).
+template <int FMT>
+__host__ __device__ constexpr int m4_bank_shift() {
+  return (FMT == QGEMV_INT8_G32 || FMT == QGEMV_INT8_ROW || FMT == QGEMV_INT4_G128) ? 1 : 2;
+}
+template <int FMT>
+__host__ __device__ __forceinline__ uint32_t m4_xrow(int K) {
+  const uint32_t run = 136u * static_cast<uint32_t>((K + 63) / 64);
+  return (run + 127u) / 128u * 128u + 8u * m4_bank_shift<FMT>();
+}
+__device__ __forceinline__ uint32_t m4_xoff(int e) {
+  return 136u * static_cast<uint32_t>(e >> 6) + 2u * static_cast<uint32_t>(e & 63);
+}
+
+template <int CTRL>
+__device__ __forceinline__ f32x4 dpp4(const f32x4& v) {
+  f32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = dpp_f<CTRL>(v[k]);
+  return o;
+}
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8
+constexpr int kDppRowRor4 = 0x124;    // row_ror:4
+
+// Tiles t0 .. t1 - 1 (kTR rows each) of one GEMV by one workgroup. The
+// workgroup's (tile, step) pairs are laid end to end and every wave takes an
+// equal contiguous share, so all waves stream the same number of steps
+// whatever the tile count, and no barrier stands between tiles. A wave
+// stores a tile it holds whole; a tile split between waves leaves one
+// partial result per wave in LDS, and after the workgroup's last barrier the
+// wave holding the tile's last step adds them in wave order (a fixed order:
+// results are deterministic, and a row's arithmetic does not depend on the
+// batch or on the other rows).
 template <int FMT, int NB, bool FUSED = false>
-__device__ __forceinline__ void mfma_units(const MfmaEntry& ent, int g0, int g1, int batch, int KS,
+__device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1, int batch,
                                            u32x4* lds_v4, const Fusion& fu) {
-  using F = MfmaFmt<FMT>;
-  constexpr int kCPS = F::kChunksPerSlice;
-  constexpr int kChunks = F::kSlices * kCPS;          // chunks per step
-  constexpr int kSW = F::kGroups > 0 ? F::kGroups / 2 : 1;   // scale dwords per step
-  constexpr int kOutLanes = 4 * NB;                    // lanes holding real batch rows
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds_v4);
+  using F = M4<FMT>;
+  constexpr int NBh = NB / 4;                          // batch halves of 4 rows
+  constexpr int R = NB == 8 ? 2 : 4;                   // row groups of 4 rows per tile
+  constexpr int kTR = 4 * R;                           // rows per tile
+  constexpr int kV = R * NBh * 4;                      // running sums per lane (16)
+  static_assert(kV == 16, "sums per lane");
+  constexpr bool kScaled = F::kUnitsPerScale > 0;      // a scale per group inside the row
   const uint8_t* __restrict__ W = ent.W;
   const uint16_t* __restrict__ S = ent.S;
   const uint16_t* __restrict__ X = ent.X;
   float* __restrict__ Y = ent.Y;
   const int M = ent.M, K = ent.K;
-  const int iters = g1 - g0;                           // units of this call
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int TW = static_cast<int>(blockDim.x >> 6) / KS;
-  const int tg = wave / KS;                            // tile slot of this wave
-  const int ks = wave - tg * KS;                       // K range of this wave
-  const int i = lane & 15, q = lane >> 4;
-  const int bcl = min(i, NB - 1);                      // A row this lane supplies
-  const int nchunk = K >> 5;
-  const int ngroups = F::kGroups ? K / (F::kStepElems / F::kGroups) : 0;
-  const int nsteps = K / F::kStepElems;
-  const int Lw = nsteps / KS;                          // steps per wave per tile
+  const int nw = static_cast<int>(blockDim.x >> 6);
+  const int lb = lane >> 2, lj = lane & 3;             // MFMA block (unit of the step), row / batch index
+  const int nst = K / F::kStepElems;                   // steps per tile
+  const int nflat = (t1 - t0) * nst;                   // the workgroup's (tile, step) pairs
+  const int va = static_cast<int>(static_cast<long>(wave) * nflat / nw);
+  const int vb = static_cast<int>(static_cast<long>(wave + 1) * nflat / nw);
   const uint32_t row_bytes = static_cast<uint32_t>(
       FMT == QGEMV_BF16 ? 2 * K : is_int8_fmt(FMT) ? K : K / 2);
-  constexpr bool kBiasSums = F::kChunksPerGroup > 0 && !is_int8_fmt(FMT);   // 4-bit formats
-  // LDS: x [nchunk][NB][32] bf16 | group sums [ngroups][NB] (4-bit) | partial tiles
-  float* sneg = reinterpret_cast<float*>(xs + static_cast<size_t>(nchunk) * NB * 32);
-  f32x4* red = reinterpret_cast<f32x4*>(sneg + (kBiasSums ? ngroups * NB : 0));
+  const int spr = F::kUnitsPerScale > 0 ? (K / F::kUnitElems) / F::kUnitsPerScale : 0;   // scales per row
+  const int nunits = K / F::kUnitElems;
+  const uint32_t xrow = m4_xrow<FMT>(K);
+  // LDS: partial tiles [waves][2][16 lanes] f32x4 | RMSNorm scratch (fused) |
+  //      x [NB][xrow bytes] | -8 * unit sums [nunits][NB] (4-bit)
+  f32x4* part = reinterpret_cast<f32x4*>(lds_v4);
+  float* scr = reinterpret_cast<float*>(part + nw * 2 * 16);
+  char* xs = reinterpret_cast<char*>(scr) + (FUSED ? kNormScratchBytes : 0);
+  float* sneg = reinterpret_cast<float*>(xs + static_cast<size_t>(NB) * xrow);
 
-  const uint32_t woff = i * row_bytes + 16 * q;
-  const uint32_t soff = i * ngroups * 2;
-  // Scales: lane l loads dword l % kSW of row l / kSW of the step's
-  // 16 x kSW-dword block (one coalesced load), and the lanes of a row fetch
-  // their dwords from those lanes (ds_bpermute). Loading each row's dwords in
-  // every lane of the row instead repeats every address 4 times across the
-  // wave, which measured 20 % slower on the int8 LM head.
-  constexpr bool kScaleShfl = QGEMV_MFMA_SCALE_SHFL && F::kGroups > 0 && kSW <= 4;
-  const uint32_t soff_lin = lane < 16 * kSW ? (lane / kSW) * ngroups * 2 + 4 * (lane % kSW) : 0x80000000u;
-  constexpr int kSR = kScaleShfl ? 1 : kSW;            // scale registers per buffer
-
-  u32x4 wa[F::kSlices], wb[F::kSlices];
-  uint32_t sa[kSR], sb[kSR];
-
-  // loads of step s (of this wave's range) of the tile of unit g0 + n;
-  // rows past M, and units past g1, read as zero
-  // buffer resources of the tile of unit g0 + rn (recomputed when the tile changes)
-  int rn = -1;
+  // Loads of one step: the tile's buffer resources are rebuilt when the tile
+  // changes; a step past the wave's share uses resources of zero range, so
+  // its loads read zero and move no data.
+  int rkey = -1;
   __amdgpu_buffer_rsrc_t rw = make_rsrc(W, 0), rs = make_rsrc(S, 0);
-  auto load = [&](u32x4 (&w)[F::kSlices], uint32_t (&s)[kSR], int n, int st_local) {
-    if (n != rn) {
-      rn = n;
-      const int tile = (g0 + n) * TW + tg;
-      const int row0 = tile * 16;
-      // (written as a select and a min: a clamp would be selected as a
-      // vector med3, and a buffer resource built from a vector register is
-      // looped over lanes)
-      const int rows = (n < iters && row0 < M) ? min(16, M - row0) : 0;
+  const uint32_t woff = lj * row_bytes + 16 * lb;
+  auto load = [&](u32x4 (&w)[R], uint32_t (&s)[R], int tile, int st, bool live) {
+    const int key = live ? tile : -2;
+    if (key != rkey) {
+      rkey = key;
+      const int row0 = tile * kTR;
+      // (a select and a min rather than a clamp: see the register-x kernel)
+      const int rows = (live && row0 < M) ? min(kTR, M - row0) : 0;
       rw = make_rsrc(W + (rows ? static_cast<size_t>(row0) * row_bytes : 0), static_cast<uint32_t>(rows) * row_bytes);
-      if constexpr (F::kGroups > 0)
-        rs = make_rsrc(S + (rows ? static_cast<size_t>(row0) * ngroups : 0), static_cast<uint32_t>(rows * ngroups * 2));
+      if constexpr (kScaled)
+        rs = make_rsrc(S + (rows ? static_cast<size_t>(row0) * spr : 0), static_cast<uint32_t>(rows * spr * 2));
     }
-    const int st = ks * Lw + st_local;
-    // The lane's offset (row i, byte 16q) is the VGPR offset, which the
-    // range check covers: rows past M read as zero. The step's offset along
-    // the row is the SGPR offset (not range checked, always inside the row),
-    // so no vector register is computed here.
-    const int so = st * (F::kSlices * 64);
+    // row lj of each row group, unit lb of the step: the VGPR offset (range
+    // checked: rows past M read as zero); the step's offset in the SGPR offset
+    const int so = st * (16 * 16);
 #pragma unroll
-    for (int l = 0; l < F::kSlices; ++l)
-      w[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 64 * l, so, kWeightAux));
-    if constexpr (F::kGroups > 0) {
-      const int sso = st * (F::kGroups * 2);
-      static_assert(kSW == 2 || kSW % 4 == 0, "scale dwords per step");
-      if constexpr (kScaleShfl) {
-        // one dword per lane, consecutive lanes on consecutive addresses;
-        // lanes past the tile's 16 x kSW dwords read out of range (zero)
-        s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff_lin, sso, 0);
-      } else if constexpr (kSW % 4 == 0) {
+    for (int g = 0; g < R; ++g)
+      w[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 4 * g * row_bytes, so, kWeightAux));
+    if constexpr (kScaled) {
+      const int sidx = (st * 16 + lb) / F::kUnitsPerScale;
 #pragma unroll
-        for (int u = 0; u < kSW / 4; ++u) {
-          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, soff + 16 * u, sso, 0));
-          s[4 * u] = v.x; s[4 * u + 1] = v.y; s[4 * u + 2] = v.z; s[4 * u + 3] = v.w;
-        }
-      } else {
-        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff, sso, 0));
-        s[0] = v.x; s[1] = v.y;
-      }
+      for (int g = 0; g < R; ++g)
+        s[g] = __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<uint32_t>(((4 * g + lj) * spr + sidx) * 2), 0, 0);
     }
   };
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  // per step: one D tile per scale group (all of them issued before any is scaled)
-  constexpr int kDch = F::kGroups > 0 ? F::kGroups : 1;
-  auto compute = [&](const u32x4 (&w)[F::kSlices], const uint32_t (&sr)[kSR], int st_local,
-                     f32x4& acc, f32x4& bacc) {
-    const int st = ks * Lw + st_local;
-    const int c0 = st * kChunks;
-    f32x4 dch[kDch];
-    uint32_t s[kSW];
-    if constexpr (kScaleShfl) {
+  f32x4 tot[R][NBh];                                   // running sums of this tile
 #pragma unroll
-      for (int k = 0; k < kSW; ++k) s[k] = __shfl(sr[0], i * kSW + k);
-    } else {
+  for (int g = 0; g < R; ++g)
 #pragma unroll
-      for (int k = 0; k < kSW; ++k) s[k] = sr[k];
+    for (int h = 0; h < NBh; ++h) tot[g][h] = zero;
+
+  auto compute = [&](const u32x4 (&w)[R], const uint32_t (&s)[R], int st) {
+    const int u = st * 16 + lb;                        // this lane group's unit
+    f32x4 d[R][NBh];
+    f32x4 c0[NBh];
+#pragma unroll
+    for (int h = 0; h < NBh; ++h) {
+      if constexpr (F::kBias) c0[h] = *reinterpret_cast<const f32x4*>(sneg + u * NB + 4 * h);
+      else c0[h] = zero;
     }
 #pragma unroll
-    for (int l = 0; l < F::kSlices; ++l) {
-      uint32_t r[4] = {w[l].x, w[l].y, w[l].z, w[l].w};
-#if QGEMV_MFMA_COPY_BEFORE_SWAP
-      if constexpr (FMT != QGEMV_BF16) {
-        // The swaps below overwrite both of their registers. Swapping copies
-        // leaves the loaded registers untouched, so they stay where the next
-        // prefetch into this buffer puts them (otherwise the register
-        // allocator may rotate them and have to copy in-flight load results,
-        // which waits for the prefetch).
+    for (int g = 0; g < R; ++g)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(r[k]) : "v"(r[k]));
-      }
-#endif
-      if constexpr (is_int8_fmt(FMT)) {
-        swap32(r[0], r[2]);
-        swap32(r[1], r[3]);
-      } else if constexpr (FMT != QGEMV_BF16) {
-        swap32(r[0], r[2]);
-        swap32(r[1], r[3]);
-        swap16(r[0], r[1]);
-        swap16(r[2], r[3]);
-      }
-      f32x4 dg = zero;
+      for (int h = 0; h < NBh; ++h) d[g][h] = kScaled ? c0[h] : tot[g][h];
 #pragma unroll
-      for (int ch = 0; ch < kCPS; ++ch) {
-        const int c = c0 + l * kCPS + ch;
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4*>(xs + (static_cast<size_t>(c) * NB + bcl) * 32 + 8 * q));
-        if constexpr (FMT == QGEMV_BF16) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, w[l]), acc, 0, 0, 0);
-        } else if constexpr (FMT == QGEMV_INT8_ROW) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), acc, 0, 0, 0);
-        } else if constexpr (FMT == QGEMV_INT4_G64) {
-          // two chunks per group: the second accumulates onto the first
-          const int gi = (l * kCPS + ch) >> 1;
-          dch[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), (ch & 1) ? dch[gi] : zero, 0, 0, 0);
-        } else if constexpr (FMT == QGEMV_INT8_G32) {
-          dch[l * kCPS + ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int8_to_b(r[2 * ch], r[2 * ch + 1]), zero, 0, 0, 0);
-        } else if constexpr (FMT == QGEMV_Q4_0_G32) {
-          dch[l * kCPS + ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), zero, 0, 0, 0);
-        } else {
-          dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, nibbles_to_b(r[ch]), dg, 0, 0, 0);
-        }
-      }
-      if constexpr (FMT == QGEMV_INT4_G128) dch[l] = dg;
-    }
-    // group scales, applied after all of the step's matrix instructions are
-    // issued (each scale FMA waits for its MFMA's result; interleaving them
-    // stalls on every chunk)
-    if constexpr (F::kGroups > 0) {
+    for (int sub = 0; sub < F::kSub; ++sub) {
+      const uint32_t xo = m4_xoff(m4_elem<FMT>(u, sub));
+      v4i16 a[NBh];
 #pragma unroll
-      for (int g = 0; g < kDch; ++g) {
-        const float sc = scale_of(s, g);
+      for (int h = 0; h < NBh; ++h)
+        a[h] = __builtin_bit_cast(v4i16, *reinterpret_cast<const u32x2*>(xs + (4 * h + lj) * xrow + xo));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(sc, dch[g][j], acc[j]);
+      for (int g = 0; g < R; ++g) {
+        const v4i16 bv = m4_b<FMT>(w[g], sub);
+#pragma unroll
+        for (int h = 0; h < NBh; ++h) d[g][h] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a[h], bv, d[g][h], 0, 0, 0);
       }
     }
-    if constexpr (kBiasSums) {
-      // bias term: D[b][i] += sum over 4 groups of (-8 sum_g x_b) * d_ig;
-      // A lane (b, q) supplies group q's x sum, B lane (i, q) group q's scale
 #pragma unroll
-      for (int h = 0; h < F::kGroups / 4; ++h) {
-        const float av = sneg[(st * F::kGroups + 4 * h + q) * NB + bcl];
-        const uint32_t sw = (q >> 1) ? s[2 * h + 1] : s[2 * h];
-        const float bv = half_to_float(static_cast<uint16_t>(sw >> (16 * (q & 1))));
-        bacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, bacc, 0, 0, 0);
+    for (int g = 0; g < R; ++g) {
+      if constexpr (kScaled) {
+        const float sc = half_to_float(static_cast<uint16_t>(s[g]));
+#pragma unroll
+        for (int h = 0; h < NBh; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tot[g][h][r] = __builtin_fmaf(sc, d[g][h][r], tot[g][h][r]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < NBh; ++h) tot[g][h] = d[g][h];
       }
     }
   };
 
-  // D tile -> y: lane (i, q) holds batch rows 4q..4q+3 of row i of the tile
-  // (the paired row of a gate/up pair is in lane i ^ 1, same q)
-  auto store = [&](const f32x4& v_in, int n) {
-    const int tile = (g0 + n) * TW + tg;
-    const int row = tile * 16 + i;
-    f32x4 v = v_in;
+  // The tile's sums added over the 16 lane groups: value v = 4 (g * NBh + h)
+  // + r goes through two halvings (v bit 0 <-> lane bit 5, v bit 1 <-> lane
+  // bit 4), then rotations by 8 and 4 inside each 16-lane row; afterwards
+  // register n of every lane holds the total of v = 4n + 2 (lane bit 4) +
+  // (lane bit 5), for weight row 4 (v >> 2) / NBh + (lane & 3).
+  auto reduce = [&]() {
+    float t[kV];
+#pragma unroll
+    for (int g = 0; g < R; ++g)
+#pragma unroll
+      for (int h = 0; h < NBh; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[(g * NBh + h) * 4 + r] = tot[g][h][r];
+    float u8[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) u8[m] = halve32(t[2 * m], t[2 * m + 1]);
+    f32x4 q;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) q[n] = halve16(u8[2 * n], u8[2 * n + 1]);
+    const f32x4 q8 = dpp4<kDppRowRor8>(q);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) q[n] += q8[n];
+    const f32x4 q4 = dpp4<kDppRowRor4>(q);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) q[n] += q4[n];
+#pragma unroll
+    for (int g = 0; g < R; ++g)
+#pragma unroll
+      for (int h = 0; h < NBh; ++h) tot[g][h] = zero;
+    return q;
+  };
+
+  // results -> y (lanes whose bits 3, 2 are 0 store; the row paired with row
+  // 2i of a gate/up pair is in the lane next to it)
+  const int vlo = 2 * ((lane >> 4) & 1) + ((lane >> 5) & 1);
+  auto store = [&](const f32x4& q_in, int tile) {
+    f32x4 q = q_in;
     if constexpr (FMT == QGEMV_INT8_ROW) {
-      // the row's scale, applied once to the finished dot products
-      const float d = half_to_float(S[min(row, M - 1)]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] *= d;
+      for (int n = 0; n < 4; ++n) {
+        const int v = 4 * n + vlo;
+        const int row = tile * kTR + 4 * ((v >> 2) / NBh) + lj;
+        q[n] *= half_to_float(S[min(row, M - 1)]);     // the row's scale, once per dot product
+      }
     }
+    f32x4 pq = q;
     if constexpr (FUSED) {
-      f32x4 pv = v;
-      if (fu.epi == kEpiSwiglu) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pv[j] = __shfl_xor(v[j], 1);
-      }
-      if (row < M) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int b = 4 * q + j;
-          if (b < batch) epi_store(fu, Y, M, b, row, v[j], pv[j]);
-        }
-      }
-      return;
+      if (fu.epi == kEpiSwiglu) pq = dpp4<kDppXor1>(q);
     }
-    if (row < M) {
+    if (((lane >> 2) & 3) == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int b = 4 * q + j;
-        if (b < batch) Y[static_cast<size_t>(b) * M + row] = v[j];
+      for (int n = 0; n < 4; ++n) {
+        const int v = 4 * n + vlo;
+        const int b = 4 * ((v >> 2) % NBh) + (v & 3);
+        const int row = tile * kTR + 4 * ((v >> 2) / NBh) + lj;
+        if (row < M && b < batch) {
+          if constexpr (FUSED) epi_store(fu, Y, M, b, row, q[n], pq[n]);
+          else Y[static_cast<size_t>(b) * M + row] = q[n];
+        }
       }
     }
   };
-  int par = 0;
-  auto finish = [&](int n, f32x4& acc, f32x4& bacc) {
-    f32x4 t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t[j] = acc[j] + bacc[j];
-    acc = zero;
-    bacc = zero;
-    if (KS == 1) {
-      store(t, n);
-    } else {
-      f32x4* slot = red + static_cast<size_t>((par * TW + tg) * KS) * kOutLanes;
-      if (lane < kOutLanes) slot[ks * kOutLanes + lane] = t;
-      __syncthreads();
-      if (ks == 0 && lane < kOutLanes) {
-        f32x4 sum = slot[lane];
-        for (int k2 = 1; k2 < KS; ++k2) {
-          const f32x4 o = slot[k2 * kOutLanes + lane];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sum[j] += o[j];
-        }
-        store(sum, n);
+  const int pslot = ((lane >> 4) << 2) | lj;           // lanes with bits 3, 2 = 0 -> 0..15
+
+  // the wave's share [va, vb) of the (tile, step) sequence
+  const int tfirst = t0 + va / nst;
+  int lt = tfirst, ls = va - (va / nst) * nst, lv = va;
+  int ct = lt, cs = ls, cv = va;
+  auto issue = [&](u32x4 (&w)[R], uint32_t (&s)[R]) {
+    load(w, s, lt, ls, lv < vb);
+    if (++ls == nst) { ls = 0; ++lt; }
+    ++lv;
+  };
+  auto step = [&](const u32x4 (&w)[R], const uint32_t (&s)[R]) {
+    compute(w, s, cs);
+    if (cs == nst - 1 || cv == vb - 1) {
+      const f32x4 q = reduce();
+      const int fstart = (ct - t0) * nst;              // the tile's first flattened step
+      if (fstart >= va && fstart + nst <= vb) {
+        store(q, ct);                                  // the whole tile is this wave's
+      } else if (((lane >> 2) & 3) == 0) {
+        part[(wave * 2 + (ct == tfirst ? 0 : 1)) * 16 + pslot] = q;
       }
-      par ^= 1;
     }
+    if (++cs == nst) { cs = 0; ++ct; }
+    ++cv;
   };
 
-  const int nv = iters * Lw;           // steps of this wave (same for every wave)
-  if (nv > 0) load(wa, sa, 0, 0);
+  // three steps of weights in flight: the first two issued before x is staged
+  u32x4 w0[R], w1[R], w2[R];
+  uint32_t s0[R], s1[R], s2[R];
+  issue(w0, s0);
+  issue(w1, s1);
 
-  // ---- stage x (all K, NB rows; rows >= batch as zero) in chunk order,
-  // four 16-byte slots per thread per round so the loads overlap
-  bool staged = false;
-  if constexpr (FUSED) {
-    if (fu.h != nullptr) {
-      // RMSNorm prologue: the same slots, written from h and g
-      float* scr = reinterpret_cast<float*>(red + (KS > 1 ? 2 * TW * KS * kOutLanes : 0));
-      block_rms_factors<NB>(fu, K, batch, scr);
-      const int nslots = nchunk * NB * 4;
-      const int nt = static_cast<int>(blockDim.x);
-      // rounds of four slots per thread (their loads issued together) while
-      // all four exist, then one slot per round; rows past the batch re-read
-      // the last row (in bounds) and store zero
-      int base = tid;
-      auto round = [&](auto width) {
-        constexpr int kW = decltype(width)::value;
-        f32x4 h0[kW], h1[kW];
-        u32x2 g0[kW], g1[kW];
-        float r[kW];
+  // ---- stage x (all K, NB rows; rows >= batch as zero): 8 elements per
+  // thread per round, two 8-byte LDS stores
+  {
+    const int per_row = K / 8;
+    const int nslots = NB * per_row;
+    const int nt = static_cast<int>(blockDim.x);
+    bool staged = false;
+    if constexpr (FUSED) {
+      if (fu.h != nullptr) {
+        // RMSNorm prologue: x = bf16(h * rms factor * g)
+        block_rms_factors<NB>(fu, K, batch, scr);
+        for (int p = tid; p < nslots; p += nt) {
+          const int r = p / per_row, e = 8 * (p - r * per_row);
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (r < batch) {
+            const float* hr = fu.h + static_cast<size_t>(r) * K + e;
+            const f32x4 h0 = *reinterpret_cast<const f32x4*>(hr);
+            const f32x4 h1 = *reinterpret_cast<const f32x4*>(hr + 4);
+            const u32x4 gg = *reinterpret_cast<const u32x4*>(fu.g + e);
+            const float f = scr[kNormFactorOff + r];
+            v = u32x4{pack_bf16(h0.x * f * bf16_lo(gg.x), h0.y * f * bf16_hi(gg.x)),
+                      pack_bf16(h0.z * f * bf16_lo(gg.y), h0.w * f * bf16_hi(gg.y)),
+                      pack_bf16(h1.x * f * bf16_lo(gg.z), h1.y * f * bf16_hi(gg.z)),
+                      pack_bf16(h1.z * f * bf16_lo(gg.w), h1.w * f * bf16_hi(gg.w))};
+          }
+          char* dst = xs + r * xrow + m4_xoff(e);
+          *reinterpret_cast<u32x2*>(dst) = u32x2{v.x, v.y};
+          *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v.z, v.w};
+        }
+        staged = true;
+      }
+    }
+    if (!staged) {
+      for (int base = tid; base < nslots; base += 4 * nt) {
+        u32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < kW; ++u) {
-          const int sl = base + u * nt;
-          const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
-          const float* hr = fu.h + static_cast<size_t>(min(b, batch - 1)) * K;
-          const int e0 = chunk_elem<FMT>(c, 8 * qq), e1 = chunk_elem<FMT>(c, 8 * qq + 4);
-          h0[u] = *reinterpret_cast<const f32x4*>(hr + e0);
-          h1[u] = *reinterpret_cast<const f32x4*>(hr + e1);
-          g0[u] = *reinterpret_cast<const u32x2*>(fu.g + e0);
-          g1[u] = *reinterpret_cast<const u32x2*>(fu.g + e1);
-          r[u] = b < batch ? scr[kNormFactorOff + b] : -1.f;  // -1: a row past the batch
+        for (int k = 0; k < 4; ++k) {
+          const int p = base + k * nt;
+          const int r = p / per_row, e = 8 * (p - r * per_row);
+          v[k] = u32x4{0u, 0u, 0u, 0u};
+          if (p < nslots && r < batch) v[k] = *reinterpret_cast<const u32x4*>(X + static_cast<size_t>(r) * K + e);
         }
 #pragma unroll
-        for (int u = 0; u < kW; ++u) {
-          const int sl = base + u * nt;
-          {
-            u32x4 v = {pack_bf16(h0[u].x * r[u] * bf16_lo(g0[u].x), h0[u].y * r[u] * bf16_hi(g0[u].x)),
-                             pack_bf16(h0[u].z * r[u] * bf16_lo(g0[u].y), h0[u].w * r[u] * bf16_hi(g0[u].y)),
-                             pack_bf16(h1[u].x * r[u] * bf16_lo(g1[u].x), h1[u].y * r[u] * bf16_hi(g1[u].x)),
-                             pack_bf16(h1[u].z * r[u] * bf16_lo(g1[u].y), h1[u].w * r[u] * bf16_hi(g1[u].y))};
-            if (r[u] < 0.f) v = u32x4{0u, 0u, 0u, 0u};
-            reinterpret_cast<u32x4*>(xs)[sl] = v;
+        for (int k = 0; k < 4; ++k) {
+          const int p = base + k * nt;
+          if (p < nslots) {
+            const int r = p / per_row, e = 8 * (p - r * per_row);
+            char* dst = xs + r * xrow + m4_xoff(e);
+            *reinterpret_cast<u32x2*>(dst) = u32x2{v[k].x, v[k].y};
+            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v[k].z, v[k].w};
           }
         }
-        base += kW * nt;
-      };
-      while (base + 3 * nt < nslots) round(std::integral_constant<int, 4>{});
-      while (base < nslots) round(std::integral_constant<int, 1>{});
-      staged = true;
-    }
-  }
-  if (!staged) {
-    const int nslots = nchunk * NB * 4;
-    for (int base = tid; base < nslots; base += 4 * static_cast<int>(blockDim.x)) {
-      u32x2 r0[4], r1[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sl = base + u * static_cast<int>(blockDim.x);
-        const int qq = sl & 3, cb = sl >> 2, b = cb % NB, c = cb / NB;
-        r0[u] = u32x2{0u, 0u};
-        r1[u] = u32x2{0u, 0u};
-        if (sl < nslots && b < batch) {
-          const uint16_t* xr = X + static_cast<size_t>(b) * K;
-          r0[u] = *reinterpret_cast<const u32x2*>(xr + chunk_elem<FMT>(c, 8 * qq));
-          r1[u] = *reinterpret_cast<const u32x2*>(xr + chunk_elem<FMT>(c, 8 * qq + 4));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sl = base + u * static_cast<int>(blockDim.x);
-        if (sl < nslots) reinterpret_cast<u32x4*>(xs)[sl] = u32x4{r0[u].x, r0[u].y, r1[u].x, r1[u].y};
       }
     }
   }
   __syncthreads();
-  if constexpr (kBiasSums) {
-    // -8 * (sum of x over each group), per batch row
+  if constexpr (F::kBias) {
+    // -8 * (sum of x over each unit), per batch row
     constexpr uint32_t kOnes = 0x3f803f80u;
-    for (int e = tid; e < ngroups * NB; e += blockDim.x) {
-      const int g = e / NB, b = e - g * NB;
+    for (int e = tid; e < nunits * NB; e += blockDim.x) {
+      const int u = e / NB, r = e - u * NB;
       float sum = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < F::kChunksPerGroup; ++cc) {
-        const u32x4* row = reinterpret_cast<const u32x4*>(xs + (static_cast<size_t>(g * F::kChunksPerGroup + cc) * NB + b) * 32);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const u32x4 v = row[d];
-          sum = dot2(v.x, kOnes, sum);
-          sum = dot2(v.y, kOnes, sum);
-          sum = dot2(v.z, kOnes, sum);
-          sum = dot2(v.w, kOnes, sum);
-        }
+      for (int sub = 0; sub < F::kSub; ++sub) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(xs + r * xrow + m4_xoff(m4_elem<FMT>(u, sub)));
+        sum = dot2(v.x, kOnes, sum);
+        sum = dot2(v.y, kOnes, sum);
       }
       sneg[e] = -8.f * sum;
     }
     __syncthreads();
   }
 
-  // The next step's loads are issued unconditionally (past the last tile
-  // they address zero rows, read as zero and move no data): with a
-  // conditional issue the compiler could not count outstanding loads and
-  // would wait for all of them, prefetch included, before computing.
-  f32x4 acc = zero, bacc = zero;
-  int n = 0, s = 0;                    // (iteration, step) held in wa/sa
-  for (int v = 0; v < nv; v += 2) {
-    int n1 = n, s1 = s + 1;
-    if (s1 == Lw) { s1 = 0; ++n1; }
-    load(wb, sb, n1, s1);
-    compute(wa, sa, s, acc, bacc);
-    if (s + 1 == Lw) finish(n, acc, bacc);
-    if (v + 1 >= nv) break;
-    int n2 = n1, s2 = s1 + 1;
-    if (s2 == Lw) { s2 = 0; ++n2; }
-    load(wa, sa, n2, s2);
-    compute(wb, sb, s1, acc, bacc);
-    if (s1 + 1 == Lw) finish(n1, acc, bacc);
-    n = n2;
-    s = s2;
+  for (int v = va; v < vb; v += 3) {
+    issue(w2, s2);
+    step(w0, s0);
+    if (v + 1 >= vb) break;
+    issue(w0, s0);
+    step(w1, s1);
+    if (v + 2 >= vb) break;
+    issue(w1, s1);
+    step(w2, s2);
+  }
+
+  // ---- tiles split between waves: the wave holding a tile's last step adds
+  // the partial results of every wave holding part of it, in wave order
+  __syncthreads();
+  const int rel = va / nst;                            // the wave's first tile, relative to t0
+  if (va < vb && va != rel * nst && (rel + 1) * nst <= vb) {
+    int wf = wave - 1;                                 // the wave holding the tile's first step
+    while (static_cast<int>(static_cast<long>(wf) * nflat / nw) > rel * nst) --wf;
+    f32x4 sum = zero;
+    if (((lane >> 2) & 3) == 0) {
+      for (int w = wf; w <= wave; ++w) {
+        const int a2 = static_cast<int>(static_cast<long>(w) * nflat / nw);
+        const int b2 = static_cast<int>(static_cast<long>(w + 1) * nflat / nw);
+        if (a2 == b2) continue;                        // a wave with no steps
+        const f32x4 o = part[(w * 2 + (a2 / nst == rel ? 0 : 1)) * 16 + pslot];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) sum[n] += o[n];
+      }
+    }
+    store(sum, t0 + rel);
   }
 }
 
@@ -1929,24 +1817,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 // A table of GEMVs of one format, K and batch. Workgroup w takes the
 // contiguous units [w*units/G, (w+1)*units/G), entry by entry (x is staged
 // again when the entry changes), so most workgroups stage x once.
+// The matrix-core launch: workgroup b belongs to the entry whose
+// [wg0, wg0 + nwg) holds b and takes the b-th of its nwg balanced tile ranges.
 template <int FMT, int NB, int N, bool FUSED = false>
 __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch,
                                                                     const Fusion fu) {
   extern __shared__ u32x4 lds_v4[];
-  const long U = tab.units, G = gridDim.x;
-  const int u0 = static_cast<int>(blockIdx.x * U / G);
-  const int u1 = static_cast<int>((blockIdx.x + 1) * U / G);
-  if (u0 >= u1) return;                          // the whole workgroup (no barrier reached)
+  const int b = static_cast<int>(blockIdx.x);
   int j = 0;
   if constexpr (N > 1) {
-    while (j + 1 < tab.n && u0 >= tab.e[j + 1].ustart) ++j;
+    while (j + 1 < tab.n && b >= tab.e[j + 1].wg0) ++j;
   }
-  for (int u = u0; u < u1; ++j) {
-    const int uend = min(u1, (N > 1 && j + 1 < tab.n) ? tab.e[j + 1].ustart : tab.units);
-    if (u != u0) __syncthreads();                // the previous entry's LDS is no longer read
-    mfma_units<FMT, NB, FUSED>(tab.e[j], u - tab.e[j].ustart, uend - tab.e[j].ustart, batch, tab.KS, lds_v4, fu);
-    u = uend;
-  }
+  const MfmaEntry& ent = tab.e[j];
+  const long tiles = (ent.M + kMfmaTileRows<NB> - 1) / kMfmaTileRows<NB>;
+  const int r = b - ent.wg0;
+  const int t0 = static_cast<int>(r * tiles / ent.nwg);
+  const int t1 = static_cast<int>((r + 1) * tiles / ent.nwg);
+  mfma_tiles<FMT, NB, FUSED>(ent, t0, t1, batch, lds_v4, fu);
 }
 
 int round_batch(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
@@ -2102,106 +1989,112 @@ hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n,
 }
 
 // ---- matrix-core kernel: launch plan
+#ifndef QGEMV_MFMA_WAVES
+#define QGEMV_MFMA_WAVES 16                // waves per workgroup (one workgroup per CU)
+#endif
+#ifndef QGEMV_MFMA_STEPS_PER_WG
+#define QGEMV_MFMA_STEPS_PER_WG 128        // (tile, step) pairs worth a workgroup of their own
+#endif
 int mfma_step_elems(int fmt) {
-  return with_fmt(fmt, [](auto F) { return MfmaFmt<decltype(F)::value>::kStepElems; });
+  return with_fmt(fmt, [](auto F) { return M4<decltype(F)::value>::kStepElems; });
 }
 
-size_t mfma_lds_bytes(int fmt, int K, int NB, int KS, int TW) {
-  size_t b = static_cast<size_t>(NB) * K * 2;                       // x
-  if (fmt == QGEMV_Q4_0_G32) b += static_cast<size_t>(K / 32) * NB * 4;   // group sums
-  if (fmt == QGEMV_INT4_G128) b += static_cast<size_t>(K / 128) * NB * 4;
-  if (fmt == QGEMV_INT4_G64) b += static_cast<size_t>(K / 64) * NB * 4;
-  if (KS > 1) b += static_cast<size_t>(2) * TW * KS * (4 * NB) * 16;  // partial tiles
-  return b;
+// LDS of one workgroup: partial tiles of `waves` waves, x of NB rows in the
+// padded layout, and the 4-bit formats' unit sums (extra: the fused
+// prologue's scratch)
+size_t mfma_lds_bytes(int fmt, int K, int NB, int waves, size_t extra) {
+  return with_fmt(fmt, [&](auto F) {
+    constexpr int FMT = decltype(F)::value;
+    size_t b = static_cast<size_t>(waves) * 2 * 16 * 16 + extra;
+    b += static_cast<size_t>(NB) * m4_xrow<FMT>(K);
+    if (M4<FMT>::kBias) b += static_cast<size_t>(K / M4<FMT>::kUnitElems) * NB * 4;
+    return b;
+  });
 }
-
-struct MfmaPlan {
-  int KS = 0, TW = 0, grid = 0;
-  size_t lds = 0;
-};
 
 constexpr size_t kLdsPerCu = 160 * 1024;
 
-// Choose the K split (KS waves per tile, dividing the row's steps) and the
-// tiles per workgroup (TW) that keep the most waves busy on real tiles, up
-// to the target per CU; among equals, the fewest workgroups (each stages x
-// once), then the smallest workgroup.
-bool plan_mfma(int fmt, int M, int K, int batch, int cus, MfmaPlan* out, size_t extra_lds = 0) {
+// Whether the matrix-core kernel takes (fmt, K) at this batch: batch 3..8, K a
+// multiple of one step, x of the compiled batch rows in LDS.
+bool mfma_fits(int fmt, int K, int batch, size_t extra) {
   const int NB = round_batch(batch);
   if (NB < 4) return false;
   const int step = mfma_step_elems(fmt);
-  if (K % step != 0) return false;
-  const int nsteps = K / step;
-  const int ntiles = (M + 15) / 16;
-  long best_score = -1;
-  MfmaPlan best;
-  for (int KS = 1; KS <= 16; ++KS) {
-    if (nsteps % KS != 0) continue;
-    if (QGEMV_MFMA_FORCE_KS && KS != QGEMV_MFMA_FORCE_KS) continue;
-    for (int TW = 1; TW * KS <= 16; TW *= 2) {
-      if (QGEMV_MFMA_FORCE_TW && TW != QGEMV_MFMA_FORCE_TW) continue;
-      const size_t lds = mfma_lds_bytes(fmt, K, NB, KS, TW) + extra_lds;
-      if (lds > kLdsPerCu) continue;
-      const int wg_cu = std::min(static_cast<int>(kLdsPerCu / lds), QGEMV_MFMA_MAX_WAVES_PER_CU / (KS * TW));
-      if (wg_cu < 1) continue;
-      const int wgs_needed = (ntiles + TW - 1) / TW;
-      const int grid = std::max(1, std::min(wgs_needed, cus * wg_cu));
-      const long busy = static_cast<long>(std::min(ntiles, grid * TW)) * KS;
-      const long score = std::min(busy, static_cast<long>(cus) * QGEMV_MFMA_TARGET_WAVES_PER_CU);
-      const bool better = score > best_score ||
-                          (score == best_score && (grid < best.grid ||
-                                                   (grid == best.grid && KS * TW < best.KS * best.TW)));
-      if (better) {
-        best_score = score;
-        best.KS = KS;
-        best.TW = TW;
-        best.grid = grid;
-        best.lds = lds;
-      }
-    }
-  }
-  if (best_score < 0) return false;
-  *out = best;
-  return true;
+  return K % step == 0 && K / step >= 1 && mfma_lds_bytes(fmt, K, NB, QGEMV_MFMA_WAVES, extra) <= kLdsPerCu;
 }
 
-// n GEMVs of one format, K and batch on the matrix cores with plan p (made
-// for their tiles together; one entry for qgemv_run).
-template <int FMT, int NB, int N, bool FUSED = false>
-hipError_t launch_mfma_table(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st,
-                             const Fusion& fu = Fusion{}) {
-  MfmaTable<N> tab{};
-  tab.n = n;
-  tab.KS = p.KS;
-  int u = 0;
-  for (int i = 0; i < n; ++i) {
-    const int tiles = (a[i].M + 15) / 16;
-    tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
-                         a[i].M, a[i].K, u, 0};
-    u += (tiles + p.TW - 1) / p.TW;
+struct MfmaPlan {
+  int grid = 0;
+  size_t lds = 0;
+};
+
+// Workgroups per entry: the launch aims at one workgroup per
+// QGEMV_MFMA_STEPS_PER_WG (tile, step) pairs of work and at least one per CU
+// (or per tile, if fewer), shares them out in proportion to each entry's
+// pairs, at least one and at most one per tile each. Depends on (fmt, M, K)
+// of the entries and the CU count only, not on the batch.
+MfmaPlan plan_mfma(const GemvArgs* a, int n, int cus, int nb, size_t extra, int* nwg) {
+  const int step = mfma_step_elems(a[0].fmt);
+  long total = 0, tiles_all = 0;
+  int kmax = 0;
+  const int tr = nb == 8 ? kMfmaTileRows<8> : kMfmaTileRows<4>;
+  for (int e = 0; e < n; ++e) {
+    const long tiles = (a[e].M + tr - 1) / tr;
+    total += tiles * (a[e].K / step);
+    tiles_all += tiles;
+    kmax = std::max(kmax, a[e].K);
   }
-  tab.units = u;
-  const int grid = std::max(1, std::min(p.grid, u));
+  long target = (total + QGEMV_MFMA_STEPS_PER_WG - 1) / QGEMV_MFMA_STEPS_PER_WG;
+  target = std::max(target, std::min<long>(cus, tiles_all));
+  MfmaPlan p;
+  long grid = 0;
+  for (int e = 0; e < n; ++e) {
+    const long tiles = (a[e].M + tr - 1) / tr;
+    const long pairs = tiles * (a[e].K / step);
+    long g = (target * pairs + total / 2) / std::max<long>(total, 1);
+    g = std::max<long>(1, std::min(g, tiles));
+    nwg[e] = static_cast<int>(g);
+    grid += g;
+  }
+  p.grid = static_cast<int>(grid);
+  p.lds = mfma_lds_bytes(a[0].fmt, kmax, nb, QGEMV_MFMA_WAVES, extra);
+  return p;
+}
+
+// n GEMVs of one format and batch on the matrix cores (one entry for
+// qgemv_run), nb batch rows compiled.
+template <int FMT, int NB, int N, bool FUSED = false>
+hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fusion& fu = Fusion{}) {
+  MfmaTable<N> tab{};
+  int nwg[N];
+  const MfmaPlan p = plan_mfma(a, n, device_cu_count(), NB, FUSED ? kNormScratchBytes : 0, nwg);
+  tab.n = n;
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
+                         a[i].M, a[i].K, wg, nwg[i]};
+    wg += nwg[i];
+  }
   if (p.lds > 64 * 1024) {
     static const hipError_t once = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N, FUSED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
     if (once != hipSuccess) return once;
   }
-  gemv_mfma_kernel<FMT, NB, N, FUSED><<<grid, 64 * p.KS * p.TW, p.lds, st>>>(tab, a[0].batch, fu);
+  gemv_mfma_kernel<FMT, NB, N, FUSED><<<p.grid, 64 * QGEMV_MFMA_WAVES, p.lds, st>>>(tab, a[0].batch, fu);
   return hipGetLastError();
 }
 
 // nb: batch rows the kernel is compiled for (4 or 8; >= batch)
 template <int FMT, int N>
-hipError_t launch_mfma(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st, int nb) {
-  if (nb == 4) return launch_mfma_table<FMT, 4, N>(a, n, p, st);
-  return launch_mfma_table<FMT, 8, N>(a, n, p, st);
+hipError_t launch_mfma(const GemvArgs* a, int n, hipStream_t st, int nb) {
+  if (nb == 4) return launch_mfma_table<FMT, 4, N>(a, n, st);
+  return launch_mfma_table<FMT, 8, N>(a, n, st);
 }
 
 template <int N>
-hipError_t launch_mfma_fmt(const GemvArgs* a, int n, const MfmaPlan& p, hipStream_t st, int nb) {
-  return with_fmt(a[0].fmt, [&](auto F) { return launch_mfma<decltype(F)::value, N>(a, n, p, st, nb); });
+hipError_t launch_mfma_fmt(const GemvArgs* a, int n, hipStream_t st, int nb) {
+  return with_fmt(a[0].fmt, [&](auto F) { return launch_mfma<decltype(F)::value, N>(a, n, st, nb); });
 }
 }  // namespace
 
@@ -2261,8 +2154,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
     const int grid = std::max(1, std::min(wg_needed, cus * QGEMV_MAX_WG_PER_CU));
     return with_fmt(a.fmt, [&](auto F) { return launch_xreg<decltype(F)::value>(a, R, nch, grid, stream); });
   }
-  MfmaPlan plan;
-  if (plan_mfma(a.fmt, a.M, a.K, inv ? 8 : a.batch, cus, &plan)) return launch_mfma_fmt<1>(&a, 1, plan, stream, nb);
+  if (mfma_fits(a.fmt, a.K, inv ? 8 : a.batch, 0)) return launch_mfma_fmt<1>(&a, 1, stream, nb);
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, nb);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
@@ -2295,19 +2187,10 @@ int gemv_group_class(int fmt, int K, int batch) {
 
 int gemv_group_max() { return kGroupMax; }
 
-bool gemv_mfma_groupable(int fmt, int K, int batch) {
-  MfmaPlan p;
-  return plan_mfma(fmt, 16, K, batch, device_cu_count(), &p);
-}
+bool gemv_mfma_groupable(int fmt, int K, int batch) { return mfma_fits(fmt, K, batch, 0); }
 
 hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream) {
-  long rows = 0;
-  for (int i = 0; i < n; ++i) rows += static_cast<long>((a[i].M + 15) / 16) * 16;
-  MfmaPlan plan;
-  if (!plan_mfma(a[0].fmt, static_cast<int>(std::min<long>(rows, 1L << 30)), a[0].K, a[0].batch,
-                 device_cu_count(), &plan))
-    return hipErrorInvalidValue;                   // the caller checked gemv_mfma_groupable
-  return launch_mfma_fmt<kGroupMax>(a, n, plan, stream, round_batch(a[0].batch));
+  return launch_mfma_fmt<kGroupMax>(a, n, stream, round_batch(a[0].batch));
 }
 
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,
@@ -2394,10 +2277,9 @@ hipError_t launch_fused_fmt(const GemvArgs& a, const Fusion& f, uint64_t* slots,
     return launch_fused_xreg_shape<FMT, 2>(a, nch, r4, f, slots, idx, st);
   }
   hipError_t e;
-  MfmaPlan plan;
-  if (plan_mfma(FMT, a.M, a.K, a.batch, cus, &plan, kNormScratchBytes)) {
-    e = nb == 4 ? launch_mfma_table<FMT, 4, 1, true>(&a, 1, plan, st, f)
-                : launch_mfma_table<FMT, 8, 1, true>(&a, 1, plan, st, f);
+  if (mfma_fits(FMT, a.K, a.batch, kNormScratchBytes)) {
+    e = nb == 4 ? launch_mfma_table<FMT, 4, 1, true>(&a, 1, st, f)
+                : launch_mfma_table<FMT, 8, 1, true>(&a, 1, st, f);
   } else {
     const size_t lds = gemv_lds_bytes(FMT, a.K, a.batch) + kNormScratchBytes;
     int R = 4;

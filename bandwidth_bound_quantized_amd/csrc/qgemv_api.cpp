@@ -372,7 +372,7 @@ namespace {
 // computes the argmax of its output if the small-batch kernel takes it
 // (*fused = true), else the caller launches the argmax.
 // launch of qgemv_run_grouped an entry goes to (QGEMV_GROUP_*): the register-x
-// group of its format, the matrix-core group of its format and K, or alone
+// group of its format, the matrix-core group of its format, or alone
 int grouped_kind(int fmt, int K, int batch) {
   return qgemv::gemv_group_class(fmt, K, batch) != 0 ? QGEMV_GROUP_XREG
          : qgemv::gemv_mfma_groupable(fmt, K, batch) ? QGEMV_GROUP_MFMA : QGEMV_GROUP_ALONE;
@@ -382,8 +382,8 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
                      uint64_t* slots, int32_t* idx, bool* fused) {
   // GEMVs the register-x kernel takes are launched together, one launch per
   // format (up to gemv_group_max() entries) in order of first appearance;
-  // so are those the matrix-core kernel takes, one launch per format and K;
-  // the others are launched one by one.
+  // so are those the matrix-core kernel takes, one launch per format (any
+  // mix of K); the others are launched one by one.
   std::vector<qgemv::GemvArgs> todo;
   std::vector<int> ids;
   std::vector<char> done(static_cast<size_t>(n), 0);
@@ -399,8 +399,7 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
     for (int k = i; k < n; ++k) {
       const qgemv_gemv_desc& h = gemvs[k];
       if (done[k]) continue;
-      if (cls == QGEMV_GROUP_ALONE ? k != i
-                   : (h.fmt != g.fmt || kind[k] != cls || (cls == QGEMV_GROUP_MFMA && h.K != g.K)))
+      if (cls == QGEMV_GROUP_ALONE ? k != i : (h.fmt != g.fmt || kind[k] != cls))
         continue;
       todo.push_back(qgemv::GemvArgs{h.fmt, h.W, h.scales, h.x, h.y, h.M, h.K, batch});
       ids.push_back(k);
