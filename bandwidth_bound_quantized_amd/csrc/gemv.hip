@@ -1017,10 +1017,38 @@ struct MfmaEntry {
 template <int N>
 struct MfmaTable {
   int n;
-  int pad[3];
+  int am;       // entry whose output's argmax the launch computes (-1: none)
+  int pad[2];
   MfmaEntry e[N];
 };
 
+// Where the matrix-core launch's argmax meets: row b's key of the entry's
+// workgroup w in slots[b * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + w].
+struct MfmaArgmax {
+  uint64_t* slots = nullptr;   // nullptr: this workgroup's entry has no argmax
+  int wg = 0;                  // this workgroup within the entry
+};
+
+// The argmax of a matrix-core launch: idx[b] = the index in the largest of
+// row b's nwg keys (nwg <= kMaxArgmaxKeyWords); every key word is cleared
+// again. One wave per batch row, all of a lane's loads issued together.
+constexpr int kMaxArgmaxKeyWords = 8 * 64;
+__global__ __launch_bounds__(512) void argmax_keys_kernel(uint64_t* __restrict__ slots, int nwg,
+                                                           int32_t* __restrict__ idx) {
+  const int b = static_cast<int>(threadIdx.x >> 6), lane = static_cast<int>(threadIdx.x & 63);
+  uint64_t* row = slots + static_cast<size_t>(b) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;
+  uint64_t v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < nwg ? row[lane + 64 * u] : uint64_t{0};
+  uint64_t k = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    k = umax64(k, v[u]);
+    if (lane + 64 * u < nwg) row[lane + 64 * u] = 0;
+  }
+  k = wave_umax64(k);
+  if (lane == 0) idx[b] = argmax_index(k);
+}
 constexpr int kNormFactorOff = (kMfmaMaxThreads / 64) * QGEMV_MAX_BATCH;   // floats
 static_assert((kNormFactorOff + QGEMV_MAX_BATCH) * 4 <= static_cast<int>(kNormScratchBytes), "norm scratch");
 
@@ -1281,9 +1309,9 @@ constexpr int kDppRowRor4 = 0x124;    // row_ror:4
 // wave holding the tile's last step adds them in wave order (a fixed order:
 // results are deterministic, and a row's arithmetic does not depend on the
 // batch or on the other rows).
-template <int FMT, int NB, bool FUSED = false>
+template <int FMT, int NB, bool FUSED = false, bool AM = false>
 __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1, int batch,
-                                           u32x4* lds_v4, const Fusion& fu) {
+                                           u32x4* lds_v4, const Fusion& fu, const MfmaArgmax& amx = MfmaArgmax{}) {
   using F = M4<FMT>;
   constexpr int NBh = NB / 4;                          // batch halves of 4 rows
   constexpr int R = NB == 8 ? 2 : 4;                   // row groups of 4 rows per tile
@@ -1433,6 +1461,11 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
   // results -> y (lanes whose bits 3, 2 are 0 store; the row paired with row
   // 2i of a gate/up pair is in the lane next to it)
   const int vlo = 2 * ((lane >> 4) & 1) + ((lane >> 5) & 1);
+  // argmax keys of the outputs this lane stores: batch rows vlo (+ 4)
+  uint64_t amk[NBh];
+#pragma unroll
+  for (int h = 0; h < NBh; ++h) amk[h] = 0;
+  const bool am_on = AM && amx.slots != nullptr;
   auto store = [&](const f32x4& q_in, int tile) {
     f32x4 q = q_in;
     if constexpr (FMT == QGEMV_INT8_ROW) {
@@ -1456,6 +1489,9 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
         if (row < M && b < batch) {
           if constexpr (FUSED) epi_store(fu, Y, M, b, row, q[n], pq[n]);
           else Y[static_cast<size_t>(b) * M + row] = q[n];
+          if constexpr (AM) {
+            if (am_on) amk[n % NBh] = umax64(amk[n % NBh], argmax_key(q[n], static_cast<uint32_t>(row)));
+          }
         }
       }
     }
@@ -1486,11 +1522,13 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
     ++cv;
   };
 
-  // three steps of weights in flight: the first two issued before x is staged
+  // steps of weights in flight: three of 2 KiB per wave (8-row tiles) or two
+  // of 4 KiB (16-row tiles); all but one issued before x is staged
+  constexpr int kDepth = R == 2 ? 3 : 2;
   u32x4 w0[R], w1[R], w2[R];
   uint32_t s0[R], s1[R], s2[R];
   issue(w0, s0);
-  issue(w1, s1);
+  if constexpr (kDepth == 3) issue(w1, s1);
 
   // ---- stage x (all K, NB rows; rows >= batch as zero): 8 elements per
   // thread per round, two 8-byte LDS stores
@@ -1565,15 +1603,25 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
     __syncthreads();
   }
 
-  for (int v = va; v < vb; v += 3) {
-    issue(w2, s2);
-    step(w0, s0);
-    if (v + 1 >= vb) break;
-    issue(w0, s0);
-    step(w1, s1);
-    if (v + 2 >= vb) break;
-    issue(w1, s1);
-    step(w2, s2);
+  if constexpr (kDepth == 3) {
+    for (int v = va; v < vb; v += 3) {
+      issue(w2, s2);
+      step(w0, s0);
+      if (v + 1 >= vb) break;
+      issue(w0, s0);
+      step(w1, s1);
+      if (v + 2 >= vb) break;
+      issue(w1, s1);
+      step(w2, s2);
+    }
+  } else {
+    for (int v = va; v < vb; v += 2) {
+      issue(w1, s1);
+      step(w0, s0);
+      if (v + 1 >= vb) break;
+      issue(w0, s0);
+      step(w1, s1);
+    }
   }
 
   // ---- tiles split between waves: the wave holding a tile's last step adds
@@ -1595,6 +1643,27 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
       }
     }
     store(sum, t0 + rel);
+  }
+
+  if constexpr (AM) {
+    // ---- argmax of the entry's output: the workgroup's largest key per
+    // batch row (waves, then through LDS) goes to its own word of the
+    // caller's workspace; argmax_keys_kernel, launched next, takes the
+    // largest of the words. (A counter that let the last workgroup finish
+    // the argmax made every workgroup queue on one address at the end.)
+    if (!am_on) return;                                // (uniform over the workgroup)
+    uint64_t* wk = reinterpret_cast<uint64_t*>(xs);    // x is no longer read
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint64_t k = wave_umax64(vlo == (b & 3) ? amk[b >> 2] : uint64_t{0});
+      if (lane == 0) wk[wave * NB + b] = k;
+    }
+    __syncthreads();
+    if (tid < NB && tid < batch) {
+      uint64_t k = 0;
+      for (int w = 0; w < nw; ++w) k = umax64(k, wk[w * NB + tid]);
+      amx.slots[static_cast<size_t>(tid) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + amx.wg] = k;
+    }
   }
 }
 
@@ -1819,9 +1888,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 // again when the entry changes), so most workgroups stage x once.
 // The matrix-core launch: workgroup b belongs to the entry whose
 // [wg0, wg0 + nwg) holds b and takes the b-th of its nwg balanced tile ranges.
-template <int FMT, int NB, int N, bool FUSED = false>
+template <int FMT, int NB, int N, bool FUSED = false, bool AM = false>
 __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch,
-                                                                    const Fusion fu) {
+                                                                    const Fusion fu, uint64_t* am_slots) {
   extern __shared__ u32x4 lds_v4[];
   const int b = static_cast<int>(blockIdx.x);
   int j = 0;
@@ -1833,7 +1902,12 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTa
   const int r = b - ent.wg0;
   const int t0 = static_cast<int>(r * tiles / ent.nwg);
   const int t1 = static_cast<int>((r + 1) * tiles / ent.nwg);
-  mfma_tiles<FMT, NB, FUSED>(ent, t0, t1, batch, lds_v4, fu);
+  MfmaArgmax amx;
+  if (AM && j == tab.am) {
+    amx.slots = am_slots;
+    amx.wg = r;
+  }
+  mfma_tiles<FMT, NB, FUSED, AM>(ent, t0, t1, batch, lds_v4, fu, amx);
 }
 
 int round_batch(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
@@ -1989,12 +2063,6 @@ hipError_t launch_group1(const GemvArgs* a, const int* R, const int* nch, int n,
 }
 
 // ---- matrix-core kernel: launch plan
-#ifndef QGEMV_MFMA_WAVES
-#define QGEMV_MFMA_WAVES 16                // waves per workgroup (one workgroup per CU)
-#endif
-#ifndef QGEMV_MFMA_STEPS_PER_WG
-#define QGEMV_MFMA_STEPS_PER_WG 128        // (tile, step) pairs worth a workgroup of their own
-#endif
 int mfma_step_elems(int fmt) {
   return with_fmt(fmt, [](auto F) { return M4<decltype(F)::value>::kStepElems; });
 }
@@ -2020,55 +2088,80 @@ bool mfma_fits(int fmt, int K, int batch, size_t extra) {
   const int NB = round_batch(batch);
   if (NB < 4) return false;
   const int step = mfma_step_elems(fmt);
-  return K % step == 0 && K / step >= 1 && mfma_lds_bytes(fmt, K, NB, QGEMV_MFMA_WAVES, extra) <= kLdsPerCu;
+  return K % step == 0 && K / step >= 1 && mfma_lds_bytes(fmt, K, NB, 16, extra) <= kLdsPerCu;
 }
 
 struct MfmaPlan {
   int grid = 0;
+  int waves = 16;
   size_t lds = 0;
 };
 
-// Workgroups per entry: the launch aims at one workgroup per
-// QGEMV_MFMA_STEPS_PER_WG (tile, step) pairs of work and at least one per CU
-// (or per tile, if fewer), shares them out in proportion to each entry's
-// pairs, at least one and at most one per tile each. Depends on (fmt, M, K)
-// of the entries and the CU count only, not on the batch.
+// Launch shape and workgroups per entry. Workgroups of 8 waves, two per CU,
+// where two fit in LDS (a workgroup's x staging and start-up then overlap
+// the other's streaming), else 16 waves, one per CU; one round of
+// workgroups, so that no CU waits for a second round. Every entry gets one
+// workgroup, the rest go one at a time to the entry with the most (tile,
+// step) pairs per workgroup, never more than one per tile. Depends on (fmt,
+// M, K) of the entries and the CU count only, not on the batch.
 MfmaPlan plan_mfma(const GemvArgs* a, int n, int cus, int nb, size_t extra, int* nwg) {
   const int step = mfma_step_elems(a[0].fmt);
+  const int tr = nb == 8 ? kMfmaTileRows<8> : kMfmaTileRows<4>;
   long total = 0, tiles_all = 0;
   int kmax = 0;
-  const int tr = nb == 8 ? kMfmaTileRows<8> : kMfmaTileRows<4>;
+  long pairs[kGroupMax], tiles[kGroupMax];
   for (int e = 0; e < n; ++e) {
-    const long tiles = (a[e].M + tr - 1) / tr;
-    total += tiles * (a[e].K / step);
-    tiles_all += tiles;
+    tiles[e] = (a[e].M + tr - 1) / tr;
+    pairs[e] = tiles[e] * (a[e].K / step);
+    total += pairs[e];
+    tiles_all += tiles[e];
     kmax = std::max(kmax, a[e].K);
   }
-  long target = (total + QGEMV_MFMA_STEPS_PER_WG - 1) / QGEMV_MFMA_STEPS_PER_WG;
-  target = std::max(target, std::min<long>(cus, tiles_all));
   MfmaPlan p;
+  p.waves = 8;
+  p.lds = mfma_lds_bytes(a[0].fmt, kmax, nb, 8, extra);
+  int per_cu = 2;
+  if (2 * p.lds > kLdsPerCu) {
+    p.waves = 16;
+    p.lds = mfma_lds_bytes(a[0].fmt, kmax, nb, 16, extra);
+    per_cu = 1;
+  }
+  // (at most kMaxArgmaxKeyWords workgroups: an argmax entry's keys fit argmax_keys_kernel)
+  const long target = std::max<long>(
+      std::min<long>({static_cast<long>(cus) * per_cu, tiles_all, static_cast<long>(kMaxArgmaxKeyWords)}), n);
+  // a proportional start (every entry at least one, at most one per tile),
+  // then the remainder one at a time
   long grid = 0;
   for (int e = 0; e < n; ++e) {
-    const long tiles = (a[e].M + tr - 1) / tr;
-    const long pairs = tiles * (a[e].K / step);
-    long g = (target * pairs + total / 2) / std::max<long>(total, 1);
-    g = std::max<long>(1, std::min(g, tiles));
-    nwg[e] = static_cast<int>(g);
-    grid += g;
+    nwg[e] = static_cast<int>(std::max<long>(1, std::min(tiles[e], target * pairs[e] / std::max<long>(total, 1))));
+    grid += nwg[e];
+  }
+  while (grid < target) {
+    int best = -1;
+    for (int e = 0; e < n; ++e) {
+      if (nwg[e] >= tiles[e]) continue;
+      // the entry whose workgroups have the most pairs each (compared exactly)
+      if (best < 0 || pairs[e] * nwg[best] > pairs[best] * nwg[e]) best = e;
+    }
+    if (best < 0) break;
+    ++nwg[best];
+    ++grid;
   }
   p.grid = static_cast<int>(grid);
-  p.lds = mfma_lds_bytes(a[0].fmt, kmax, nb, QGEMV_MFMA_WAVES, extra);
   return p;
 }
 
 // n GEMVs of one format and batch on the matrix cores (one entry for
-// qgemv_run), nb batch rows compiled.
-template <int FMT, int NB, int N, bool FUSED = false>
-hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fusion& fu = Fusion{}) {
+// qgemv_run), NB batch rows compiled; am >= 0: also the argmax of entry am's
+// output into idx (slots: zero on entry, zero on exit).
+template <int FMT, int NB, int N, bool FUSED = false, bool AM = false>
+hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fusion& fu = Fusion{},
+                             int am = -1, uint64_t* slots = nullptr, int32_t* idx = nullptr) {
   MfmaTable<N> tab{};
   int nwg[N];
   const MfmaPlan p = plan_mfma(a, n, device_cu_count(), NB, FUSED ? kNormScratchBytes : 0, nwg);
   tab.n = n;
+  tab.am = am;
   int wg = 0;
   for (int i = 0; i < n; ++i) {
     tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
@@ -2077,24 +2170,34 @@ hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fus
   }
   if (p.lds > 64 * 1024) {
     static const hipError_t once = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N, FUSED>),
+        reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, NB, N, FUSED, AM>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
     if (once != hipSuccess) return once;
   }
-  gemv_mfma_kernel<FMT, NB, N, FUSED><<<p.grid, 64 * QGEMV_MFMA_WAVES, p.lds, st>>>(tab, a[0].batch, fu);
+  gemv_mfma_kernel<FMT, NB, N, FUSED, AM><<<p.grid, 64 * p.waves, p.lds, st>>>(tab, a[0].batch, fu, slots);
+  if (AM) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    argmax_keys_kernel<<<1, 64 * a[0].batch, 0, st>>>(slots, nwg[am], idx);
+  }
   return hipGetLastError();
 }
 
 // nb: batch rows the kernel is compiled for (4 or 8; >= batch)
 template <int FMT, int N>
-hipError_t launch_mfma(const GemvArgs* a, int n, hipStream_t st, int nb) {
+hipError_t launch_mfma(const GemvArgs* a, int n, hipStream_t st, int nb, int am, uint64_t* slots, int32_t* idx) {
+  if (am >= 0) {
+    if (nb == 4) return launch_mfma_table<FMT, 4, N, false, true>(a, n, st, Fusion{}, am, slots, idx);
+    return launch_mfma_table<FMT, 8, N, false, true>(a, n, st, Fusion{}, am, slots, idx);
+  }
   if (nb == 4) return launch_mfma_table<FMT, 4, N>(a, n, st);
   return launch_mfma_table<FMT, 8, N>(a, n, st);
 }
 
 template <int N>
-hipError_t launch_mfma_fmt(const GemvArgs* a, int n, hipStream_t st, int nb) {
-  return with_fmt(a[0].fmt, [&](auto F) { return launch_mfma<decltype(F)::value, N>(a, n, st, nb); });
+hipError_t launch_mfma_fmt(const GemvArgs* a, int n, hipStream_t st, int nb, int am = -1,
+                           uint64_t* slots = nullptr, int32_t* idx = nullptr) {
+  return with_fmt(a[0].fmt, [&](auto F) { return launch_mfma<decltype(F)::value, N>(a, n, st, nb, am, slots, idx); });
 }
 }  // namespace
 
@@ -2189,8 +2292,9 @@ int gemv_group_max() { return kGroupMax; }
 
 bool gemv_mfma_groupable(int fmt, int K, int batch) { return mfma_fits(fmt, K, batch, 0); }
 
-hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream) {
-  return launch_mfma_fmt<kGroupMax>(a, n, stream, round_batch(a[0].batch));
+hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,
+                                  int32_t* idx) {
+  return launch_mfma_fmt<kGroupMax>(a, n, stream, round_batch(a[0].batch), am, slots, idx);
 }
 
 hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int am, uint64_t* slots,

@@ -412,7 +412,11 @@ int run_grouped_impl(const qgemv_gemv_desc* gemvs, int n, int batch, hipStream_t
       if (cls == QGEMV_GROUP_ALONE) {
         e = qgemv::launch_gemv(todo[off], s);
       } else if (cls == QGEMV_GROUP_MFMA) {
-        e = qgemv::launch_gemv_mfma_group(&todo[off], cnt, s);
+        int local_am = -1;
+        for (int t = 0; t < cnt; ++t)
+          if (ids[off + t] == am) local_am = t;
+        e = qgemv::launch_gemv_mfma_group(&todo[off], cnt, s, local_am, slots, idx);
+        if (local_am >= 0 && fused) *fused = true;
       } else {
         int local_am = -1;
         for (int t = 0; t < cnt; ++t)

@@ -85,10 +85,13 @@ hipError_t launch_gemv_group(const GemvArgs* a, int n, hipStream_t stream, int a
 
 // Grouped launches on the matrix cores (batch 3..8): whether qgemv_run runs
 // a GEMV of this (fmt, K, batch) on the matrix-core kernel; GEMVs of one
-// format, K and batch for which it does can share a launch
+// format and batch for which it does can share a launch, whatever their K
 // (n <= gemv_group_max(), already validated).
+// am >= 0: the launch also writes idx[b] = argmax of row b of a[am].y (slots as
+// for launch_gemv_group: zero on entry, zero on exit).
 bool gemv_mfma_groupable(int fmt, int K, int batch);
-hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream);
+hipError_t launch_gemv_mfma_group(const GemvArgs* a, int n, hipStream_t stream, int am = -1,
+                                  uint64_t* slots = nullptr, int32_t* idx = nullptr);
 
 // Launch the argmax (one kernel). ws: batch * 2 u64 words, zero on entry.
 hipError_t launch_argmax(const float* logits, int64_t V, int batch, uint64_t* ws, int32_t* idx,

@@ -206,10 +206,11 @@ typedef struct {
  * Entries of one format that the small-batch kernel handles (batch <= 2 and
  * at most 256 16-byte units per row: K <= 2048 bf16, 4096 int8, 8192 4-bit;
  * int8 at batch 1 up to 512 units, K <= 8192) share launches (one per format, up to 64 entries each), and so do entries
- * of one format and K that the matrix-core kernel handles (batch 3..8, K a
- * multiple of 256 for Q4_0 and int4-g64, 128 for int8 and bf16, 512 for int4-g128, x in
- * LDS), so the per-launch start-up cost is paid once per group instead of
- * once per GEMV; other entries are launched one by one. All validation
+ * of one format that the matrix-core kernel handles, whatever their K
+ * (batch 3..8, K a multiple of 512 for the 4-bit formats, 256 for int8, 128
+ * for bf16, x of 8 (batch 5..8) or 4 rows in LDS), so the per-launch
+ * start-up cost is paid once per group instead of once per GEMV; other
+ * entries are launched one by one. All validation
  * happens before anything is launched. Errors as qgemv_run; ESHAPE also
  * for n > QGEMV_GROUP_MAX.
  */
@@ -295,6 +296,11 @@ int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx
  * does no GEMV work, collects the words while the other entries still
  * stream and takes the largest; no separate launch and no second pass over
  * the logits.
+ * When the matrix-core kernel computes it (batch 3..8), each of the entry's
+ * workgroups folds the logits it writes into one key per batch row and
+ * stores it in its own word of ws, and a one-workgroup kernel launched next
+ * takes the largest of those words and clears them (a second launch of a
+ * few hundred words, no second pass over the logits).
  * Otherwise the argmax is a qgemv_argmax launch after the GEMVs, on the same
  * stream, with the same ws. The logits (gemvs[argmax_entry].y) are written
  * in full either way.
