@@ -219,7 +219,7 @@ int qgemv_run_grouped(const qgemv_gemv_desc* gemvs, int n, int batch, void* stre
 /* launches of qgemv_run_grouped (qgemv_grouped_class) */
 #define QGEMV_GROUP_ALONE 0   /* a launch of its own */
 #define QGEMV_GROUP_XREG 1    /* the small-batch launch of its format */
-#define QGEMV_GROUP_MFMA 2    /* the matrix-core launch of its format and K */
+#define QGEMV_GROUP_MFMA 2    /* the matrix-core launch of its format */
 
 /*
  * qgemv_grouped_class - which launch qgemv_run_grouped (and

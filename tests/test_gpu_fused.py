@@ -173,11 +173,9 @@ def test_fused_lm_head_norm_argmax(fmt, M, K, B):
         out = c.run(norm=True, argmax=True)
         assert out["ws_zero"]
         assert (out["idx"] == oracle.argmax_ref(out["y"])).all(), rep
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
-                                     np.random.default_rng(0).choice(M, 512, replace=False)]))
     xb = ofused.rmsnorm_bf16(c.h, c.g, EPS)
-    y_ref, a_ref = oracle.gemv_ref(fmt, c.w, c.s, xb, M, K, rows=rows)
-    _parity(out["y"][:, rows], y_ref, a_ref, "lm head")
+    y_ref, a_ref = oracle.gemv_ref(fmt, c.w, c.s, xb, M, K)
+    _parity(out["y"], y_ref, a_ref, "lm head")
 
 
 def test_fused_norm_constant_rows_exact():
