@@ -849,13 +849,13 @@ __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, 
   for (int b = 0; b < batch; ++b) {
     uint64_t* row = slots + static_cast<size_t>(b) * kFusedSlots;
     uint64_t key = 1;
-    bool pending = false;
+    bool gave_up = false;          // a bounded wait ran out: the rest is read once, not waited for
     for (int k0 = 0; k0 < kFusedPerThread && k0 * kThreads < grid; k0 += kFusedChunk) {
       uint64_t v[kFusedChunk];
 #pragma unroll
       for (int k = 0; k < kFusedChunk; ++k) v[k] = 0;
-      pending = true;
-      for (int spin = 0; pending && spin < kFusedSpinLimit; ++spin) {
+      bool pending = true;
+      for (int spin = 0; pending && spin < (gave_up ? 1 : kFusedSpinLimit); ++spin) {
 #pragma unroll
         for (int k = 0; k < kFusedChunk; ++k) {
           const int w = tid + (k0 + k) * kThreads;
@@ -874,12 +874,15 @@ __device__ __forceinline__ void fused_argmax_tail(uint64_t* __restrict__ slots, 
           __hip_atomic_store(row + w, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      if (pending) break;                                // bounded wait ran out: idx -1
+      // (every slot of every chunk is cleared, arrived or not; after a
+      // timeout, idx is -1, and a wave that publishes later still leaves its
+      // word behind: the caller zeroes ws again, as the header says)
+      gave_up |= pending;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) key = umax64(key, __shfl_xor(key, o));
     if ((tid & 63) == 0) red[tid >> 6] = key;
-    const int all_arrived = __syncthreads_and(pending ? 0 : 1);
+    const int all_arrived = __syncthreads_and(gave_up ? 0 : 1);
     if (tid == 0) {
       uint64_t m = red[0];
       for (int w = 1; w < kWaves; ++w) m = umax64(m, red[w]);

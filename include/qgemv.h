@@ -307,9 +307,12 @@ int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx
  * ws: device, batch * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW u64 words (8-byte
  * aligned), owned by the caller, all zero before its first use; every call
  * leaves it all zero. Calls that may run concurrently need distinct ws.
- * idx: device int32 [batch], 4-byte aligned. (idx -1 would mean a workgroup
- * never published its key, which a launch that runs to completion rules
- * out; the last workgroup's wait for the others is bounded.)
+ * idx: device int32 [batch], 4-byte aligned. idx -1 means that the
+ * collecting workgroup's bounded wait (about 2^20 polls) ran out before every
+ * wave had published its key, which happens only if other work keeps the
+ * launch's workgroups from running for that long. The collector then clears
+ * every word it can, but a wave that publishes afterwards leaves its word
+ * set: after idx -1, zero ws again before the next call.
  * Errors: as qgemv_run_grouped; EINVAL for argmax_entry outside [0, n) or a
  * null ws or idx; EALIGN for misaligned ws or idx. Nothing is launched on
  * error.
