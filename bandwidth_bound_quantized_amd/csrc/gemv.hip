@@ -1032,25 +1032,72 @@ struct MfmaArgmax {
   int wg = 0;                  // this workgroup within the entry
 };
 
-// The argmax of a matrix-core launch: idx[b] = the index in the largest of
-// row b's nwg keys (nwg <= kMaxArgmaxKeyWords); every key word is cleared
-// again. One wave per batch row, all of a lane's loads issued together.
-constexpr int kMaxArgmaxKeyWords = 8 * 64;
-__global__ __launch_bounds__(512) void argmax_keys_kernel(uint64_t* __restrict__ slots, int nwg,
-                                                           int32_t* __restrict__ idx) {
-  const int b = static_cast<int>(threadIdx.x >> 6), lane = static_cast<int>(threadIdx.x & 63);
-  uint64_t* row = slots + static_cast<size_t>(b) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW;
-  uint64_t v[8];
+// The argmax of a matrix-core launch, run by its workgroup 0 (which does no
+// GEMV work) while the others stream: wait until each of the argmax entry's
+// nwords workgroups has published its key for every batch row
+// (slots[b * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + w], nonzero once
+// written), take the largest, write idx[b], and clear the words again. A
+// thread takes words tid, tid + blockDim.x, ..., all batch rows' loads in
+// flight together. The wait is bounded: a key never published (which needs
+// a workgroup that never runs) gives idx -1 instead of a hang. red: LDS for
+// NB + 1 words per wave (the kernel's dynamic LDS: a reduction through
+// static LDS, as __syncthreads_and uses, would leave the dynamic LDS short
+// of the 160 KiB a workgroup may take). (Before, a one-workgroup kernel
+// launched after the matrix-core launch took the keys: 4.5 us plus its
+// launch gap, at batch 8.)
+constexpr int kMaxArgmaxKeyWords = 8 * 64;     // argmax workgroups per launch (<= a collector's threads)
+template <int NB>
+__device__ __forceinline__ void mfma_argmax_collect(uint64_t* __restrict__ slots, int nwords, int batch,
+                                                    int32_t* __restrict__ idx, uint64_t* red) {
+  const int tid = static_cast<int>(threadIdx.x), nt = static_cast<int>(blockDim.x);
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  uint64_t key[NB];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < nwg ? row[lane + 64 * u] : uint64_t{0};
-  uint64_t k = 0;
+  for (int b = 0; b < NB; ++b) key[b] = 1;
+  bool gave_up = false;
+  for (int w = tid; w < nwords; w += nt) {
+    uint64_t v[NB];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    k = umax64(k, v[u]);
-    if (lane + 64 * u < nwg) row[lane + 64 * u] = 0;
+    for (int b = 0; b < NB; ++b) v[b] = b < batch ? 0 : 1;
+    bool pending = true;
+    for (int spin = 0; pending && spin < (gave_up ? 1 : kFusedSpinLimit); ++spin) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (v[b] == 0)
+          v[b] = __hip_atomic_load(slots + static_cast<size_t>(b) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + w,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pending = false;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pending |= v[b] == 0;
+      if (pending) __builtin_amdgcn_s_sleep(2);
+    }
+    gave_up |= pending;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < batch) {
+        key[b] = umax64(key[b], v[b]);
+        __hip_atomic_store(slots + static_cast<size_t>(b) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + w, uint64_t{0},
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
-  k = wave_umax64(k);
-  if (lane == 0) idx[b] = argmax_index(k);
+  const bool wave_gave_up = __builtin_amdgcn_ballot_w64(gave_up) != 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint64_t k = wave_umax64(key[b]);
+    if (lane == 0) red[wave * (NB + 1) + b] = k;
+  }
+  if (lane == 0) red[wave * (NB + 1) + NB] = wave_gave_up ? 1 : 0;
+  __syncthreads();
+  if (tid < batch) {
+    uint64_t m = 1;
+    bool all_arrived = true;
+    for (int w = 0; w < nw; ++w) {
+      m = umax64(m, red[w * (NB + 1) + tid]);
+      all_arrived &= red[w * (NB + 1) + NB] == 0;
+    }
+    idx[tid] = (all_arrived && m > 1) ? argmax_index(m) : -1;
+  }
 }
 constexpr int kNormFactorOff = (kMfmaMaxThreads / 64) * QGEMV_MAX_BATCH;   // floats
 static_assert((kNormFactorOff + QGEMV_MAX_BATCH) * 4 <= static_cast<int>(kNormScratchBytes), "norm scratch");
@@ -1666,8 +1713,9 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
   if constexpr (AM) {
     // ---- argmax of the entry's output: the workgroup's largest key per
     // batch row (waves, then through LDS) goes to its own word of the
-    // caller's workspace; argmax_keys_kernel, launched next, takes the
-    // largest of the words. (A counter that let the last workgroup finish
+    // caller's workspace (a relaxed device-scope store; key 1 never wins);
+    // workgroup 0 of the launch takes the largest of the words
+    // (mfma_argmax_collect). (A counter that let the last workgroup finish
     // the argmax made every workgroup queue on one address at the end.)
     if (!am_on) return;                                // (uniform over the workgroup)
     uint64_t* wk = reinterpret_cast<uint64_t*>(xs);    // x is no longer read
@@ -1680,7 +1728,8 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
     if (tid < NB && tid < batch) {
       uint64_t k = 0;
       for (int w = 0; w < nw; ++w) k = umax64(k, wk[w * NB + tid]);
-      amx.slots[static_cast<size_t>(tid) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + amx.wg] = k;
+      __hip_atomic_store(amx.slots + static_cast<size_t>(tid) * QGEMV_FUSED_ARGMAX_WS_WORDS_PER_ROW + amx.wg,
+                         umax64(k, 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1906,11 +1955,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 // again when the entry changes), so most workgroups stage x once.
 // The matrix-core launch: workgroup b belongs to the entry whose
 // [wg0, wg0 + nwg) holds b and takes the b-th of its nwg balanced tile ranges.
+// AM: workgroup 0 collects the argmax keys of entry tab.am (into am_idx),
+// the workers are workgroups 1.. (b = blockIdx.x - 1).
 template <int FMT, int NB, int N, bool FUSED = false, bool AM = false>
 __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTable<N> tab, int batch,
-                                                                    const Fusion fu, uint64_t* am_slots) {
+                                                                    const Fusion fu, uint64_t* am_slots,
+                                                                    int32_t* am_idx) {
   extern __shared__ u32x4 lds_v4[];
-  const int b = static_cast<int>(blockIdx.x);
+  if constexpr (AM) {
+    if (blockIdx.x == 0) {
+      mfma_argmax_collect<NB>(am_slots, tab.e[tab.am].nwg, batch, am_idx, reinterpret_cast<uint64_t*>(lds_v4));
+      return;
+    }
+  }
+  const int b = static_cast<int>(blockIdx.x) - (AM ? 1 : 0);
   int j = 0;
   if constexpr (N > 1) {
     while (j + 1 < tab.n && b >= tab.e[j + 1].wg0) ++j;
@@ -2137,7 +2195,7 @@ struct MfmaPlan {
 // workgroup, the rest go one at a time to the entry with the most (tile,
 // step) pairs per workgroup, never more than one per tile. Depends on (fmt,
 // M, K) of the entries and the CU count only, not on the batch.
-MfmaPlan plan_mfma(const GemvArgs* a, int n, int cus, int nb, size_t extra, int* nwg) {
+MfmaPlan plan_mfma(const GemvArgs* a, int n, int cus, int nb, size_t extra, int reserve, int* nwg) {
   const int step = mfma_step_elems(a[0].fmt);
   const int tr = nb == 8 ? kMfmaTileRows<8> : kMfmaTileRows<4>;
   long total = 0, tiles_all = 0;
@@ -2159,9 +2217,11 @@ MfmaPlan plan_mfma(const GemvArgs* a, int n, int cus, int nb, size_t extra, int*
     p.lds = mfma_lds_bytes(a[0].fmt, kmax, nb, 16, extra);
     per_cu = 1;
   }
-  // (at most kMaxArgmaxKeyWords workgroups: an argmax entry's keys fit argmax_keys_kernel)
+  // (reserve: workgroups kept free for the argmax collector; at most
+  // kMaxArgmaxKeyWords workgroups, as many as the collector has threads)
   const long target = std::max<long>(
-      std::min<long>({static_cast<long>(cus) * per_cu, tiles_all, static_cast<long>(kMaxArgmaxKeyWords)}), n);
+      std::min<long>({static_cast<long>(cus) * per_cu - reserve, tiles_all, static_cast<long>(kMaxArgmaxKeyWords)}),
+      n);
   // a proportional start (every entry at least one, at most one per tile),
   // then the remainder one at a time
   long grid = 0;
@@ -2191,14 +2251,19 @@ template <int FMT, int NB, int N, bool FUSED = false, bool AM = false>
 hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fusion& fu = Fusion{},
                              int am = -1, uint64_t* slots = nullptr, int32_t* idx = nullptr) {
   MfmaTable<N> tab{};
+  // the argmax entry first: its workgroups are dispatched first and finish
+  // before most others, so the collector's wait overlaps their streaming
+  // (last, it held the launch open about 3 us at batch 8)
+  GemvArgs o[N];
+  for (int t = 0; t < n; ++t) o[t] = a[am < 0 ? t : t == 0 ? am : (t <= am ? t - 1 : t)];
   int nwg[N];
-  const MfmaPlan p = plan_mfma(a, n, device_cu_count(), NB, FUSED ? kNormScratchBytes : 0, nwg);
+  const MfmaPlan p = plan_mfma(o, n, device_cu_count(), NB, FUSED ? kNormScratchBytes : 0, AM ? 1 : 0, nwg);
   tab.n = n;
-  tab.am = am;
+  tab.am = am < 0 ? -1 : 0;
   int wg = 0;
   for (int i = 0; i < n; ++i) {
-    tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(a[i].W), a[i].scales, a[i].x, a[i].y,
-                         a[i].M, a[i].K, wg, nwg[i]};
+    tab.e[i] = MfmaEntry{static_cast<const uint8_t*>(o[i].W), o[i].scales, o[i].x, o[i].y,
+                         o[i].M, o[i].K, wg, nwg[i]};
     wg += nwg[i];
   }
   if (p.lds > 64 * 1024) {
@@ -2207,12 +2272,10 @@ hipError_t launch_mfma_table(const GemvArgs* a, int n, hipStream_t st, const Fus
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
     if (once != hipSuccess) return once;
   }
-  gemv_mfma_kernel<FMT, NB, N, FUSED, AM><<<p.grid, 64 * p.waves, p.lds, st>>>(tab, a[0].batch, fu, slots);
-  if (AM) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    argmax_keys_kernel<<<1, 64 * a[0].batch, 0, st>>>(slots, nwg[am], idx);
-  }
+  // (with the argmax, workgroup 0 collects the keys: the workers get one
+  // workgroup fewer, so that all of them and the collector are resident)
+  gemv_mfma_kernel<FMT, NB, N, FUSED, AM><<<p.grid + (AM ? 1 : 0), 64 * p.waves, p.lds, st>>>(
+      tab, a[0].batch, fu, slots, idx);
   return hipGetLastError();
 }
 

@@ -298,9 +298,9 @@ int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx
  * the logits.
  * When the matrix-core kernel computes it (batch 3..8), each of the entry's
  * workgroups folds the logits it writes into one key per batch row and
- * stores it in its own word of ws, and a one-workgroup kernel launched next
- * takes the largest of those words and clears them (a second launch of a
- * few hundred words, no second pass over the logits).
+ * publishes it in its own word of ws, and again one workgroup of the launch
+ * collects the words and takes the largest (the argmax entry's workgroups
+ * are dispatched first, so the collecting overlaps the other entries).
  * Otherwise the argmax is a qgemv_argmax launch after the GEMVs, on the same
  * stream, with the same ws. The logits (gemvs[argmax_entry].y) are written
  * in full either way.
@@ -309,10 +309,10 @@ int qgemv_argmax_noalloc(const float* logits, int64_t V, int batch, int32_t* idx
  * leaves it all zero. Calls that may run concurrently need distinct ws.
  * idx: device int32 [batch], 4-byte aligned. idx -1 means that the
  * collecting workgroup's bounded wait (about 2^20 polls) ran out before every
- * wave had published its key, which happens only if other work keeps the
- * launch's workgroups from running for that long. The collector then clears
- * every word it can, but a wave that publishes afterwards leaves its word
- * set: after idx -1, zero ws again before the next call.
+ * wave or workgroup had published its key, which happens only if other work
+ * keeps the launch's workgroups from running for that long. The collector
+ * then clears every word it can, but a key published afterwards leaves its
+ * word set: after idx -1, zero ws again before the next call.
  * Errors: as qgemv_run_grouped; EINVAL for argmax_entry outside [0, n) or a
  * null ws or idx; EALIGN for misaligned ws or idx. Nothing is launched on
  * error.
