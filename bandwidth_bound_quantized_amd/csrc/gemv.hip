@@ -2334,6 +2334,25 @@ bool gemv_uses_lds(int fmt, int K, int batch, bool fused) {
   return !(round_batch(batch) <= 2 && xreg_units(fmt, K) <= xreg_max_units(fmt, batch, fused));
 }
 
+// A lone GEMV at batch 3..8 (qgemv_run) below these weight sizes runs faster
+// on the dot2 LDS kernel than on the matrix-core kernel, whose start-up
+// (x staging by every workgroup, the first steps' round trip, the stream-K
+// finisher) costs more than it saves on a few MB. Measured per GEMV,
+// graph-replayed, dot2 against matrix cores: at batch 4, Q4_0 2048x2048 4.3
+// against 6.6 us, 11264x2048 7.8 / 9.6, int8 16384x2048 10.7 / 12.3, but
+// 4-bit 2048x8192 10.5 / 9.9 and the 32000-row Q4_0 LM head 14.0 / 12.1; at
+// batch 8, bf16 2048x2048 5.9 / 7.4, int8 3072x2048 6.3 / 8.8, but Q4_0
+// 11264x2048 11.6 / 10.3 and Q4_0 2048x5632 16.9 / 11.4.
+bool lone_prefers_lds(const GemvArgs& a) {
+  const FmtInfo f = fmt_info(a.fmt);
+  const double code = static_cast<double>(a.K) / f.elems_per_unit * 16;
+  const double scale = f.group > 1 ? static_cast<double>(a.K) / f.group * 2 : (f.group == 0 ? 2 : 0);
+  const double bytes = static_cast<double>(a.M) * (code + scale);
+  const bool four_bit = f.elems_per_unit == 32;
+  if (round_batch(a.batch) <= 4) return bytes <= 36e6 && !(four_bit && a.K > 6144);
+  return bytes <= 9e6 && a.K <= 4096;
+}
+
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
   const int cus = device_cu_count();
   const int nch = xreg_units(a.fmt, a.K);
@@ -2353,7 +2372,8 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream, int flags) {
     const int grid = std::max(1, std::min(wg_needed, cus * QGEMV_MAX_WG_PER_CU));
     return with_fmt(a.fmt, [&](auto F) { return launch_xreg<decltype(F)::value>(a, R, nch, grid, stream); });
   }
-  if (mfma_fits(a.fmt, a.K, inv ? 8 : a.batch, 0)) return launch_mfma_fmt<1>(&a, 1, stream, nb);
+  if (mfma_fits(a.fmt, a.K, inv ? 8 : a.batch, 0) && (inv || !lone_prefers_lds(a)))
+    return launch_mfma_fmt<1>(&a, 1, stream, nb);
   const size_t lds = gemv_lds_bytes(a.fmt, a.K, nb);
   // rows per wave step: as many as keep at least two workgroups per CU busy
   int R = 4;
