@@ -33,6 +33,9 @@ Reported (one JSON line):
                    8 TB/s spec, and the size-matched ceiling
   measured_peak    best median rate of the streaming-read kernel over 4 GiB
   cpu_baseline     the fp64 CPU oracle on whole steps, all cores and one thread
+  lm_head_alone    a 128256x2048 GEMV (the Llama-3.2-1B LM head shape) alone at
+                   batch 1 in bf16, int8-g32 and Q4_0-g32: the per-format
+                   fraction of the measured peak at a size one launch can reach
 Algorithmic bytes per GEMV = code bytes + scale bytes + x (2*B*K) + y (4*B*M);
 a separate argmax = 4*B*V read + 4*B written; a fused argmax = 4*B written.
 """
@@ -95,6 +98,7 @@ def parse():
     p.add_argument("--per-kernel", action="store_true", help="focused run: also time every GEMV alone")
     p.add_argument("--no-attention", action="store_true", help="skip the decode-attention measurements")
     p.add_argument("--no-fused-layer", action="store_true", help="skip the fused decode-layer chain")
+    p.add_argument("--no-lm-heads", action="store_true", help="skip the 128256x2048 LM heads alone")
     p.add_argument("--pmc-pass", action="store_true",
                    help="only run calibration kernels (a 64 MiB streaming read, a 64 MiB fill) and "
                         "--steps eager steps of --workload, for hardware-counter collection")
@@ -678,6 +682,24 @@ def main():
     del w5
     torch.cuda.empty_cache()
 
+    # ---- the batch-1 fraction-of-peak targets per format, at a size one launch can reach
+    # them: the Llama-3.2-1B LM head shape (128256 x 2048) alone through qgemv_run
+    lm_heads = None
+    if not args.no_lm_heads:
+        lm_heads = {}
+        for fmt in (synth.BF16, synth.INT8_G32, synth.Q4_0_G32):
+            g = synth.make_gemv("lm_head", fmt, 128256, 2048, 1, 5, 0, "lm_head")
+            wh = Weights(torch, [g], rotate)
+            wl = Workload(qg, torch, 1, 1, wh)
+            s = time_calls(torch, lambda i, h: wl.launch_one(0, i, h), wl.launch_count(4, 32), args.trials)
+            f = figure(wl.bytes[0], s, pk, ceil(wl.bytes[0]))
+            f.update({"M": g.M, "K": g.K, "call": "qgemv_run", "rotation_sets": wh.n_sets})
+            lm_heads[synth.FMT_NAMES[fmt]] = f
+            print(f"[bench] {synth.FMT_NAMES[fmt]} 128256x2048 alone: {f['us']:.2f} us, {f['GBps']} GB/s",
+                  file=sys.stderr, flush=True)
+            del wl, wh, g
+            torch.cuda.empty_cache()
+
     attention = None
     if not args.no_attention:
         attention = attention_bench(qg, torch, rotate, args.trials)
@@ -751,6 +773,8 @@ def main():
         out["fused_layer"] = fused_layer
     if attention is not None:
         out["attention_decode"] = attention
+    if lm_heads is not None:
+        out["lm_head_alone"] = lm_heads
     out["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(out), flush=True)
 
