@@ -45,8 +45,8 @@
 #include "qgemv_internal.h"
 #include "qgemv.h"
 
-// Launch-shape defaults (build-time; the values were chosen by measurement
-// on MI355X, see the tuning notes of this repository's design document).
+// Launch-shape defaults (build-time overrides; the values were chosen by
+// sweeping each one on MI355X with graph-timed, rotated launches).
 #ifndef QGEMV_XREG_MAX_R
 #define QGEMV_XREG_MAX_R 4        // rows per wave step, register-x kernel
 #endif
@@ -516,6 +516,20 @@ struct GemvTable {
   TableEntry e[N];
 };
 
+// The entry of a table whose entries' first row groups (or workgroups), read
+// by key, ascend: the last entry e with key(e) <= v. Lane l reads entry l and
+// a ballot counts the entries at or below v: one load, where walking the
+// table costs one dependent scalar load per entry passed (a workgroup of the
+// fifth entry waited for four of them before its first weight load). All 64
+// lanes must be active; n <= 64.
+template <typename Tab, typename Key>
+__device__ __forceinline__ int find_entry(const Tab& tab, int v, Key key) {
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  bool le = false;
+  if (lane < tab.n) le = key(tab.e[lane]) <= v;
+  return __popcll(__builtin_amdgcn_ballot_w64(le)) - 1;
+}
+
 // Small-batch variant: x never goes through LDS. Lane l always works on the
 // same NCH units (l, l+64, ...) of every row of a GEMV, so it loads the x
 // values those units pair with once, straight into registers (with the 4-bit
@@ -620,7 +634,6 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
   // per lane: byte offset of its unit in a row and of its unit's scale in a scale row
   int woff[NCH], soff[NCH];
 
-  // make entry j current: its geometry and this lane's x registers
   // make entry j current: its geometry (enter_geom), then this lane's x
   // registers (enter_x)
   auto enter_geom = [&](int jj) {
@@ -934,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
   AmLane am;
   if (item < end) {
     int j = 0;
-    while (j + 1 < tab.n && item >= tab.e[j + 1].start) ++j;
+    if constexpr (N > 1) j = find_entry(tab, item, [](const TableEntry& e) { return e.start; });
     while (item < end) {
       if constexpr (AM) {
         if (j > tab.am && !am.left) am_leave<NB>(am, slots, batch, lane);   // past the entry
@@ -1970,9 +1983,7 @@ __global__ __launch_bounds__(kMfmaMaxThreads) void gemv_mfma_kernel(const MfmaTa
   }
   const int b = static_cast<int>(blockIdx.x) - (AM ? 1 : 0);
   int j = 0;
-  if constexpr (N > 1) {
-    while (j + 1 < tab.n && b >= tab.e[j + 1].wg0) ++j;
-  }
+  if constexpr (N > 1) j = find_entry(tab, b, [](const MfmaEntry& e) { return e.wg0; });
   const MfmaEntry& ent = tab.e[j];
   const long tiles = (ent.M + kMfmaTileRows<NB> - 1) / kMfmaTileRows<NB>;
   const int r = b - ent.wg0;
@@ -2065,6 +2076,7 @@ hipError_t launch_xreg(const GemvArgs& a, int R, int nch, int grid, hipStream_t 
 }
 
 constexpr int kGroupMax = 64;       // GEMVs per grouped launch (kernel-argument table)
+static_assert(kGroupMax <= 64, "find_entry reads one entry per lane");
 
 // Entries of one format and batch with their (R, NCH) already chosen; am >= 0:
 // also the argmax of entry am's output (into idx, through slots).
