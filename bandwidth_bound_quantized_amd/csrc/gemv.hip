@@ -1550,10 +1550,11 @@ __device__ __forceinline__ void mfma_tiles(const MfmaEntry& ent, int t0, int t1,
         const int b = 4 * ((v >> 2) % NBh) + (v & 3);
         const int row = tile * kTR + 4 * ((v >> 2) / NBh) + lj;
         if (row < M && b < batch) {
-          if constexpr (FUSED) epi_store(fu, Y, M, b, row, q[n], pq[n]);
+          float out = q[n];
+          if constexpr (FUSED) out = epi_store(fu, Y, M, b, row, q[n], pq[n]);
           else Y[static_cast<size_t>(b) * M + row] = q[n];
           if constexpr (AM) {
-            if (am_on) amk[n % NBh] = umax64(amk[n % NBh], argmax_key(q[n], static_cast<uint32_t>(row)));
+            if (am_on) amk[n % NBh] = umax64(amk[n % NBh], argmax_key(out, static_cast<uint32_t>(row)));
           }
         }
       }
@@ -2510,6 +2511,12 @@ hipError_t launch_fused_fmt(const GemvArgs& a, const Fusion& f, uint64_t* slots,
   }
   hipError_t e;
   if (mfma_fits(FMT, a.K, a.batch, kNormScratchBytes)) {
+    if (idx) {
+      // the argmax inside the launch, collected by its workgroup 0 (as in
+      // the grouped launch; slots: zero on entry, zero on exit)
+      return nb == 4 ? launch_mfma_table<FMT, 4, 1, true, true>(&a, 1, st, f, 0, slots, idx)
+                     : launch_mfma_table<FMT, 8, 1, true, true>(&a, 1, st, f, 0, slots, idx);
+    }
     e = nb == 4 ? launch_mfma_table<FMT, 4, 1, true>(&a, 1, st, f)
                 : launch_mfma_table<FMT, 8, 1, true>(&a, 1, st, f);
   } else {
