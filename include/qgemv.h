@@ -343,7 +343,8 @@ int qgemv_run_grouped_argmax(const qgemv_gemv_desc* gemvs, int n, int batch, int
  *             be NULL), M must be even. Not with residual or the argmax.
  * argmax_idx, argmax_ws  as idx and ws of qgemv_run_grouped_argmax for the
  *             argmax of each row of y (fused into the launch at batch <= 2
- *             with short rows, a separate launch otherwise).
+ *             with short rows and on the matrix-core kernel at batch 3..8,
+ *             a separate launch otherwise).
  */
 typedef struct qgemv_fusion {
   const float* norm_input;
