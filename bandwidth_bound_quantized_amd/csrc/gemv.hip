@@ -39,6 +39,7 @@
 // No MFMA: at batch <= 8 this is a matrix-vector product, not a dense
 // contraction.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "argmax_key.h"
@@ -615,11 +616,15 @@ __device__ __forceinline__ void am_leave(AmLane& am, uint64_t* __restrict__ slot
 template <int NB>
 __device__ __forceinline__ void stage_norm_rows(const Fusion& fu, int K, int batch, uint32_t* xs, float* scr);
 
+// first (with has_first): entry j's fields, already read by the caller, so
+// that the first loads need no further table read.
 template <int FMT, int NB, int R, int NCH, int N, bool AM = false, bool FUSED = false>
 __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int item, int stride,
                                         int batch, int lane, AmLane& am,
                                         uint64_t* am_slots, const Fusion& fu,
-                                        uint32_t* xn = nullptr, int end = -1) {
+                                        uint32_t* xn = nullptr, int end = -1,
+                                        const TableEntry& first = TableEntry{}, bool has_first = false,
+                                        int first_next_start = 0) {
   if (end < 0) end = tab.total;                  // row groups item, item + stride, ... below end
   using T = Traits<FMT>;
   static_assert(!FUSED || R % 2 == 0, "gate/up pairs must share a row group");
@@ -635,11 +640,18 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
   int woff[NCH], soff[NCH];
 
   // make entry j current: its geometry (enter_geom), then this lane's x
-  // registers (enter_x)
+  // registers (enter_x); use_first: the caller's copy of entry j (used once;
+  // taken by value, never through a pointer that may point at either copy,
+  // which would put the table in scratch memory)
+  bool use_first = has_first;
+  auto entry = [&](int jj) -> TableEntry {
+    if (use_first) return first;
+    return tab.e[jj];
+  };
   auto enter_geom = [&](int jj) {
-    const TableEntry& e = tab.e[jj];
+    const TableEntry e = entry(jj);
     W = e.W; S = e.S; Y = e.Y; M = e.M; start = e.start;
-    next_start = (N > 1 && jj + 1 < tab.n) ? tab.e[jj + 1].start : tab.total;
+    next_start = use_first ? first_next_start : (N > 1 && jj + 1 < tab.n) ? tab.e[jj + 1].start : tab.total;
     U = e.K / T::kElems;
     row_bytes = U * 16;
     nsc = scales_per_row<FMT>(U);
@@ -651,7 +663,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     }
   };
   auto enter_x = [&](int jj) {
-    const TableEntry& e = tab.e[jj];
+    const TableEntry e = entry(jj);
     // (fused prologue: x was normalized into LDS by the workgroup, xn)
     const uint32_t* xsrc = reinterpret_cast<const uint32_t*>(e.X);
     if constexpr (FUSED) {
@@ -726,6 +738,7 @@ __device__ __forceinline__ int xreg_run(const GemvTable<N>& tab, int& j, int ite
     enter(j);
     load_step(item - start);
   }
+  use_first = false;
   bias_sums();
 
   float acc[R][NB];
@@ -930,15 +943,32 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
       return;
     }
   }
+  // With the argmax: the table's header, entry 0 (the argmax entry) and
+  // where entry 1 starts, at fixed offsets of the argument table, are read
+  // together at the start with one wait (the empty asm needs every value
+  // there). A wave whose first row group is in entry 0 (with strided row
+  // groups, every wave) then issues its first loads one table round trip
+  // after it starts instead of three (the walk or ballot, then the entry's
+  // shape, then its fields, each waiting for the one before): the TinyLlama
+  // set at batch 1 14.98 -> 14.60 us. (Without the argmax the first entry
+  // holds fewer waves' first row groups, and the early wait measured
+  // slower: the int8 set 13.94 -> 14.36 us.)
+  const TableEntry e0 = AM ? tab.e[0] : TableEntry{};
+  const int e1_start = AM && N > 1 ? tab.e[1].start : tab.total;   // (entries past n start at INT_MAX)
+  const int t_total = tab.total, t_contig = tab.contig;
+  if constexpr (AM) {
+    asm volatile("" ::"s"(e0.W), "s"(e0.S), "s"(e0.X), "s"(e0.Y), "s"(e0.M), "s"(e0.K), "s"(e0.start),
+                 "s"(e0.shape), "s"(e1_start), "s"(t_total), "s"(t_contig));
+  }
   int stride;
   int item = first_item<AM ? 1 : 0>(stride);
-  int end = tab.total;
-  if (tab.contig) {
+  int end = t_total;
+  if (t_contig) {
     // one contiguous range of row groups per wave (waves in order), so a
     // wave stays in one entry for many steps instead of reloading x at
     // almost every step
     const int nw = stride, wid = item;
-    const int per = tab.total / nw, rem = tab.total % nw;
+    const int per = t_total / nw, rem = t_total % nw;
     item = wid * per + min(wid, rem);
     end = item + per + (wid < rem ? 1 : 0);
     stride = 1;
@@ -947,21 +977,26 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
   AmLane am;
   if (item < end) {
     int j = 0;
-    if constexpr (N > 1) j = find_entry(tab, item, [](const TableEntry& e) { return e.start; });
+    if constexpr (N > 1) {
+      if (!AM || item >= e1_start) j = find_entry(tab, item, [](const TableEntry& e) { return e.start; });
+    }
+    bool has_first = AM && j == 0;
     while (item < end) {
       if constexpr (AM) {
         if (j > tab.am && !am.left) am_leave<NB>(am, slots, batch, lane);   // past the entry
       }
-      switch (tab.e[j].shape) {
+      switch (has_first ? e0.shape : tab.e[j].shape) {
 #define QG_SHAPE(R_, C_) \
         case xreg_shape(R_, C_): \
-          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end); break;
+          item = xreg_run<FMT, NB, R_, C_, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end, \
+                                                  e0, has_first, e1_start); break;
         // the shapes launch_gemv_group produces (the kernel's register budget,
         // and with it its occupancy, is the largest of theirs)
         QG_SHAPE(4, 1) QG_SHAPE(2, 1)
         case xreg_shape(8, 1):                   // batch 1, contiguous ranges only
           if constexpr (NB == 1)
-            item = xreg_run<FMT, NB, 8, 1, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end);
+            item = xreg_run<FMT, NB, 8, 1, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end,
+                                                  e0, has_first, e1_start);
           else
             item = end;
           break;
@@ -969,13 +1004,15 @@ __global__ __launch_bounds__(kThreads) void gemv_xreg_group_kernel(const GemvTab
         QG_SHAPE(QGEMV_GROUP_RLONG, 3) QG_SHAPE(QGEMV_GROUP_RLONG, 4)
         case xreg_shape(1, 8):                   // int8 at batch 1 only
           if constexpr (is_int8_fmt(FMT) && NB == 1)
-            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end);
+            item = xreg_run<FMT, NB, 1, 8, N, AM>(tab, j, item, stride, batch, lane, am, slots, Fusion{}, nullptr, end,
+                                                  e0, has_first, e1_start);
           else
             item = tab.total;
           break;
 #undef QG_SHAPE
         default: item = tab.total;               // not produced by the host
       }
+      has_first = false;
     }
   }
   if constexpr (AM) {
@@ -2105,6 +2142,7 @@ hipError_t launch_group2(const GemvArgs* a, const int* R_in, const int* nch, int
       start += (a[i].M + R[i] - 1) / R[i];
     }
     tab.total = start;
+    for (int t = n; t < kGroupMax; ++t) tab.e[t].start = INT_MAX;   // never a wave's entry
   };
   build();
   // The grid is at most what is resident at once (workgroups per CU from the
