@@ -79,3 +79,37 @@ def test_random_grouped_call(seed):
         ym = items[am][4].cpu().numpy()
         assert (idx.cpu().numpy() == oracle.argmax_ref(ym)).all()
         assert (ws.cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("B,am", [(1, 3), (1, 66), (2, 3), (4, 3), (8, 66)])
+def test_many_entries_grouped_argmax(B, am):
+    """70 GEMVs in one call (two launches of the 64-entry table): every workgroup finds its
+    entry by the lane-parallel lookup, the argmax entry in the first or the second launch;
+    every row of every GEMV and the index against the oracle, and the workspace left zero."""
+    rng = np.random.default_rng(4000 + 10 * B + am)
+    gemvs = []
+    for i in range(70):
+        K = 5632 if i % 9 == 4 else 2048
+        M = int(rng.choice([64, 100, 257, 1000, 1500, 3001]))
+        gemvs.append(synth.make_gemv(f"m{i}", qg.Q4_0_G32, M, K, B, 6, 5000 + 100 * B + i, "o"))
+    items = []
+    for g in gemvs:
+        W = _dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+        S = _dev(g.s.reshape(-1))
+        X = _dev(np.ascontiguousarray(g.x).reshape(B, g.K))
+        Y = torch.full((B, g.M), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((g.fmt, W, S, X, Y, g.M, g.K))
+    descs = qg.grouped_descs(items)
+    ws = qg.fused_argmax_workspace(B)
+    idx = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    print(f"[gpu] many entries B={B} argmax entry {am}", flush=True)
+    qg.run_grouped_argmax(descs, B, am, ws, idx)
+    torch.cuda.synchronize()
+    for g, it in zip(gemvs, items):
+        y = it[4].cpu().numpy()
+        assert np.isfinite(y).all(), g.name
+        y_ref, a_ref = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K)
+        rep = oracle.parity_report(y, y_ref, a_ref)
+        assert rep["ok"], f"{g.name} {g.M}x{g.K} {rep}"
+    assert (idx.cpu().numpy() == oracle.argmax_ref(items[am][4].cpu().numpy())).all()
+    assert bool((ws == 0).all().item())
