@@ -193,3 +193,56 @@ def test_fused_norm_constant_rows_exact():
     qg.run_fused(fmt, c.Wd, c.Sd, dev(xb), y_x, M, K, B)
     torch.cuda.synchronize()
     assert (y_n.cpu().numpy().view(np.uint32) == y_x.cpu().numpy().view(np.uint32)).all()
+
+
+FUSED_FMTS = [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64]
+FUSED_K_STEP = {qg.BF16: 32, qg.INT8_G32: 32, qg.Q4_0_G32: 32, qg.INT4_G128: 128, qg.INT8_ROW: 32,
+                qg.INT4_G64: 64}
+
+
+def _random_fused_case(seed):
+    """A seeded draw of format, batch, ragged M and K, and the fused operations."""
+    rng = np.random.default_rng(7000 + seed)
+    fmt = int(rng.choice(FUSED_FMTS))
+    B = int(rng.choice([1, 1, 2, 2, 3, 4, 5, 6, 7, 8]))
+    step = FUSED_K_STEP[fmt]
+    kmax = 8192 if B <= 2 else 4096              # x of the batch staged in LDS where the kernel does
+    K = int(step * rng.integers(max(1, 256 // step), kmax // step + 1))
+    if rng.random() < 0.4:
+        K = int(rng.choice([2048, 4096] + ([5632, 8192] if B <= 2 else []))) // step * step
+    epi = str(rng.choice(["plain", "residual", "inplace", "swiglu"]))
+    M = int(rng.choice([2, 64, 130, 1000, 2050, 4098, int(rng.integers(1, 6000))]))
+    if epi == "swiglu" and M % 2:
+        M += 1
+    norm = bool(rng.random() < 0.6)
+    argmax = epi != "swiglu" and bool(rng.random() < 0.5)
+    return fmt, M, K, B, norm, epi, argmax
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_fused_call(seed):
+    """Seeded random qgemv_run_fused calls across the three kernels: every row of y
+    (or of the SwiGLU activations) against the oracle, the argmax bit-exact on the
+    GPU's own logits, and the workspace left zero."""
+    fmt, M, K, B, norm, epi, argmax = _random_fused_case(seed)
+    c = Case(fmt, M, K, B, 31 * seed + 5)
+    y_ref, a_ref = c.oracle_y(norm=norm)
+    tol = REL_TOL * a_ref + ABS_TOL
+    if epi == "swiglu":
+        act = oracle.bf16_to_f64(c.run(norm=norm, swiglu=True)["act"])
+        bad = np.abs(act - ofused.swiglu_ref(y_ref)) > ofused.swiglu_bound(y_ref, tol)
+        assert not bad.any(), f"swiglu: {int(bad.sum())} outside the bound"
+        return
+    if epi == "plain":
+        out = c.run(norm=norm, argmax=argmax)
+        _parity(out["y"], y_ref, a_ref, "plain")
+    else:
+        out = c.run(norm=norm, argmax=argmax, residual="separate" if epi == "residual" else "inplace",
+                    y_init=c.res if epi == "inplace" else None)
+        want = c.res.astype(np.float64) + y_ref
+        err = np.abs(out["y"] - want)
+        assert np.isfinite(out["y"]).all()
+        assert (err <= ofused.residual_bound(want, tol)).all(), f"residual: worst {np.max(err)}"
+    if argmax:
+        assert out["ws_zero"]
+        assert (out["idx"] == oracle.argmax_ref(out["y"])).all()
