@@ -1,5 +1,5 @@
 """Seeded random grouped calls: mixed formats, row lengths (ragged M and K), batch 1..8,
-with and without the fused LM-head argmax, each GEMV's sampled rows against the fp64
+with and without the fused LM-head argmax, every row of each GEMV against the fp64
 oracle and the index bit-exact against the oracle's argmax of the GPU's own logits."""
 from __future__ import annotations
 
@@ -48,7 +48,7 @@ def _case(seed):
     return rng, B, gemvs, rng.random() < 0.5, int(rng.integers(0, n))
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_grouped_call(seed):
     rng, B, gemvs, use_am, am = _case(seed)
     items = []
@@ -71,9 +71,8 @@ def test_random_grouped_call(seed):
     for g, it in zip(gemvs, items):
         y = it[4].cpu().numpy()
         assert np.isfinite(y).all(), g.name
-        rows = None if g.M <= 512 else np.unique(np.concatenate([[0, g.M - 1], rng.choice(g.M, 64, replace=False)]))
-        y_ref, a_ref = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K, rows=rows)
-        rep = oracle.parity_report(y if rows is None else y[:, rows], y_ref, a_ref)
+        y_ref, a_ref = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K)
+        rep = oracle.parity_report(y, y_ref, a_ref)
         assert rep["ok"], f"{g.name} {qg.FMT_NAMES[g.fmt]} {g.M}x{g.K} {rep}"
     if use_am:
         ym = items[am][4].cpu().numpy()
