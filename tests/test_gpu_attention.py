@@ -105,3 +105,28 @@ def test_attention_peaked_scores():
     out, _ = gpu_attention(at, n_q, n_kv, d, T)
     assert np.isfinite(out).all()
     check(at, out, "peaked")
+
+
+def _random_attention_case(seed):
+    """A seeded draw of batch, heads (group size 1..8), head size, context and a
+    per-sequence length mix (lengths from 1 to the context, block edges included)."""
+    rng = np.random.default_rng(9100 + seed)
+    B = int(rng.integers(1, 9))
+    n_kv = int(rng.choice([1, 2, 4, 8]))
+    n_q = n_kv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    T = int(rng.choice([1, 63, 64, 65, 300, 1000, 2048, int(rng.integers(1, 6000))]))
+    lens = rng.integers(1, T + 1, size=B)
+    lens[int(rng.integers(0, B))] = T
+    if T > 1 and rng.random() < 0.5:
+        lens[int(rng.integers(0, B))] = int(rng.choice([1, min(64, T), T - 1]))
+    return B, n_q, n_kv, d, T, [int(v) for v in lens]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_attention_call(seed):
+    """Seeded random shapes and length mixes: every output against the oracle."""
+    B, n_q, n_kv, d, T, lens = _random_attention_case(seed)
+    at = synth.make_attention(B, n_q, n_kv, d, T, seed=20000 + seed, lens=lens)
+    out, _ = gpu_attention(at, n_q, n_kv, d, T)
+    check(at, out, f"seed={seed} B={B} {n_q}/{n_kv} d={d} T={T} lens={lens}")
