@@ -626,6 +626,36 @@ def test_batch_invariant_rows_bitwise_equal(fmt, M, K):
         assert (y.view(np.uint32) == want.view(np.uint32)).all(), f"B={B} rows={rows}"
 
 
+def _random_invariant_case(seed):
+    """A seeded draw of format, ragged M and K (x of 8 rows within LDS), and the
+    batch rows of one batch-B call."""
+    rng = np.random.default_rng(11000 + seed)
+    fmt = int(rng.choice(ALL_FMTS))
+    step = synth.K_ALIGN[fmt]
+    K = int(step * rng.integers(1, 6144 // step + 1))
+    M = int(rng.choice([1, 5, 64, 333, 2048, int(rng.integers(1, 9000))]))
+    B = int(rng.integers(2, 9))
+    rows = [int(v) for v in rng.integers(0, 8, size=B)]
+    return fmt, M, K, B, rows
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batch_invariant_call(seed):
+    """Seeded random shapes with the batch-invariant flag: each row of a batch-B call
+    (rows drawn with repeats) equals the batch-1 call on that row's x bit for bit, and
+    every row is within the bound of the oracle."""
+    fmt, M, K, B, rows = _random_invariant_case(seed)
+    g = synth.make_gemv("t", fmt, M, K, 8, 17, 200 + seed, "gate_up")
+    Wd = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+    Sd = dev(g.s.reshape(-1)) if g.s is not None else None
+    x = g.x.reshape(8, K)
+    singles = {b: gpu_gemv_inv(fmt, Wd, Sd, x[b:b + 1], M, K, 1)[0] for b in set(rows)}
+    y = gpu_gemv_inv(fmt, Wd, Sd, x[rows], M, K, B)
+    want = np.stack([singles[b] for b in rows])
+    assert (y.view(np.uint32) == want.view(np.uint32)).all(), f"seed={seed} B={B} rows={rows}"
+    assert_parity(fmt, g.w, g.s, x[rows], M, K, B, y, what="batch call")
+
+
 def test_batch_invariant_flag_zero_is_run():
     """flags 0 is qgemv_run: same bits."""
     fmt, M, K, B = qg.Q4_0_G32, 2048, 2048, 2
