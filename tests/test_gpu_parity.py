@@ -556,6 +556,36 @@ def test_device_quantizer_bit_exact(fmt):
         assert (codes == o_codes.reshape(-1).view(np.uint8)).all()
 
 
+def _random_quant_case(seed):
+    """A seeded draw of format, ragged M and K, and bf16 weights whose rows span many
+    magnitudes (scales from f16 subnormal to large), with zero groups and repeated
+    values (ties in |w|) mixed in."""
+    rng = np.random.default_rng(12000 + seed)
+    fmt = int(rng.choice(ALL_FMTS[1:]))
+    step = synth.K_ALIGN[fmt]
+    K = int(step * rng.integers(1, 4096 // step + 1))
+    M = int(rng.choice([1, 3, 100, int(rng.integers(1, 3000))]))
+    mag = 10.0 ** rng.uniform(-7, 4, size=(M, 1))
+    w32 = (rng.standard_normal((M, K)) * mag).astype(np.float32)
+    z = rng.random((M, K)) < 0.02
+    w32[z] = 0.0
+    rep = rng.random((M, K)) < 0.05
+    w32[rep] = np.round(w32[rep] * 4) / 4                  # repeated magnitudes within a group
+    return fmt, M, K, synth.round_f32_to_bf16_bits(w32)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_device_quantizer_bit_exact(seed):
+    """Seeded random shapes and magnitudes: qgemv_quantize equals the oracle quantizer byte
+    for byte (codes and scales)."""
+    fmt, M, K, w = _random_quant_case(seed)
+    codes, scales, err = gpu_quantize(fmt, w, M, K)
+    o_codes, o_scales = oracle.quantize_from_bf16(fmt, w, M, K)
+    assert err == 0
+    assert (scales == o_scales.reshape(-1)).all()
+    assert (codes == o_codes.reshape(-1).view(np.uint8)).all()
+
+
 def test_device_quantizer_range_errors_flagged():
     w = synth.bf16_normal(np.random.default_rng(5), (4, 128), 0.02)
     _, _, err = gpu_quantize(qg.Q4_0_G32, w, 4, 128)
