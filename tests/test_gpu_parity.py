@@ -253,6 +253,42 @@ def test_argmax_workspace_reuse_many_calls():
         assert (idx == oracle.argmax_ref(logits)).all()
 
 
+def _random_argmax_case(seed):
+    """Seeded logits: random V and batch, values on a coarse grid (many ties), and in some
+    rows a planted maximum repeated at random places, a NaN, +inf or -inf, or signed zeros."""
+    rng = np.random.default_rng(13000 + seed)
+    B = int(rng.integers(1, 9))
+    V = int(rng.choice([1, 2, 63, 64, 65, 4097, 32000, 128256, int(rng.integers(1, 300000))]))
+    levels = int(rng.choice([3, 50, 1 << 20]))
+    x = (rng.integers(0, levels, size=(B, V)) / levels - 0.5).astype(np.float32)
+    for b in range(B):
+        kind = int(rng.integers(0, 6))
+        pos = rng.integers(0, V, size=min(V, 4))
+        if kind == 1:
+            x[b, pos] = x[b].max()                       # the maximum at several places
+        elif kind == 2:
+            x[b, pos[-1]] = np.nan
+        elif kind == 3:
+            x[b, pos] = np.inf
+        elif kind == 4:
+            x[b] = -np.inf
+            x[b, pos[:1]] = -np.float32(3e38)
+        elif kind == 5:
+            x[b] = np.where(rng.random(V) < 0.5, np.float32(-0.0), np.float32(0.0))
+    return x
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_argmax_bit_exact(seed):
+    """Seeded random logits with ties, NaN, infinities and signed zeros: the index equals
+    the oracle's (lowest index among equal maxima, the first NaN), and the workspace
+    returns to zero."""
+    logits = _random_argmax_case(seed)
+    idx, ws = gpu_argmax(logits)
+    assert (idx == oracle.argmax_ref(logits)).all(), (idx, oracle.argmax_ref(logits))
+    assert (ws.cpu().numpy() == 0).all()
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_lm_head_then_argmax_on_gpu_logits(B):
     """int8-g32 LM head 128256x2048 then argmax, all on the GPU; the argmax must equal the
