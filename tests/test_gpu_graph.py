@@ -241,3 +241,86 @@ def test_graph_fused_chain_two_sets(B):
             assert (out["act"] == out0["act"]).all(), r
             assert (out["idx"] == out0["idx"]).all() and (out["idx"] == oracle.argmax_ref(out["logits"])).all()
             assert bool((c.ws == 0).all().item())
+
+
+# ------------------------------------------- seeded random captured steps
+GRAPH_FMTS = [qg.BF16, qg.INT8_G32, qg.Q4_0_G32, qg.INT4_G128, qg.INT8_ROW, qg.INT4_G64]
+
+
+def _random_graph_case(seed):
+    """A seeded random step: a grouped call (2-8 GEMVs of mixed formats and ragged
+    shapes, the fused argmax on one entry) and one decode-attention call."""
+    rng = np.random.default_rng(15000 + seed)
+    B = int(rng.integers(1, 9))
+    gemvs = []
+    for i in range(int(rng.integers(2, 9))):
+        fmt = int(rng.choice(GRAPH_FMTS))
+        step = synth.K_ALIGN[fmt]
+        K = int(step * rng.integers(1, 6144 // step + 1))
+        M = int(rng.choice([1, 63, 640, 2048, int(rng.integers(1, 9000))]))
+        gemvs.append(synth.make_gemv(f"g{i}", fmt, M, K, B, 7, 3000 + 16 * seed + i, "o"))
+    am = int(rng.integers(0, len(gemvs)))
+    n_kv = int(rng.choice([1, 2, 8]))
+    att = (int(rng.integers(1, 9)), n_kv * int(rng.choice([1, 4])), n_kv, int(rng.choice([64, 128])),
+           int(rng.choice([33, 512, 2000])))
+    return B, gemvs, am, att
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_graph_random_step(seed):
+    """The step eager (against the oracle), then captured in one graph and replayed three
+    times with the outputs overwritten in between: every replay reproduces the eager
+    outputs bit for bit, the argmax included, and leaves the workspace zero."""
+    B, gemvs, am, (Ba, n_q, n_kv, d, T) = _random_graph_case(seed)
+    items = []
+    for g in gemvs:
+        W = dev(np.ascontiguousarray(g.w).reshape(-1).view(np.uint8))
+        S = dev(g.s.reshape(-1)) if g.s is not None else None
+        Y = torch.full((B, g.M), float("nan"), dtype=torch.float32, device=DEV)
+        items.append((g.fmt, W, S, dev(np.ascontiguousarray(g.x).reshape(B, g.K)), Y, g.M, g.K))
+    descs = qg.grouped_descs(items)
+    ws = qg.fused_argmax_workspace(B)
+    idx = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    at = synth.make_attention(Ba, n_q, n_kv, d, T, seed=16000 + seed)
+    aq, ak, av, al = dev(at.q), dev(at.k), dev(at.v), dev(at.lens)
+    aout = torch.full((Ba, n_q, d), float("nan"), dtype=torch.float32, device=DEV)
+    aws = qg.attention_workspace(Ba, n_q, n_kv, d, T)
+
+    def step(stream=None):
+        qg.run_grouped_argmax(descs, B, am, ws, idx, stream=stream)
+        qg.attention_decode(aq, ak, av, al, aout, Ba, n_q, n_kv, d, T, at.scale, aws, stream=stream)
+
+    def poison():
+        for it in items:
+            it[4].fill_(float("nan"))
+        idx.fill_(-7)
+        aout.fill_(float("nan"))
+
+    shapes = " ".join(f"{qg.FMT_NAMES[g.fmt]}:{g.M}x{g.K}" for g in gemvs)
+    print(f"[gpu] graph seed={seed} B={B} argmax={am} {shapes} attention B={Ba} {n_q}/{n_kv} d={d} T={T}",
+          flush=True)
+    step()
+    torch.cuda.synchronize()
+    ys = [it[4].cpu().numpy() for it in items]
+    idx0, a0 = idx.cpu().numpy(), aout.cpu().numpy()
+    for g, y in zip(gemvs, ys):
+        y_ref, a_ref = oracle.gemv_ref(g.fmt, g.w, g.s, g.x, g.M, g.K)
+        rep = oracle.parity_report(y, y_ref, a_ref)
+        assert rep["ok"], f"eager {g.name} {rep}"
+    assert (idx0 == oracle.argmax_ref(ys[am])).all()
+    assert bool((ws == 0).all().item())
+    import oracle.attention as oatt
+    ref, A = oatt.attention_decode_ref(at.q, at.k, at.v, at.lens, at.scale)
+    assert oatt.parity_report(a0, ref, A)["ok"]
+
+    graph = capture(step)
+    for r in range(REPLAYS):
+        poison()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for it, y0 in zip(items, ys):
+            assert (it[4].cpu().numpy().view(np.uint32) == y0.view(np.uint32)).all(), r
+        assert (idx.cpu().numpy() == idx0).all(), r
+        assert bool((ws == 0).all().item()), r
+        assert (aout.cpu().numpy().view(np.uint32) == a0.view(np.uint32)).all(), r
