@@ -125,6 +125,7 @@ struct AttnPlan {
   int splits = 1;
   int positions = 0;
   size_t part_bytes = 0;
+  bool short_blocks = false;   // softmax blocks of at most 16 positions (small calls)
 };
 AttnPlan attention_plan(int batch, int n_q, int n_kv, int head_dim, int64_t max_ctx);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
