@@ -212,12 +212,24 @@ def test_run_fused_validation_errors_before_any_launch():
 def test_attention_workspace_and_validation():
     L = qg.lib()
     n = ctypes.c_size_t()
-    # Llama-3.2-1B heads at context 2048: 16 splits of 128 positions per key/value head
+    # Llama-3.2-1B heads (G = 4, head dim 64). Batch 1 at context 2048 is a small call
+    # (batch x KV heads x context <= 65536): blocks of 16 positions, 4 waves per split,
+    # 2048 / 64 = 32 splits per key/value head, each record 2G + G*D floats
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, ctypes.byref(n)) == qg.OK
+    assert n.value == 8 * 32 * (2 * 4 + 4 * 64) * 4
+    # ... at context 1024: 16 splits
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 1024, ctypes.byref(n)) == qg.OK
     assert n.value == 8 * 16 * (2 * 4 + 4 * 64) * 4
-    # one split (short context): no records, the 256-byte minimum
-    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 128, ctypes.byref(n)) == qg.OK
+    # batch 8 at context 2048 is not small: blocks of 32 positions (128 per split), and
+    # the splits stop at about 256 workgroups: 256 / (8 x 8) = 4 per key/value head
+    assert L.qgemv_attention_workspace_size(8, 32, 8, 64, 2048, ctypes.byref(n)) == qg.OK
+    assert n.value == 8 * 8 * 4 * (2 * 4 + 4 * 64) * 4
+    # one split (a context within one split of 4 x 16 positions): no records, the
+    # 256-byte minimum; 128 positions are two splits
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 64, ctypes.byref(n)) == qg.OK
     assert n.value == 256
+    assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 128, ctypes.byref(n)) == qg.OK
+    assert n.value == 8 * 2 * (2 * 4 + 4 * 64) * 4
     assert L.qgemv_attention_workspace_size(1, 32, 8, 64, 2048, None) == qg.EINVAL
     for args in ((1, 24, 8, 64, 2048), (1, 32, 8, 96, 2048), (1, 32, 8, 64, 0), (0, 32, 8, 64, 16),
                  (1, 32, 0, 64, 16), (1, 32, 8, 128, 1 << 24)):
